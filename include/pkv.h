@@ -1,0 +1,225 @@
+/*
+ * pkv.h -- C ABI of the paged KV-cache attention library (libpkv.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Plain C: only integers, floats and pointers cross this boundary.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Ownership: every pointer is owned by the caller.  Tensor pointers are
+ *    DEVICE pointers (hipMalloc'd or torch CUDA tensors on the current device);
+ *    the library allocates no device memory and keeps no state beyond a
+ *    thread-local error string and the host block managers the caller creates.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream).  Kernel calls are asynchronous on that stream.
+ *  - Errors: scalar arguments are validated on the host before any launch; a
+ *    failure returns a non-zero pkv_status and leaves all memory untouched.
+ *    A failed launch returns PKV_ERR_HIP.  pkv_last_error() gives detail.
+ *  - Device-resident CONTENTS (block ids, slots, lengths, cu_seqlens) are the
+ *    caller's contract and are not validated: out-of-range values are undefined
+ *    behaviour.  The host block manager below only ever produces valid ones.
+ *  - KV pool layout: K and V are separate pools of shape [NB, B, Hkv, D]
+ *    (block, offset in block, kv head, head dim), elements of dtype kv_dtype,
+ *    row-major.  (S06 PagedAttention chapter, "implementation" section: the
+ *    pool is [num_blocks, block_size, n_kv_heads, head_dim].)
+ *  - A slot is an absolute row index of a pool: slot = block * B + offset.
+ *  - Supported instantiations: kv dtype {f32, f16, bf16}; D in {64, 128};
+ *    B in {1, 2, 4, 8, 16, 32}; any Hkv >= 1 and Hq a multiple of Hkv.
+ *    Anything else returns PKV_ERR_UNSUPPORTED.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1, /* bad scalar argument or null pointer */
+  PKV_ERR_UNSUPPORTED = 2, /* valid but not instantiated (dtype, D, B) */
+  PKV_ERR_WORKSPACE = 3,   /* workspace too small or null */
+  PKV_ERR_OOM = 4,         /* block manager: free list exhausted */
+  PKV_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+/* Human-readable name of a status code (static storage). */
+const char* pkv_status_string(pkv_status s);
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+/* Library version string, e.g. "pkv 0.1 gfx950". */
+const char* pkv_version(void);
+
+/* ------------------------------------------------------------------------
+ * reshape_and_cache -- scatter new tokens' K/V rows into their slots.
+ *
+ * Defined by "LLM inference, part 3: single node", ch. 13 sec. 1 (the CPU
+ * precomputes one absolute slot per new token and the GPU performs
+ * kv_cache[slot_mapping[i]] = new_kv) and CS349D lecture 3 sec. 3.2 (the
+ * split/reorder/block-write is one fused kernel).
+ *
+ *   key, value   : device, [T, Hkv, D] of kv_dtype (row-major)
+ *   k_cache,
+ *   v_cache      : device pools [NB, B, Hkv, D] of kv_dtype, written in place
+ *   slot_mapping : device int64 [T]; slot < 0 means "skip this token"
+ *                  (padding); otherwise 0 <= slot < NB * B
+ * Bytes are copied unchanged (bit-exact).  T == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                 const int64_t* slot_mapping, int32_t T, int32_t Hkv, int32_t D,
+                                 int32_t B, int64_t NB, pkv_dtype kv_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * paged_attention_decode -- one query token per sequence attends to its
+ * whole paged context.
+ *
+ * Defined by CS349D lecture 3 sec. 3.2 (attention over the blocks of a block
+ * table is mathematically identical to contiguous attention: one softmax over
+ * every position of every block), CMU 11-868 lecture 24 sec. 3.2 (scores
+ * within a block, blocks merged with an online softmax, no gather into a
+ * contiguous buffer), "LLM inference, part 3" ch. 9 sec. 1 (GQA: query head h
+ * uses KV head h / (Hq / Hkv)) and ch. 11 sec. 3 (block table tensor
+ * [max_num_reqs, max_num_blocks_per_req], physical = table[req][logical]).
+ *
+ *   out            : device [S, Hq, D] of out_dtype (f32, f16 or bf16)
+ *   q              : device [S, Hq, D] of kv_dtype
+ *   k_cache,v_cache: device pools [NB, B, Hkv, D] of kv_dtype
+ *   block_tables   : device int32 [S, max_blocks_per_seq]; entries past
+ *                    ceil(context_lens[s] / B) are never read
+ *   context_lens   : device int32 [S]; tokens cached for sequence s, the
+ *                    current token included; rows past it are never read.
+ *                    0 gives an all-zero output row.
+ *   max_context_len: host bound >= every context_lens[s] (sizes the grid)
+ *   scale          : softmax scale, usually 1/sqrt(D)
+ *   workspace      : device scratch of at least pkv_decode_workspace_size()
+ *                    bytes (may be NULL when that size is 0); contents on
+ *                    entry are ignored.
+ * out[s, h, :] = sum_t softmax_t(scale * q[s,h,:] . K[s,t,:]) V[s,t,:],
+ * computed in fp32.  The summation order depends only on logical positions,
+ * so the result is bit-identical under any permutation of physical blocks and
+ * when sequences alias shared blocks.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_decode_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                     int32_t max_context_len, size_t* bytes);
+
+pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
+                                      const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t max_context_len,
+                                      int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                      float scale, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * paged_attention_prefill -- a causal query chunk per sequence over its
+ * paged context (earlier prompt + the chunk itself).
+ *
+ * Defined by "LLM inference, part 3" ch. 13 sec. 1 (flattened varlen batch
+ * with cu_seqlens boundaries; the block table locates earlier KV) and sec. 2
+ * (chunked prefill: each chunk reads the earlier prompt's KV through the block
+ * table) and CS349D lecture 3 sec. 7.2 (a token's K/V depend only on earlier
+ * tokens, so the mask is causal).
+ *
+ *   out            : device [Tq, Hq, D] of out_dtype
+ *   q              : device [Tq, Hq, D] of kv_dtype (rows of all chunks
+ *                    concatenated)
+ *   cu_seqlens_q   : device int32 [S + 1]; chunk of sequence s is rows
+ *                    cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1; cu_seqlens_q[S]==Tq
+ *   max_query_len  : host bound >= every chunk length
+ *   context_lens   : device int32 [S]; prior context + chunk, the chunk's K/V
+ *                    already written to the cache (pkv_reshape_and_cache)
+ * Row i of sequence s sits at position context_lens[s] - Q_s + i and attends
+ * to positions 0 .. context_lens[s] - Q_s + i.  kv_dtype f16/bf16 use the
+ * matrix cores (16-bit operands, fp32 accumulation; the softmax weights are
+ * rounded to kv_dtype before the PV product); f32 uses fp32 vector math.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* q,
+                                       const int32_t* cu_seqlens_q, int32_t Tq,
+                                       int32_t max_query_len, const void* k_cache,
+                                       const void* v_cache, pkv_dtype kv_dtype,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t max_context_len,
+                                       int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                       float scale, void* stream);
+
+/* ------------------------------------------------------------------------
+ * copy_blocks -- batched whole-block copies for copy-on-write.
+ *
+ * Defined by CS349D lecture 3 sec. 4.1 (writing into a block whose refcount is
+ * above one first copies it to a fresh block) and sec. 3.2 (the many small CoW
+ * copies are merged into one kernel launch).
+ *
+ *   k_caches, v_caches : HOST arrays of num_layers DEVICE pointers, each a
+ *                        pool [NB, B, Hkv, D] of kv_dtype
+ *   block_pairs        : DEVICE int64 [N, 2] of (src, dst) physical blocks
+ * For every layer and pair, block dst of the K pool and of the V pool becomes
+ * a bit copy of block src.  Destinations must be distinct and no destination
+ * may also be a source in the same call (copy-on-write targets are freshly
+ * allocated blocks); then every pair reads the pre-call contents.  N == 0 or
+ * num_layers == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                           const int64_t* block_pairs, int32_t N, int32_t B, int32_t Hkv,
+                           int32_t D, pkv_dtype kv_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host block manager (CPU only; builds block tables, slots and CoW pairs).
+ *
+ * Defined by the S06 PagedAttention chapter ("block manager" listing: a free
+ * list; a request gets ceil(n / B) blocks, any free block will do; out of
+ * blocks -> the allocator fails; "reference counts must be exact" section: the
+ * number of tables holding a block equals its refcount), the kwkr.cn
+ * PagedAttention post (KV-cache manager: blocks taken from the front of the free
+ * list, a new block only once the last one is full, OOM on exhaustion) and
+ * CS349D lecture 3 sec. 4.1 (fork copies the parent's table and raises every
+ * refcount; the first write into a shared partly-filled last block copies it;
+ * freeing decrements refcounts and returns blocks that reach zero).
+ *
+ * Sequences are identified by small non-negative ids assigned by the manager.
+ * Every call returns PKV_OK or an error and leaves the state unchanged on
+ * error.  Not thread-safe: one manager per thread.
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* free_order: host int32 [num_blocks] permutation of 0..num_blocks-1 giving the
+ * order blocks are handed out (NULL = 0, 1, 2, ...).  Freed blocks go to the
+ * back of the free list. */
+pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                         pkv_block_manager** out);
+void pkv_bm_destroy(pkv_block_manager* bm);
+/* New sequence holding n_tokens tokens (ceil(n_tokens / B) fresh blocks). */
+pkv_status pkv_bm_add_seq(pkv_block_manager* bm, int32_t n_tokens, int32_t* seq_id);
+/* Grow sequence by one token.  *slot receives the new token's slot.  If the
+ * last block was shared and partly filled, it is replaced by a fresh private
+ * copy: *cow_src / *cow_dst receive (old, new) block ids, which the caller must
+ * copy (pkv_copy_blocks) before writing the slot; otherwise both are -1. */
+pkv_status pkv_bm_append_token(pkv_block_manager* bm, int32_t seq_id, int64_t* slot,
+                               int32_t* cow_src, int32_t* cow_dst);
+/* New sequence sharing every block of parent (refcounts + 1). */
+pkv_status pkv_bm_fork(pkv_block_manager* bm, int32_t parent, int32_t* child);
+/* Drop a sequence: refcounts - 1, blocks reaching zero return to the free list. */
+pkv_status pkv_bm_free_seq(pkv_block_manager* bm, int32_t seq_id);
+/* Copy the sequence's table into out[0..cap); *n receives its length. */
+pkv_status pkv_bm_table(const pkv_block_manager* bm, int32_t seq_id, int32_t* out, int32_t cap,
+                        int32_t* n);
+pkv_status pkv_bm_seq_len(const pkv_block_manager* bm, int32_t seq_id, int32_t* n_tokens);
+/* Slots of positions [start, start + count) of the sequence (all < seq_len). */
+pkv_status pkv_bm_slots(const pkv_block_manager* bm, int32_t seq_id, int32_t start,
+                        int32_t count, int64_t* out);
+pkv_status pkv_bm_refcount(const pkv_block_manager* bm, int32_t block, int32_t* refcount);
+pkv_status pkv_bm_num_free(const pkv_block_manager* bm, int32_t* n);
+/* Verify every invariant: refcount(b) == number of live tables holding b, free
+ * blocks have refcount 0 and appear once, every table has ceil(len / B)
+ * entries.  Returns PKV_OK or PKV_ERR_INVALID_ARG with detail. */
+pkv_status pkv_bm_check(const pkv_block_manager* bm);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,73 @@
+"""Each plausible mistake planted in a copy of the oracle's C source (on the CPU,
+never in the product) must make at least one pin fail."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "pkv_oracle.c")
+
+# (name, original text, mutated text) -- each must occur exactly once
+MUTATIONS = [
+    ("gather_offset_off_by_one", "int64_t off = t % B;", "int64_t off = (t + 1) % B;"),
+    ("gather_block_index", "int64_t blk = table[t / B];", "int64_t blk = table[t / B + (t >= B)];"),
+    ("gqa_strided_grouping", "const int32_t h = g * G + j;\n        const int64_t base = ((int64_t)s * Hq + h) * D;",
+     "const int32_t h = j * Hkv + g;\n        const int64_t base = ((int64_t)s * Hq + h) * D;"),
+    ("scale_dropped", "z[t] = scale * acc;", "z[t] = acc;"),
+    ("no_normalisation", "double p = z[t] / denom;", "double p = z[t];"),
+    ("values_from_keys", "if (rc == PKVO_OK) rc = pkvo_gather(V, v_cache, dtype, table, L, NB, Hkv, D, B, g);\n      for (int32_t j = 0; j < G",
+     "if (rc == PKVO_OK) rc = pkvo_gather(V, k_cache, dtype, table, L, NB, Hkv, D, B, g);\n      for (int32_t j = 0; j < G"),
+    ("causal_off_by_one", "const int32_t visible = L - Qs + i + 1;", "const int32_t visible = L - Qs + i;"),
+    ("causal_sees_future", "const int32_t visible = L - Qs + i + 1;", "const int32_t visible = L;"),
+    ("f16_subnormal_exponent", "v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    ("f16_normal_bias", "v = ldexp((double)(m | 0x400), e - 25);", "v = ldexp((double)(m | 0x400), e - 24);"),
+    ("bf16_shift", "uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    ("reshape_skips_slot_zero", "if (slot < 0) continue;", "if (slot <= 0) continue;"),
+    ("reshape_k_into_v", "memcpy((char*)v_cache + dst, (const char*)value", "memcpy((char*)v_cache + dst, (const char*)key"),
+    ("copy_reads_destination", "memcpy(snap + (size_t)(2 * i) * blk_bytes, kc + (size_t)pairs[2 * i] * blk_bytes",
+     "memcpy(snap + (size_t)(2 * i) * blk_bytes, kc + (size_t)pairs[2 * i + 1] * blk_bytes"),
+]
+
+# the pins, called directly (parametrised ones with representative arguments)
+CASES = [
+    (pins.test_f16_widening_matches_numpy_for_every_bit_pattern, {}),
+    (pins.test_bf16_widening_matches_torch_for_every_bit_pattern, {}),
+    (pins.test_gather_reproduces_kwkr_kvcache_manager_example,
+     {"case": pins.golden("kwkr_kvcache_manager.json")["cases"][0]}),
+    (pins.test_decode_contiguous_case_matches_torch_sdpa, {"dtype": "bf16", "Hq": 8, "Hkv": 2}),
+    (pins.test_decode_matches_brute_force_loops, {"B": 4}),
+    (pins.test_decode_single_token_returns_its_value_exactly, {}),
+    (pins.test_decode_equal_keys_give_mean_of_values, {}),
+    (pins.test_tiny_workload_matches_sdpa, {}),
+    (pins.test_prefill_matches_causal_sdpa_on_whole_sequences, {"dtype": "f32"}),
+    (pins.test_reshape_and_cache_matches_numpy_scatter, {"dtype": "f32"}),
+    (pins.test_copy_blocks_matches_numpy_indexing, {}),
+]
+
+
+@pytest.mark.parametrize("name,orig,mut", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, orig, mut, tmp_path):
+    src = open(SRC).read()
+    assert src.count(orig) == 1, f"mutation anchor not unique for {name}"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(orig, mut))
+    lib = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-ffp-contract=off", "-shared", "-o",
+                    str(lib), str(path), "-lm"], check=True)
+    caught = []
+    with oracle.use_library(str(lib)):
+        for fn, kw in CASES:
+            try:
+                fn(**kw)
+            except (AssertionError, oracle.OracleError):
+                caught.append(fn.__name__)
+    assert caught, f"no pin caught mutation {name}"
+
+
+def test_unmutated_oracle_passes_every_case():
+    for fn, kw in CASES:
+        fn(**kw)

@@ -1,0 +1,113 @@
+"""Host-side checks of the seeded input generators (no GPU)."""
+import numpy as np
+import pytest
+
+from conftest import golden
+from paged_kv_cache_71_amd import workloads as W
+
+
+@pytest.mark.parametrize("case", golden("kv_sizes.json")["cases"], ids=lambda c: str(c["kv_heads"]))
+def test_kv_bytes_per_token_matches_pages(case):
+    bpt = W.kv_bytes_per_token(case["layers"], case["kv_heads"], case["head_dim"], case["elem_bytes"])
+    assert bpt == case["bytes_per_token"]
+    if "bytes_per_block" in case:
+        assert bpt * case["block_size"] == case["bytes_per_block"]
+    if "blocks_fit" in case:
+        assert case["tokens_fit"] // case["block_size"] == case["blocks_fit"]
+
+
+def test_split_and_cu_seqlens_match_pages():
+    cases = golden("chunked_prefill.json")["cases"]
+    assert W.split_chunks(cases[0]["n_tokens"], cases[0]["budget"]) == cases[0]["chunks"]
+    assert W.cu_seqlens(cases[1]["counts"]).tolist() == cases[1]["cu_seqlens"]
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-9, -2.5, 1.0 + 2**-9], np.float32)
+    bits = W.to_storage(x, "bf16")
+    # 1+2^-9 is a tie between 1 and 1+2^-7 -> even (1.0); 1+3*2^-9 rounds up
+    assert bits.tolist() == [0x3F80, 0x3F80, 0x3F81, 0xC020, 0x3F80]
+    assert np.array_equal(W.storage_to_f32(W.to_storage(np.float32([3.0]), "bf16"), "bf16"), [3.0])
+
+
+def _check_tables(batch):
+    """Every sequence has ceil(L/B) table entries (waste < one block), the rest -1;
+    data rows are finite and unwritten rows poisoned."""
+    B = batch.B
+    where = {int(b): i for i, b in enumerate(batch.block_ids)}
+    for s in range(batch.S):
+        L = int(batch.context_lens[s])
+        nb = -(-L // B)
+        row = batch.block_tables[s]
+        assert np.all(row[:nb] >= 0) and np.all(row[:nb] < batch.NB) and np.all(row[nb:] == -1)
+        assert B * nb - L < B                       # waste below one block
+        last = where[int(row[nb - 1])] if nb else None
+        if last is not None:
+            fill = L - (nb - 1) * B
+            kb = W.storage_to_f32(batch.k_blocks[last], batch.dtype)
+            assert np.all(np.isfinite(kb[:fill]))
+            if batch.name != "shared_prefix_bf16":
+                assert np.all(np.isnan(kb[fill:]))
+
+
+def test_tiny_workload_shape_and_tables():
+    b = W.tiny_f32(0)
+    assert b.context_lens.tolist() == [6, 17, 1, 33]
+    assert (b.S, b.Hq, b.Hkv, b.D, b.B, b.NB, b.dtype) == (4, 4, 4, 64, 4, 64, "f32")
+    assert b.block_ids.shape[0] == 2 + 5 + 1 + 9
+    # tables hand out a seeded permutation of the pool from its front
+    perm = np.random.default_rng(0).permutation(64)
+    assert np.concatenate([b.block_tables[s][b.block_tables[s] >= 0] for s in range(4)]).tolist() == perm[:17].tolist()
+    _check_tables(b)
+    assert b.kv_read_bytes() == 57 * 2 * 4 * 64 * 4
+
+
+def test_llama_workload_lengths():
+    # lengths are the first draw of the seeded generator
+    L = W.lognormal_lengths(np.random.default_rng(0), 256)
+    assert L.min() >= 16 and L.max() <= 8192
+    assert 700 < np.median(L) < 1500
+    b = W.llama3_8b_bf16(0, S=12)
+    assert np.array_equal(b.context_lens, L[:12])
+    _check_tables(b)
+    assert b.NB == 183105 and b.max_nb == -(-b.context_lens.max() // 16)
+
+
+def test_shared_prefix_workload_aliases_prompt_blocks():
+    b = W.shared_prefix_bf16(0, prompts=3, n=4, prompt_len=2000)
+    assert b.S == 12
+    for p in range(3):
+        rows = b.block_tables[p * 4:(p + 1) * 4, :125]
+        assert np.all(rows == rows[0])              # 125 full prompt blocks shared by all 4
+    assert b.meta["cow_pairs"].shape == (0, 2)      # 2000 % 16 == 0: no copy-on-write
+    _check_tables(b)
+    cow = W.shared_prefix_bf16(0, prompts=3, n=4, prompt_len=1999)
+    assert cow.meta["cow_pairs"].shape == (9, 2)    # n - 1 = 3 copies per prompt
+    for p in range(3):
+        rows = cow.block_tables[p * 4:(p + 1) * 4]
+        assert np.all(rows[:, :124] == rows[0, :124])
+        last = rows[:, 124]
+        assert len(set(last.tolist())) == 4         # 3 private copies + the original
+    # the copies hold the same 15 prompt rows as the original
+    where = {int(x): i for i, x in enumerate(cow.block_ids)}
+    for src, dst in cow.meta["cow_pairs"]:
+        assert np.array_equal(cow.k_blocks[where[int(src)], :15], cow.k_blocks[where[int(dst)], :15])
+    assert cow.unique_kv_bytes() < cow.kv_read_bytes()
+
+
+def test_prefill_workload():
+    b = W.prefill_bf16(0, S=3, prior_lo=40, prior_hi=90, chunk=20, NB=100)
+    assert b.cu_seqlens_q.tolist() == [0, 20, 40, 60]
+    assert np.all(b.context_lens >= 60) and np.all(b.context_lens <= 110)
+    assert b.new_slots.shape == (60,) and b.q.shape == (60, 32, 128)
+    _check_tables(b)
+
+
+def test_new_token_values_are_the_cached_ones():
+    b = W.decode_batch(3, [5, 16, 17], 2, 1, 8, 4, "f16", NB=20)
+    k, v = b.full_pool()
+    flat_k = k.reshape(-1, 1, 8)
+    assert np.array_equal(flat_k[b.new_slots], b.new_k)
+    for s in range(3):
+        L = int(b.context_lens[s])
+        assert b.new_slots[s] == b.block_tables[s, (L - 1) // 4] * 4 + (L - 1) % 4
