@@ -1,0 +1,304 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+A step is one decode step of the Llama-3-8B-shaped layer batch (256 sequences,
+32 query / 8 KV heads, head_dim 128, block 16, bf16 KV, log-normal context
+lengths with median 1024 clipped to [16, 8192], blocks scattered over a 12 GB
+pool): reshape_and_cache of the 256 new tokens, then paged_attention_decode.
+The headline metric is the achieved KV-read bandwidth of that step:
+algorithmic K+V bytes (every valid token of every sequence, once per KV head)
+divided by the step time.
+
+Also reported (``rows``): the other kernels of the path on their own
+workloads -- OPT-13B-shaped fp16 decode, shared-prefix decode, the 192-pair
+copy-on-write copy_blocks, and the chunked causal prefill (TFLOP/s).
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--headline-only]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the other rows and the CPU baseline (used under the profilers)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="context tokens of the bounded oracle sample (0: the whole batch)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is by sequence, KV head or context; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_71_amd as pkv
+    from paged_kv_cache_71_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pkv.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    TD = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+    def up(a, dtype):
+        a = np.ascontiguousarray(a)
+        if dtype == "f32":
+            return torch.from_numpy(a).to(dev)
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(TD[dtype])
+
+    class Dev:
+        def __init__(self, b):
+            self.b = b
+            shape = (b.NB, b.B, b.Hkv, b.D)
+            self.k = torch.full(shape, float("nan"), dtype=TD[b.dtype], device=dev)
+            self.v = torch.full(shape, float("nan"), dtype=TD[b.dtype], device=dev)
+            idx = torch.from_numpy(b.block_ids).to(dev)
+            self.k.index_copy_(0, idx, up(b.k_blocks, b.dtype))
+            self.v.index_copy_(0, idx, up(b.v_blocks, b.dtype))
+            self.q = up(b.q, b.dtype)
+            self.tables = torch.from_numpy(b.block_tables).to(dev)
+            self.lens = torch.from_numpy(b.context_lens).to(dev)
+            self.cu = torch.from_numpy(b.cu_seqlens_q).to(dev) if b.cu_seqlens_q is not None else None
+            self.slots = torch.from_numpy(b.new_slots).to(dev)
+            self.new_k = up(b.new_k, b.dtype)
+            self.new_v = up(b.new_v, b.dtype)
+            self.out = torch.empty(tuple(self.q.shape), dtype=torch.float32, device=dev)
+            self.ws = None
+            if b.cu_seqlens_q is None:
+                n = pkv.decode_workspace_size(b.S, b.Hq, b.Hkv, b.D, b.B, b.max_context_len)
+                self.ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+
+        def reshape(self):
+            pkv.reshape_and_cache(self.new_k, self.new_v, self.k, self.v, self.slots)
+
+        def decode(self):
+            b = self.b
+            pkv.paged_attention_decode(self.out, self.q, self.k, self.v, self.tables, self.lens,
+                                       b.max_context_len, b.scale, workspace=self.ws)
+
+        def prefill(self):
+            b = self.b
+            maxq = int(np.max(np.diff(b.cu_seqlens_q)))
+            pkv.paged_attention_prefill(self.out, self.q, self.cu, maxq, self.k, self.v,
+                                        self.tables, self.lens, b.max_context_len, b.scale)
+
+        def free(self):
+            del self.k, self.v
+
+    def time_fn(fn, iters, warm=3):
+        """Mean ms of fn() over iters launches, HIP events on the current stream."""
+        for _ in range(warm):
+            fn()
+        s = torch.cuda.current_stream()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        torch.cuda.synchronize()
+        for a, z in evs:
+            a.record(s)
+            fn()
+            z.record(s)
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(z) for a, z in evs])
+        return float(t.mean()), float(np.median(t))
+
+    # ------------------------------------------------------------ headline
+    t0 = time.time()
+    b = W.llama3_8b_bf16(args.seed)
+    log(f"[bench] llama3_8b_bf16 generated in {time.time() - t0:.1f}s: S={b.S} sum(L)="
+        f"{int(b.context_lens.sum())} max={b.max_context_len} blocks={b.block_ids.shape[0]}")
+    d = Dev(b)
+    kv_bytes = b.kv_read_bytes()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        d.reshape()
+        d.decode()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        d.reshape()
+        dec_ev[i][0].record(stream)
+        d.decode()
+        dec_ev[i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    dec_ms = float(np.mean([a.elapsed_time(z) for a, z in dec_ev]))
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (dec_ms * 1e-3) / 1e9
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us, "
+        f"{achieved:.0f} GB/s on the decode kernels")
+
+    result = {
+        "metric": "paged-attn decode achieved KV-read HBM GB/s (% of peak), Llama-3-8B GQA",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3_8b_gqa_decode_bf16: one decode step (reshape_and_cache + "
+                        "paged_attention_decode), 256 sequences, 32 q / 8 kv heads, head_dim 128, "
+                        "block 16, log-normal lengths median 1024 clipped [16, 8192], 12 GB pool",
+            "sequences": b.S,
+            "context_tokens": int(b.context_lens.sum()),
+            "kv_bytes_per_step": kv_bytes,
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "paged_attention_decode (partition + reduce launches)",
+            "ms_per_launch": round(dec_ms, 5),
+        },
+    }
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if not args.headline_only:
+        rows = {}
+        # decode with an L2/MALL flush before every launch
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        fl = []
+        for _ in range(10):
+            flush.random_(0, 255)
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            d.decode()
+            z.record(stream)
+            fl.append((a, z))
+        torch.cuda.synchronize()
+        fms = float(np.mean([a.elapsed_time(z) for a, z in fl]))
+        rows["decode_llama3_8b_flushed"] = {"ms": round(fms, 5), "GB/s": round(kv_bytes / fms / 1e6, 1)}
+        del flush
+        rms, _ = time_fn(d.reshape, 20)
+        rb = 2 * 2 * b.new_k.size * 2   # read + write of K and V rows
+        rows["reshape_and_cache_256_tokens"] = {"ms": round(rms, 5), "GB/s": round(rb / rms / 1e6, 1)}
+        d.free()
+        del d
+        torch.cuda.empty_cache()
+
+        for name, gen in (("decode_opt13b_f16", lambda: W.opt13b_f16(args.seed)),
+                          ("decode_shared_prefix_bf16", lambda: W.shared_prefix_bf16(args.seed))):
+            bb = gen()
+            dd = Dev(bb)
+            ms, _ = time_fn(dd.decode, 20)
+            rows[name] = {"ms": round(ms, 5), "logical_GB/s": round(bb.kv_read_bytes() / ms / 1e6, 1),
+                          "unique_GB/s": round(bb.unique_kv_bytes() / ms / 1e6, 1)}
+            log(f"[bench] {name}: {ms * 1e3:.1f} us")
+            dd.free()
+            del dd
+            torch.cuda.empty_cache()
+
+        # copy-on-write copy of the shared-prefix sub-case: 64 prompts x 3 copies of a 16-token block
+        B, Hkv, D = 16, 8, 128
+        NBc = 4096
+        kc = torch.randn((NBc, B, Hkv, D), device=dev).to(torch.bfloat16)
+        vc = torch.randn((NBc, B, Hkv, D), device=dev).to(torch.bfloat16)
+        perm = np.random.default_rng(0).permutation(NBc)
+        pairs = torch.from_numpy(np.stack([np.repeat(perm[:64], 3), perm[64:64 + 192]], 1)
+                                 .astype(np.int64)).to(dev)
+        ms, _ = time_fn(lambda: pkv.copy_blocks([kc], [vc], pairs), 20)
+        cb = 192 * 2 * 2 * B * Hkv * D * 2
+        rows["copy_blocks_192_pairs"] = {"ms": round(ms, 5), "GB/s": round(cb / ms / 1e6, 1)}
+        del kc, vc
+        torch.cuda.empty_cache()
+
+        pb = W.prefill_bf16(args.seed)
+        pd = Dev(pb)
+        ms, _ = time_fn(pd.prefill, 5, warm=2)
+        flops = 0
+        for s in range(pb.S):
+            Q = int(pb.cu_seqlens_q[s + 1] - pb.cu_seqlens_q[s])
+            L = int(pb.context_lens[s])
+            flops += 4 * pb.Hq * pb.D * sum(L - Q + i + 1 for i in range(Q))
+        rows["prefill_bf16_8x512"] = {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 1),
+                                      "frac_of_bf16_peak": round(flops / ms / 1e9 / BF16_DENSE_TFLOPS, 4)}
+        log(f"[bench] prefill: {ms:.3f} ms, {flops / ms / 1e9:.0f} TFLOP/s")
+        pd.free()
+        del pd
+        result["rows"] = rows
+
+    if not args.headline_only and not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(b, args.cpu_sample_tokens)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(b, sample_tokens):
+    """The fp64 oracle as it is, on a bounded sample of the same workload: the
+    first sequences of the batch until ``sample_tokens`` context tokens."""
+    import oracle
+    k, v, tables = b.compact_pool()
+    n = b.S
+    if sample_tokens:
+        n = min(b.S, int(np.searchsorted(np.cumsum(b.context_lens), sample_tokens) + 1))
+    sel = np.arange(n)
+    runs, t0 = 0, time.perf_counter()
+    while runs < 3 and (runs == 0 or time.perf_counter() - t0 < 10.0):
+        oracle.decode(b.q[sel], k, v, b.dtype, tables[sel], b.context_lens[sel], b.scale)
+        runs += 1
+    dt = (time.perf_counter() - t0) / runs
+    tokens = int(b.context_lens[sel].sum())
+    bytes_ = tokens * 2 * b.Hkv * b.D * 2
+    log(f"[bench] cpu oracle: {n} sequences, {tokens} tokens, {dt:.2f} s per pass x {runs}")
+    return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {b.S} sequences ({tokens} context tokens, {bytes_ / 1e6:.0f} MB of "
+                      f"KV), single-threaded fp64 C oracle, mean of {runs} passes of {dt:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,17 @@
+"""Paged KV-cache attention for AMD Instinct MI355X (gfx950).
+
+The compute path is the HIP library ``libpkv.so`` behind the C ABI declared in
+``include/pkv.h``; this package is its thin Python binding (argument
+marshalling only) plus the seeded workload generators used by the tests and the
+benchmark.  Loading is lazy: ``load_library()`` (or the first call) loads the
+library and raises if it has not been built.
+"""
+from ._binding import (BlockManager, PkvError, PkvOOM, copy_blocks, declared_symbols,
+                       decode_workspace_size, load_library, paged_attention_decode,
+                       paged_attention_prefill, reshape_and_cache)
+
+__all__ = [
+    "BlockManager", "PkvError", "PkvOOM", "copy_blocks", "declared_symbols",
+    "decode_workspace_size", "load_library", "paged_attention_decode", "paged_attention_prefill",
+    "reshape_and_cache",
+]

@@ -1,0 +1,227 @@
+// abi.hip -- the C ABI of libpkv: host-side validation of every scalar argument,
+// choice of kernel instantiation, launch on the caller's stream, and error
+// reporting.  No device memory is allocated here.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+
+namespace {
+thread_local char g_last_error[512] = "";
+
+bool supported_dtype(int dt) { return dt == PKV_F32 || dt == PKV_F16 || dt == PKV_BF16; }
+bool supported_head_dim(int32_t D) { return D == 64 || D == 128; }
+bool supported_block(int32_t B) {
+  return B == 1 || B == 2 || B == 4 || B == 8 || B == 16 || B == 32;
+}
+int ilog2(int32_t x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+}  // namespace
+
+pkv_status fail(pkv_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+pkv_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+#define PKV_REQUIRE(cond, status, ...) \
+  do {                                 \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_OOM: return "PKV_ERR_OOM";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+  }
+  return "PKV_ERR_UNKNOWN";
+}
+
+const char* pkv_last_error(void) { return g_last_error; }
+
+const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
+
+pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                 const int64_t* slot_mapping, int32_t T, int32_t Hkv, int32_t D,
+                                 int32_t B, int64_t NB, pkv_dtype kv_dtype, void* stream) {
+  g_last_error[0] = 0;
+  PKV_REQUIRE(T >= 0, PKV_ERR_INVALID_ARG, "reshape_and_cache: T = %d", T);
+  PKV_REQUIRE(Hkv > 0 && D > 0 && B > 0 && NB > 0, PKV_ERR_INVALID_ARG,
+              "reshape_and_cache: Hkv=%d D=%d B=%d NB=%lld must be positive", Hkv, D, B,
+              (long long)NB);
+  PKV_REQUIRE(supported_dtype(kv_dtype), PKV_ERR_UNSUPPORTED, "reshape_and_cache: dtype %d",
+              (int)kv_dtype);
+  PKV_REQUIRE(supported_head_dim(D), PKV_ERR_UNSUPPORTED, "reshape_and_cache: head_dim %d", D);
+  PKV_REQUIRE(supported_block(B), PKV_ERR_UNSUPPORTED, "reshape_and_cache: block_size %d", B);
+  if (T == 0) return PKV_OK;
+  PKV_REQUIRE(key && value && k_cache && v_cache && slot_mapping, PKV_ERR_INVALID_ARG,
+              "reshape_and_cache: null pointer");
+  const int64_t row_bytes = (int64_t)Hkv * D * dt_bytes(kv_dtype);
+  return launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, T, row_bytes, B,
+                                  static_cast<hipStream_t>(stream));
+}
+
+pkv_status pkv_decode_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                     int32_t max_context_len, size_t* bytes) {
+  g_last_error[0] = 0;
+  PKV_REQUIRE(bytes, PKV_ERR_INVALID_ARG, "decode_workspace_size: null output");
+  PKV_REQUIRE(S >= 0 && Hq > 0 && Hkv > 0 && D > 0 && B > 0 && max_context_len >= 0,
+              PKV_ERR_INVALID_ARG, "decode_workspace_size: bad sizes");
+  PKV_REQUIRE(Hq % Hkv == 0, PKV_ERR_INVALID_ARG, "decode_workspace_size: Hq %% Hkv != 0");
+  DecodePlan plan;
+  plan_decode(S, Hq, Hkv, D, B, max_context_len, &plan);
+  *bytes = plan.workspace_bytes;
+  return PKV_OK;
+}
+
+pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
+                                      const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t max_context_len,
+                                      int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                      float scale, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  g_last_error[0] = 0;
+  PKV_REQUIRE(S >= 0 && Hq > 0 && Hkv > 0 && D > 0 && B > 0, PKV_ERR_INVALID_ARG,
+              "decode: S=%d Hq=%d Hkv=%d D=%d B=%d", S, Hq, Hkv, D, B);
+  PKV_REQUIRE(Hq % Hkv == 0, PKV_ERR_INVALID_ARG, "decode: Hq (%d) not a multiple of Hkv (%d)",
+              Hq, Hkv);
+  PKV_REQUIRE(max_context_len >= 0 && max_blocks_per_seq >= 0, PKV_ERR_INVALID_ARG,
+              "decode: negative max_context_len or max_blocks_per_seq");
+  PKV_REQUIRE(supported_dtype(kv_dtype) && supported_dtype(out_dtype), PKV_ERR_UNSUPPORTED,
+              "decode: dtypes kv=%d out=%d", (int)kv_dtype, (int)out_dtype);
+  PKV_REQUIRE(supported_head_dim(D), PKV_ERR_UNSUPPORTED, "decode: head_dim %d", D);
+  PKV_REQUIRE(supported_block(B), PKV_ERR_UNSUPPORTED, "decode: block_size %d", B);
+  PKV_REQUIRE((int64_t)max_context_len <= (int64_t)max_blocks_per_seq * B, PKV_ERR_INVALID_ARG,
+              "decode: max_context_len %d exceeds table capacity %d x %d", max_context_len,
+              max_blocks_per_seq, B);
+  PKV_REQUIRE(scale == scale, PKV_ERR_INVALID_ARG, "decode: scale is NaN");
+  if (S == 0) return PKV_OK;
+  PKV_REQUIRE(out && q && k_cache && v_cache && block_tables && context_lens, PKV_ERR_INVALID_ARG,
+              "decode: null pointer");
+  DecodePlan plan;
+  plan_decode(S, Hq, Hkv, D, B, max_context_len, &plan);
+  PKV_REQUIRE(workspace_bytes >= plan.workspace_bytes && (plan.workspace_bytes == 0 || workspace),
+              PKV_ERR_WORKSPACE, "decode: workspace of %zu bytes needed, %zu given",
+              plan.workspace_bytes, workspace_bytes);
+  DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_acc = static_cast<float*>(workspace);
+  a.ws_ml = a.ws_acc ? a.ws_acc + (size_t)S * Hq * plan.np_max * D : nullptr;
+  a.max_nb = max_blocks_per_seq;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.B = B;
+  a.log2B = ilog2(B);
+  a.max_ctx = max_context_len;
+  a.part_tokens = plan.part_tokens;
+  a.np_max = plan.np_max;
+  a.gc = plan.gc;
+  a.n_hchunks = (Hq / Hkv) / plan.gc;
+  a.out_dt = out_dtype;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launch_decode(kv_dtype, a, static_cast<hipStream_t>(stream));
+}
+
+pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* q,
+                                       const int32_t* cu_seqlens_q, int32_t Tq,
+                                       int32_t max_query_len, const void* k_cache,
+                                       const void* v_cache, pkv_dtype kv_dtype,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t max_context_len,
+                                       int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                       float scale, void* stream) {
+  g_last_error[0] = 0;
+  PKV_REQUIRE(S >= 0 && Tq >= 0 && max_query_len >= 0 && Hq > 0 && Hkv > 0 && D > 0 && B > 0,
+              PKV_ERR_INVALID_ARG, "prefill: S=%d Tq=%d max_query_len=%d Hq=%d Hkv=%d D=%d B=%d",
+              S, Tq, max_query_len, Hq, Hkv, D, B);
+  PKV_REQUIRE(Hq % Hkv == 0, PKV_ERR_INVALID_ARG, "prefill: Hq (%d) not a multiple of Hkv (%d)",
+              Hq, Hkv);
+  PKV_REQUIRE(max_query_len <= max_context_len || Tq == 0, PKV_ERR_INVALID_ARG,
+              "prefill: max_query_len %d > max_context_len %d", max_query_len, max_context_len);
+  PKV_REQUIRE(supported_dtype(kv_dtype) && supported_dtype(out_dtype), PKV_ERR_UNSUPPORTED,
+              "prefill: dtypes kv=%d out=%d", (int)kv_dtype, (int)out_dtype);
+  PKV_REQUIRE(supported_head_dim(D), PKV_ERR_UNSUPPORTED, "prefill: head_dim %d", D);
+  PKV_REQUIRE(supported_block(B), PKV_ERR_UNSUPPORTED, "prefill: block_size %d", B);
+  PKV_REQUIRE((int64_t)max_context_len <= (int64_t)max_blocks_per_seq * B, PKV_ERR_INVALID_ARG,
+              "prefill: max_context_len %d exceeds table capacity %d x %d", max_context_len,
+              max_blocks_per_seq, B);
+  PKV_REQUIRE(scale == scale, PKV_ERR_INVALID_ARG, "prefill: scale is NaN");
+  if (S == 0 || Tq == 0) return PKV_OK;
+  PKV_REQUIRE(out && q && cu_seqlens_q && k_cache && v_cache && block_tables && context_lens,
+              PKV_ERR_INVALID_ARG, "prefill: null pointer");
+  PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.max_nb = max_blocks_per_seq;
+  a.Tq = Tq;
+  a.max_query_len = max_query_len;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.B = B;
+  a.log2B = ilog2(B);
+  a.max_ctx = max_context_len;
+  a.out_dt = out_dtype;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launch_prefill(kv_dtype, a, static_cast<hipStream_t>(stream));
+}
+
+pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                           const int64_t* block_pairs, int32_t N, int32_t B, int32_t Hkv,
+                           int32_t D, pkv_dtype kv_dtype, void* stream) {
+  g_last_error[0] = 0;
+  PKV_REQUIRE(num_layers >= 0 && N >= 0 && B > 0 && Hkv > 0 && D > 0, PKV_ERR_INVALID_ARG,
+              "copy_blocks: layers=%d N=%d B=%d Hkv=%d D=%d", num_layers, N, B, Hkv, D);
+  PKV_REQUIRE(supported_dtype(kv_dtype), PKV_ERR_UNSUPPORTED, "copy_blocks: dtype %d",
+              (int)kv_dtype);
+  PKV_REQUIRE(supported_head_dim(D), PKV_ERR_UNSUPPORTED, "copy_blocks: head_dim %d", D);
+  PKV_REQUIRE(supported_block(B), PKV_ERR_UNSUPPORTED, "copy_blocks: block_size %d", B);
+  if (N == 0 || num_layers == 0) return PKV_OK;
+  PKV_REQUIRE(k_caches && v_caches && block_pairs, PKV_ERR_INVALID_ARG, "copy_blocks: null pointer");
+  for (int32_t l = 0; l < num_layers; ++l)
+    PKV_REQUIRE(k_caches[l] && v_caches[l], PKV_ERR_INVALID_ARG, "copy_blocks: null pool, layer %d",
+                l);
+  const int64_t block_bytes = (int64_t)B * Hkv * D * dt_bytes(kv_dtype);
+  return launch_copy_blocks(k_caches, v_caches, num_layers, block_pairs, N, block_bytes,
+                            static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

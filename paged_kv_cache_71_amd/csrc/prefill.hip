@@ -1,0 +1,423 @@
+// prefill.hip -- causal paged attention for query chunks (chunked prefill).
+//
+// What is computed ("LLM inference, part 3: single node", ch. 13 secs. 1-2;
+// CS349D lecture 3 sec. 7.2): row i of the chunk of sequence s sits at
+// position context_lens[s] - Q_s + i and attends, through the block table, to
+// the sequence's tokens 0 .. that position (earlier prompt chunks plus the
+// chunk itself, already written by reshape_and_cache).
+//
+// 16-bit KV (bf16/f16): the only dense contraction of the path, so it runs on
+// the gfx950 matrix cores (v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation).
+//  * Workgroup = 4 waves = 128 query rows of one (sequence, KV head): the rows
+//    are (token, query head of the group) pairs, so the G heads that share a KV
+//    head share every K/V tile (GQA reuse).  Each wave owns 32 rows.
+//  * S^T = K Q^T per 32-token KV tile: K rows are the MFMA A operand and are
+//    loaded straight from the paged pool into registers (each lane reads one
+//    token row's contiguous half, 16 bytes at a time, its block found through
+//    the table); Q^T is the B operand, loaded once.  In the 32x32 result each
+//    lane holds 16 scores of ONE query row, so the softmax row max needs only
+//    one cross-lane exchange (lane ^ 32).
+//  * Online softmax in log2 units with a lazy rescale: the accumulator is only
+//    rescaled when the running max grows by more than 2^8, so weights stay
+//    <= 256 and most tiles skip the rescale.
+//  * O^T = V^T P^T: the contraction runs over KV tokens, so V is staged in LDS
+//    transposed ([d][token], double buffered, one barrier per tile) and read
+//    as the A operand; the weights P^T come straight out of the score
+//    registers as the B operand.  For bf16 the weights are split into
+//    hi + lo bf16 parts (two MFMAs), keeping ~16 significant bits so the
+//    result stays within fp32-accumulation accuracy even for peaked attention;
+//    for f16 one f16 operand (11 bits) suffices.
+//  * Workgroups of one (sequence, KV head) are mapped to the same XCD
+//    (blockIdx % 8), so their shared K/V tiles are served from that XCD's L2.
+//  * Positions past the row's causal limit, rows past the chunk and tokens
+//    past the context are masked by selection (never multiplied), and memory
+//    past the context is never dereferenced.
+//
+// fp32 KV: a plain vector-ALU kernel (one wave per query token and KV head).
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWG = 32 * kWaves;
+constexpr int kKVT = 32;             // KV tokens per tile
+constexpr int kVtPitch = kKVT + 4;   // LDS row pitch of V^T (elements), 8-byte aligned rows
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ uint4 ld16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+
+template <int DT>
+__device__ __forceinline__ f32x16_t mfma32(const u32x4_t a, const u32x4_t b, f32x16_t c) {
+  if constexpr (DT == DT_BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
+// fp32 -> 16-bit storage value of dtype DT (round to nearest even).
+template <int DT>
+__device__ __forceinline__ uint32_t to16(float x) {
+  if constexpr (DT == DT_BF16) return f32_to_bf16_bits(x);
+  else return f32_to_f16_bits(x);
+}
+template <int DT>
+__device__ __forceinline__ float from16(uint32_t bits) {
+  if constexpr (DT == DT_BF16) return __uint_as_float(bits << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+__device__ __forceinline__ u32x4_t as_v(uint4 x) { return u32x4_t{x.x, x.y, x.z, x.w}; }
+
+template <int DT, int D, bool PSPLIT>
+__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArgs a) {
+  constexpr int ES = 2;
+  constexpr int NKK = D / 16;   // QK MFMAs per tile (16 of D each)
+  constexpr int HALF = D / 2;   // d-values each lane half supplies
+  constexpr int NDT = D / 32;   // 32-row d tiles of the PV output
+  constexpr int CPR = D / 8;    // 16-byte chunks per token row
+  constexpr int VCH = kKVT * CPR / kThreads;  // V chunks staged per thread per tile
+  static_assert(VCH >= 1 && kKVT * CPR % kThreads == 0, "staging split");
+
+  __shared__ uint16_t vt[2][D][kVtPitch];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hf = lane >> 5;     // lane half: which k-slice this lane supplies
+  const int c32 = lane & 31;
+
+  const int G = a.Hq / a.Hkv;
+  const int TQ = kRowsPerWG / G;  // query tokens per workgroup
+  const int nqt = (a.max_query_len + TQ - 1) / TQ;
+  const int n_pairs = a.S * a.Hkv;
+  const int b = blockIdx.x;
+  int pair, qt;
+  if ((n_pairs & 7) == 0) {  // all workgroups of a (sequence, KV head) on one XCD
+    const int r = b >> 3;
+    pair = (r / nqt) * 8 + (b & 7);
+    qt = nqt - 1 - r % nqt;
+  } else {
+    pair = b / nqt;
+    qt = nqt - 1 - b % nqt;
+  }
+  const int s = pair / a.Hkv;
+  const int kvh = pair % a.Hkv;
+  const int q0 = a.cu_seqlens_q[s];
+  const int Qs = a.cu_seqlens_q[s + 1] - q0;
+  const int L = min(a.context_lens[s], a.max_ctx);  // a larger value would overrun the table
+  const int tq0 = qt * TQ;
+  if (tq0 >= Qs || Qs > L) return;
+
+  // this lane's query row (a column of S^T)
+  const int r = wave * 32 + c32;
+  const int tok = r / G;
+  const int g = r % G;
+  const bool row_valid = tok < TQ && tq0 + tok < Qs;
+  const int pos = row_valid ? L - Qs + tq0 + tok : -1;
+  int pos_min = pos;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) pos_min = min(pos_min, __shfl_xor(pos_min, off));
+  pos_min = __builtin_amdgcn_readfirstlane(pos_min);
+
+  const int kv_end = L - Qs + min(tq0 + TQ, Qs);  // tokens any row of this workgroup sees
+  const int ntiles = (kv_end + kKVT - 1) / kKVT;
+
+  // Q^T fragments (B operand): lane supplies Q[row][HALF*hf + 8*kk + 0..7]
+  u32x4_t qf[NKK];
+  {
+    const char* qp = static_cast<const char*>(a.q) +
+                     (((int64_t)(q0 + tq0 + tok) * a.Hq + (int64_t)kvh * G + g) * D + HALF * hf) * ES;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qf[kk] = row_valid ? as_v(ld16(qp + kk * 16)) : u32x4_t{0, 0, 0, 0};
+  }
+
+  const int32_t* __restrict__ table = a.block_tables + (int64_t)s * a.max_nb;
+  const int64_t row_stride = (int64_t)a.Hkv * D * ES;
+  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)kvh * D * ES;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)kvh * D * ES;
+  const int log2B = a.log2B;
+  const int bmask = a.B - 1;
+
+  auto slot_off = [&](int kv) -> int64_t {
+    const int ph = table[kv >> log2B];
+    return ((int64_t)ph * a.B + (kv & bmask)) * row_stride;
+  };
+
+  // K fragment (A operand) of tile j: lane supplies K[kv0 + c32][HALF*hf + 8*kk + 0..7]
+  u32x4_t kf[NKK];
+  auto load_k = [&](int j) {
+    const int kv = j * kKVT + c32;
+    if (kv < kv_end) {
+      const char* kp = kbase + slot_off(kv) + HALF * hf * ES;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) kf[kk] = as_v(ld16(kp + kk * 16));
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) kf[kk] = u32x4_t{0, 0, 0, 0};
+    }
+  };
+
+  // V staging: chunk c = threadIdx.x + 256*i covers token c / CPR, d = 8*(c % CPR)
+  uint4 vs[VCH];
+  auto load_v = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = threadIdx.x + kThreads * i;
+      const int kv = j * kKVT + c / CPR;
+      vs[i] = kv < kv_end ? ld16(vbase + slot_off(kv) + (c % CPR) * 16) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_vt = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = threadIdx.x + kThreads * i;
+      const int kl = c / CPR;
+      const int d0 = (c % CPR) * 8;
+      const uint32_t w[4] = {vs[i].x, vs[i].y, vs[i].z, vs[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt[buf][d0 + 2 * e][kl] = (uint16_t)(w[e] & 0xffffu);
+        vt[buf][d0 + 2 * e + 1][kl] = (uint16_t)(w[e] >> 16);
+      }
+    }
+  };
+
+  f32x16_t o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
+  float m = -__builtin_inff();
+  float lsum = 0.f;
+
+  if (ntiles > 0) {
+    load_v(0);
+    load_k(0);
+    store_vt(0);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    const int kv0 = j * kKVT;
+    // S^T tile: rows = KV tokens kv0 + 8*(v/4) + 4*hf + v%4, column = this lane's query row
+    f32x16_t sacc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) sacc = mfma32<DT>(kf[kk], qf[kk], sacc);
+
+    const bool more = j + 1 < ntiles;
+    if (more) {
+      load_k(j + 1);
+      load_v(j + 1);
+    }
+
+    float sc[16];
+    const bool need_mask = kv0 + kKVT - 1 > pos_min;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      sc[v] = sacc[v] * a.scale_log2;
+      if (need_mask) {
+        const int kv = kv0 + 8 * (v >> 2) + 4 * hf + (v & 3);
+        sc[v] = kv <= pos ? sc[v] : -__builtin_inff();
+      }
+    }
+    float tmax = sc[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, sc[v]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mn = fmaxf(m, tmax);
+    const bool grow = mn > m + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? fast_exp2(m - mn) : 1.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+      lsum *= alpha;
+      m = grow ? mn : m;
+    }
+    const float mu = m == -__builtin_inff() ? 0.f : m;
+    uint32_t ph[8], pl[8];
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      const float p0 = fast_exp2(sc[v] - mu);
+      const float p1 = fast_exp2(sc[v + 1] - mu);
+      lsum += p0 + p1;
+      const uint32_t h0 = to16<DT>(p0), h1 = to16<DT>(p1);
+      ph[v / 2] = h0 | (h1 << 16);
+      if constexpr (PSPLIT) {
+        const uint32_t l0 = to16<DT>(p0 - from16<DT>(h0));
+        const uint32_t l1 = to16<DT>(p1 - from16<DT>(h1));
+        pl[v / 2] = l0 | (l1 << 16);
+      }
+    }
+    // O^T += V^T P^T over the tile's 32 tokens (two MFMAs of 16 tokens each)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const u32x4_t pb = u32x4_t{ph[4 * c], ph[4 * c + 1], ph[4 * c + 2], ph[4 * c + 3]};
+      u32x4_t pbl;
+      if constexpr (PSPLIT) pbl = u32x4_t{pl[4 * c], pl[4 * c + 1], pl[4 * c + 2], pl[4 * c + 3]};
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint16_t* rowp = &vt[buf][dt * 32 + c32][0];
+        const uint2 x0 = *reinterpret_cast<const uint2*>(rowp + 16 * c + 4 * hf);
+        const uint2 x1 = *reinterpret_cast<const uint2*>(rowp + 16 * c + 8 + 4 * hf);
+        const u32x4_t va = u32x4_t{x0.x, x0.y, x1.x, x1.y};
+        o[dt] = mfma32<DT>(va, pb, o[dt]);
+        if constexpr (PSPLIT) o[dt] = mfma32<DT>(va, pbl, o[dt]);
+      }
+    }
+    if (more) store_vt(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!row_valid) return;
+  const float lt = lsum + __shfl_xor(lsum, 32);
+  const float inv = 1.f / lt;
+  const int64_t orow = ((int64_t)(q0 + tq0 + tok) * a.Hq + (int64_t)kvh * G + g) * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int d = dt * 32 + 8 * v4 + 4 * hf;
+      const float r0 = o[dt][4 * v4] * inv, r1 = o[dt][4 * v4 + 1] * inv;
+      const float r2 = o[dt][4 * v4 + 2] * inv, r3 = o[dt][4 * v4 + 3] * inv;
+      if (a.out_dt == DT_F32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow + d) = make_float4(r0, r1, r2, r3);
+      } else {
+        const bool bf = a.out_dt == DT_BF16;
+        const uint32_t w0 = bf ? (f32_to_bf16_bits(r0) | ((uint32_t)f32_to_bf16_bits(r1) << 16))
+                               : (f32_to_f16_bits(r0) | ((uint32_t)f32_to_f16_bits(r1) << 16));
+        const uint32_t w1 = bf ? (f32_to_bf16_bits(r2) | ((uint32_t)f32_to_bf16_bits(r3) << 16))
+                               : (f32_to_f16_bits(r2) | ((uint32_t)f32_to_f16_bits(r3) << 16));
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow + d) = make_uint2(w0, w1);
+      }
+    }
+  }
+}
+
+// fp32 KV: one wave per (query token, KV head); each lane owns D/64 elements
+// of every head of the group and the wave walks the visible tokens one by one.
+template <int D, int GMAX>
+__global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillArgs a) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x / a.Hkv;
+  const int kvh = blockIdx.x % a.Hkv;
+  int lo = 0, hi = a.S;  // sequence of this row: last s with cu[s] <= row
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_seqlens_q[mid] <= row) lo = mid; else hi = mid;
+  }
+  const int s = lo;
+  const int q0 = a.cu_seqlens_q[s];
+  const int Qs = a.cu_seqlens_q[s + 1] - q0;
+  const int L = min(a.context_lens[s], a.max_ctx);
+  if (Qs > L) return;
+  const int visible = L - Qs + (row - q0) + 1;
+  const int G = a.Hq / a.Hkv;
+  const int32_t* table = a.block_tables + (int64_t)s * a.max_nb;
+  const float* qrow = static_cast<const float*>(a.q) + ((int64_t)row * a.Hq + (int64_t)kvh * G) * D;
+  const float* kc = static_cast<const float*>(a.k_cache);
+  const float* vc = static_cast<const float*>(a.v_cache);
+  for (int g0 = 0; g0 < G; g0 += GMAX) {
+    const int gn = min(GMAX, G - g0);
+    float q[GMAX][EPL], acc[GMAX][EPL], m[GMAX], l[GMAX];
+    for (int g = 0; g < GMAX; ++g) {
+      m[g] = -__builtin_inff();
+      l[g] = 0.f;
+      for (int e = 0; e < EPL; ++e) {
+        q[g][e] = g < gn ? qrow[(int64_t)(g0 + g) * D + lane * EPL + e] : 0.f;
+        acc[g][e] = 0.f;
+      }
+    }
+    for (int t = 0; t < visible; ++t) {
+      const int64_t base = (((int64_t)table[t >> a.log2B] * a.B + (t & (a.B - 1))) * a.Hkv + kvh) * D;
+      float kv[EPL], vv[EPL];
+      for (int e = 0; e < EPL; ++e) {
+        kv[e] = kc[base + lane * EPL + e];
+        vv[e] = vc[base + lane * EPL + e];
+      }
+#pragma unroll
+      for (int g = 0; g < GMAX; ++g) {
+        if (g >= gn) break;
+        float z = 0.f;
+        for (int e = 0; e < EPL; ++e) z = fmaf(q[g][e], kv[e], z);
+        for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+        z *= a.scale_log2;
+        const float mn = fmaxf(m[g], z);
+        const float alpha = fast_exp2(m[g] - mn);
+        const float p = fast_exp2(z - mn);
+        l[g] = l[g] * alpha + p;
+        for (int e = 0; e < EPL; ++e) acc[g][e] = acc[g][e] * alpha + p * vv[e];
+        m[g] = mn;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g)
+      for (int e = 0; e < EPL && g < gn; ++e)
+        store_out(a.out, a.out_dt, ((int64_t)row * a.Hq + (int64_t)kvh * G + g0 + g) * D + lane * EPL + e,
+                  acc[g][e] / l[g]);
+  }
+}
+
+template <int DT, int D>
+pkv_status launch_mfma(const PrefillArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  if (G > kRowsPerWG) return fail(PKV_ERR_UNSUPPORTED, "prefill: group size %d > %d", G, kRowsPerWG);
+  const int TQ = kRowsPerWG / G;
+  const int64_t nqt = (a.max_query_len + TQ - 1) / TQ;
+  const int64_t grid = nqt * a.S * a.Hkv;
+  if (grid == 0) return PKV_OK;
+  if (grid > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "prefill grid too large");
+  constexpr bool split = DT == DT_BF16;
+  hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, split>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     stream, a);
+  return check_launch("paged_attention_prefill");
+}
+
+template <int D>
+pkv_status launch_f32(const PrefillArgs& a, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.Tq * a.Hkv;
+  if (grid == 0) return PKV_OK;
+  if (grid > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "prefill grid too large");
+  hipLaunchKernelGGL((prefill_f32_kernel<D, 8>), dim3((unsigned)grid), dim3(64), 0, stream, a);
+  return check_launch("paged_attention_prefill (f32)");
+}
+
+}  // namespace
+
+pkv_status launch_prefill(int kv_dt, const PrefillArgs& a, hipStream_t stream) {
+  if (kv_dt == DT_F32) {
+    switch (a.D) {
+      case 64: return launch_f32<64>(a, stream);
+      case 128: return launch_f32<128>(a, stream);
+    }
+  } else if (kv_dt == DT_BF16) {
+    switch (a.D) {
+      case 64: return launch_mfma<DT_BF16, 64>(a, stream);
+      case 128: return launch_mfma<DT_BF16, 128>(a, stream);
+    }
+  } else if (kv_dt == DT_F16) {
+    switch (a.D) {
+      case 64: return launch_mfma<DT_F16, 64>(a, stream);
+      case 128: return launch_mfma<DT_F16, 128>(a, stream);
+    }
+  }
+  return fail(PKV_ERR_UNSUPPORTED, "prefill: kv dtype %d, head_dim %d", kv_dt, a.D);
+}
+
+}  // namespace pkv

@@ -29,8 +29,10 @@ kernel that reads them shows it.
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 import math
+import os
 
 import numpy as np
 
@@ -146,12 +148,11 @@ class PagedBatch:
         v = np.empty(shape, STORAGE_NP[self.dtype])
         k[:n], v[:n] = self.k_blocks, self.v_blocks
         k[n:], v[n:] = NAN_BITS[self.dtype], NAN_BITS[self.dtype]
-        remap = {int(b): i for i, b in enumerate(self.block_ids)}
+        order = np.argsort(self.block_ids, kind="stable")
+        ids_sorted = self.block_ids[order]
         tables = np.full_like(self.block_tables, -1)
-        for s in range(self.S):
-            nb = -(-int(self.context_lens[s]) // self.B)
-            for j in range(nb):
-                tables[s, j] = remap[int(self.block_tables[s, j])]
+        used = self.block_tables >= 0          # padding entries are -1
+        tables[used] = order[np.searchsorted(ids_sorted, self.block_tables[used])]
         return k, v, tables
 
     def full_pool(self):
@@ -164,13 +165,26 @@ class PagedBatch:
         return k, v
 
 
-def _normal(rng: np.random.Generator, shape, dtype: str, chunk: int = 1 << 24) -> np.ndarray:
-    """N(0, 1) values rounded to ``dtype``, drawn in chunks to bound host memory."""
+def _normal(rng: np.random.Generator, shape, dtype: str, chunk: int = 1 << 22) -> np.ndarray:
+    """N(0, 1) values rounded to ``dtype``.  Large draws are split into chunks, each
+    from its own generator seeded by one draw of ``rng``, filled in parallel;
+    the result depends only on ``rng``'s state and the shape."""
     n = int(np.prod(shape))
     out = np.empty(n, STORAGE_NP[dtype])
-    for i in range(0, n, chunk):
-        m = min(chunk, n - i)
-        out[i:i + m] = to_storage(rng.standard_normal(m, dtype=np.float32), dtype)
+    if n <= chunk:
+        out[:] = to_storage(rng.standard_normal(n, dtype=np.float32), dtype)
+        return out.reshape(shape)
+    starts = list(range(0, n, chunk))
+    seeds = rng.integers(0, 2**63 - 1, size=len(starts))
+
+    def fill(i):
+        lo = starts[i]
+        m = min(chunk, n - lo)
+        g = np.random.default_rng(int(seeds[i]))
+        out[lo:lo + m] = to_storage(g.standard_normal(m, dtype=np.float32), dtype)
+
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        list(ex.map(fill, range(len(starts))))
     return out.reshape(shape)
 
 

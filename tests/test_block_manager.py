@@ -1,0 +1,179 @@
+"""Host block manager against the pages' worked examples and invariants (CPU)."""
+import numpy as np
+import pytest
+
+import paged_kv_cache_71_amd as pkv
+from conftest import golden
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    pkv.load_library()
+
+
+def _check_invariants(bm, seqs):
+    bm.check()                                   # refcount == holders, free list sane
+    for s in seqs:
+        n = bm.seq_len(s)
+        assert len(bm.table(s)) * bm.block_size - n < bm.block_size   # waste < one block
+
+
+@pytest.mark.parametrize("case", golden("kwkr_kvcache_manager.json")["cases"], ids=lambda c: c["name"])
+def test_kwkr_kvcache_manager_example(case):
+    B = case["block_size"]
+    bm = pkv.BlockManager(case["num_blocks"], B)
+    if case.get("expect_oom"):
+        with pytest.raises(pkv.PkvOOM):
+            bm.add_seq(case["prompt_len"])
+        assert bm.num_free() == case["num_blocks"]          # nothing taken on failure
+        return
+    s = bm.add_seq(case["prompt_len"])
+    assert len(bm.table(s)) == case["after_prefill"]["table_len"]
+    if "free" in case["after_prefill"]:
+        assert bm.num_free() == case["after_prefill"]["free"]
+    for step in case["decode_steps"]:
+        while bm.seq_len(s) < step["seq_len"]:
+            bm.append_token(s)
+        assert len(bm.table(s)) == step["table_len"]
+        if "free" in step:
+            assert bm.num_free() == step["free"]
+        _check_invariants(bm, [s])
+    # blocks come from the front of the free list: 0, 1, 2, ...
+    assert bm.table(s) == list(range(len(bm.table(s))))
+
+
+def test_cs349d_block_table_walk():
+    g = golden("cs349d_block_table_walk.json")
+    B = g["block_size"]
+    bm = pkv.BlockManager(len(g["free_order"]), B, free_order=g["free_order"])
+    a = bm.add_seq(g["prefill"]["A"])
+    b = bm.add_seq(g["prefill"]["B"])
+    steps = {st["step"]: st for st in g["steps"]}
+    for step in range(0, max(steps) + 1):
+        if step > 0:
+            bm.append_token(a)
+            bm.append_token(b)
+        if step in steps:
+            st = steps[step]
+            for sid, key in ((a, "A"), (b, "B")):
+                assert bm.seq_len(sid) == st[key]["len"]
+                assert bm.table(sid) == st[key]["table"]
+                last_fill = bm.seq_len(sid) - (len(bm.table(sid)) - 1) * B
+                assert last_fill == st[key]["last_fill"]
+            assert bm.num_free() == st["free"]
+        _check_invariants(bm, [a, b])
+
+
+def test_s06_block_table_display():
+    g = golden("s06_block_table_display.json")
+    bm = pkv.BlockManager(g["num_blocks"], g["block_size"])
+    for r in g["requests"]:
+        s = bm.add_seq(r["tokens"])
+        assert bm.table(s) == r["table"], r["name"]
+
+
+@pytest.mark.parametrize("item", golden("cow_accounting.json")["cases"][0]["items"],
+                         ids=lambda i: f"L{i['prompt_len']}n{i['n']}")
+def test_cow_copies_n_minus_1_or_0(item):
+    B = golden("cow_accounting.json")["cases"][0]["block_size"]
+    bm = pkv.BlockManager(256, B, free_order=np.random.default_rng(1).permutation(256))
+    parent = bm.add_seq(item["prompt_len"])
+    samples = [parent] + [bm.fork(parent) for _ in range(item["n"] - 1)]
+    for blk in bm.table(parent):
+        assert bm.refcount(blk) == item["n"]
+    copies = []
+    for s in samples:                             # each sample writes its first token
+        slot, cow = bm.append_token(s)
+        if cow:
+            copies.append(cow)
+        _check_invariants(bm, samples)
+    assert len(copies) == item["copies"]
+    if copies:                                    # all copies read the shared last block
+        assert len({src for src, _ in copies}) == 1
+        assert len({dst for _, dst in copies}) == len(copies)
+        assert bm.refcount(copies[0][0]) == 1     # the last writer kept it
+
+
+def test_parallel_sampling_block_count_cs349d_exercise_2():
+    c = golden("cow_accounting.json")["cases"][1]
+    B, Lp, n, Lo = c["block_size"], c["prompt_len"], c["n"], c["output_len"]
+    bm = pkv.BlockManager(1024, B)
+    parent = bm.add_seq(Lp)
+    samples = [parent] + [bm.fork(parent) for _ in range(n - 1)]
+    for _ in range(Lo):
+        for s in samples:
+            bm.append_token(s)
+    _check_invariants(bm, samples)
+    assert 1024 - bm.num_free() == c["shared_blocks_total"]
+    un = pkv.BlockManager(1024, B)
+    for _ in range(n):
+        un.add_seq(Lp + Lo)
+    assert 1024 - un.num_free() == c["unshared_blocks_total"]
+
+
+def test_prompt_sharing_s06():
+    c = golden("cow_accounting.json")["cases"][2]
+    bm = pkv.BlockManager(4096, c["block_size"])
+    parent = bm.add_seq(c["prompt_len"])
+    for _ in range(c["n"] - 1):
+        bm.fork(parent)
+    assert 4096 - bm.num_free() == c["shared_blocks"]
+    un = pkv.BlockManager(4096, c["block_size"])
+    for _ in range(c["n"]):
+        un.add_seq(c["prompt_len"])
+    assert 4096 - un.num_free() == c["unshared_blocks"]
+
+
+def test_free_only_decrements_shared_blocks():
+    """Freeing a beam whose blocks another beam still holds only drops refcounts
+    (CMU 11-868 lecture 24, answer 5)."""
+    bm = pkv.BlockManager(32, 4)
+    a = bm.add_seq(10)
+    b = bm.fork(a)
+    free0 = bm.num_free()
+    bm.free_seq(a)
+    assert bm.num_free() == free0
+    assert all(bm.refcount(x) == 1 for x in bm.table(b))
+    bm.free_seq(b)
+    assert bm.num_free() == 32
+    bm.check()
+
+
+def test_random_ops_keep_refcount_invariant():
+    """After every operation, tables holding each block == its refcount (S06
+    chapter, 'reference counts must be exact')."""
+    rng = np.random.default_rng(0)
+    bm = pkv.BlockManager(200, 4, free_order=rng.permutation(200))
+    live = []
+    for _ in range(2000):
+        op = rng.integers(0, 4)
+        try:
+            if op == 0 or not live:
+                live.append(bm.add_seq(int(rng.integers(0, 20))))
+            elif op == 1:
+                bm.append_token(live[rng.integers(len(live))])
+            elif op == 2:
+                live.append(bm.fork(live[rng.integers(len(live))]))
+            else:
+                bm.free_seq(live.pop(rng.integers(len(live))))
+        except pkv.PkvOOM:
+            before = bm.num_free()
+            bm.check()
+            assert bm.num_free() == before
+        _check_invariants(bm, live)
+
+
+def test_slots_follow_table():
+    bm = pkv.BlockManager(16, 4, free_order=np.arange(16)[::-1].copy())
+    s = bm.add_seq(7)
+    t = bm.table(s)
+    assert bm.slots(s, 0, 7).tolist() == [t[p // 4] * 4 + p % 4 for p in range(7)]
+    slot, cow = bm.append_token(s)
+    assert slot == t[1] * 4 + 3 and cow is None
+    with pytest.raises(pkv.PkvError):
+        bm.slots(s, 5, 4)                        # past the length
+
+
+def test_bad_free_order_rejected():
+    with pytest.raises(pkv.PkvError):
+        pkv.BlockManager(4, 4, free_order=[0, 1, 1, 2])
