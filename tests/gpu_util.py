@@ -28,14 +28,41 @@ def nan_fill(shape, dtype: str) -> torch.Tensor:
     return torch.full(shape, float("nan"), dtype=TORCH_DT[dtype], device="cuda")
 
 
+def validate(b: W.PagedBatch) -> None:
+    """Host-side check that every index the device will use is in range."""
+    ids = b.block_ids
+    if ids.size and (ids.min() < 0 or ids.max() >= b.NB):
+        raise ValueError(f"{b.name}: block id outside the pool of {b.NB}")
+    if np.unique(ids).size != ids.size:
+        raise ValueError(f"{b.name}: duplicate data block ids")
+    idset = set(ids.tolist())
+    if np.any(b.context_lens < 0) or np.any(b.context_lens > b.max_nb * b.B):
+        raise ValueError(f"{b.name}: context length beyond the table capacity")
+    for s in range(b.S):
+        nb = -(-int(b.context_lens[s]) // b.B)
+        row = b.block_tables[s]
+        if not set(row[:nb].tolist()) <= idset or np.any(row[nb:] != -1):
+            raise ValueError(f"{b.name}: table row {s} refers to a block without data")
+    if b.new_slots.size and (b.new_slots.max() >= b.NB * b.B or b.new_slots.min() < -1):
+        raise ValueError(f"{b.name}: slot outside the pool")
+    if b.cu_seqlens_q is not None:
+        cu = b.cu_seqlens_q
+        if cu[0] != 0 or np.any(np.diff(cu) < 0) or cu[-1] != b.q.shape[0]:
+            raise ValueError(f"{b.name}: bad cu_seqlens_q")
+        if np.any(np.diff(cu) > b.context_lens):
+            raise ValueError(f"{b.name}: chunk longer than its context")
+    elif b.q.shape[0] != b.S:
+        raise ValueError(f"{b.name}: q rows != sequences")
+
+
 class DevBatch:
     """A PagedBatch on the device: poisoned pool of NB blocks with the data
     blocks scattered in, tables (padding -1), lengths and q."""
 
-    def __init__(self, batch: W.PagedBatch, NB: int | None = None):
+    def __init__(self, batch: W.PagedBatch):
+        validate(batch)            # every index checked on the host before any device work
         self.b = batch
-        NB = batch.NB if NB is None else NB
-        shape = (NB, batch.B, batch.Hkv, batch.D)
+        shape = (batch.NB, batch.B, batch.Hkv, batch.D)
         self.k_cache = nan_fill(shape, batch.dtype)
         self.v_cache = nan_fill(shape, batch.dtype)
         idx = torch.from_numpy(batch.block_ids).cuda()

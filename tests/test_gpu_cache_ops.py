@@ -20,13 +20,14 @@ def _rand_bits(rng, shape, dtype):
 @pytest.mark.parametrize("D,B,Hkv", [(64, 4, 4), (128, 16, 8), (128, 1, 2), (64, 32, 1)])
 def test_reshape_and_cache_bit_exact(gpu_lib, dtype, D, B, Hkv):
     rng = np.random.default_rng(D + B + Hkv)
-    NB, T = 37, 61
+    T = 61
+    NB = max(37, -(-2 * T // B))
     k0, v0 = _rand_bits(rng, (NB, B, Hkv, D), dtype), _rand_bits(rng, (NB, B, Hkv, D), dtype)
     key, val = _rand_bits(rng, (T, Hkv, D), dtype), _rand_bits(rng, (T, Hkv, D), dtype)
-    slots = rng.permutation(NB * B)[:T].astype(np.int64)
-    slots[[0, T // 2, T - 1]] = -1            # padding tokens
-    slots[1] = 0
-    slots[2] = NB * B - 1                     # first and last slot of the pool
+    # distinct slots: the first and last of the pool included, three padding tokens (-1)
+    slots = np.concatenate([[0, NB * B - 1], 1 + rng.permutation(NB * B - 2)[:T - 2]]).astype(np.int64)
+    slots[[2, T // 2, T - 1]] = -1
+    assert np.unique(slots[slots >= 0]).size == np.sum(slots >= 0) and slots.max() < NB * B
     kc, vc = to_dev(k0, dtype), to_dev(v0, dtype)
     gpu_lib.reshape_and_cache(to_dev(key, dtype), to_dev(val, dtype), kc, vc,
                               torch.from_numpy(slots).cuda())

@@ -25,10 +25,10 @@ def gpu_prefill(pkv, db: DevBatch, out_dtype="f32", write_chunk=True):
     return out
 
 
-def check(pkv, b, rows=None, NB=None):
+def check(pkv, b, rows=None):
     print(f"[prefill] {b.name} S={b.S} Hq={b.Hq} Hkv={b.Hkv} D={b.D} B={b.B} {b.dtype} "
           f"Tq={b.q.shape[0]} maxL={b.max_context_len}", flush=True)
-    db = DevBatch(b, NB)
+    db = DevBatch(b)
     out = gpu_prefill(pkv, db)
     k, v, tables = b.compact_pool()
     ref = oracle.prefill(b.q, b.cu_seqlens_q, k, v, b.dtype, tables, b.context_lens, b.scale, rows=rows)
