@@ -97,8 +97,9 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
  *   max_context_len: host bound >= every context_lens[s] (sizes the grid)
  *   scale          : softmax scale, usually 1/sqrt(D)
  *   workspace      : device scratch of at least pkv_decode_workspace_size()
- *                    bytes (may be NULL when that size is 0); contents on
- *                    entry are ignored.
+ *                    bytes (a size that depends on the arguments only, not on
+ *                    the device); contents on entry are ignored.  It holds the
+ *                    partial softmax states of rows split between waves.
  * out[s, h, :] = sum_t softmax_t(scale * q[s,h,:] . K[s,t,:]) V[s,t,:],
  * computed in fp32.  The summation order depends only on logical positions,
  * so the result is bit-identical under any permutation of physical blocks and

@@ -1,6 +1,7 @@
 // abi.hip -- the C ABI of libpkv: host-side validation of every scalar argument,
 // choice of kernel instantiation, launch on the caller's stream, and error
 // reporting.  No device memory is allocated here.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -92,8 +93,13 @@ pkv_status pkv_decode_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t
   PKV_REQUIRE(S >= 0 && Hq > 0 && Hkv > 0 && D > 0 && B > 0 && max_context_len >= 0,
               PKV_ERR_INVALID_ARG, "decode_workspace_size: bad sizes");
   PKV_REQUIRE(Hq % Hkv == 0, PKV_ERR_INVALID_ARG, "decode_workspace_size: Hq %% Hkv != 0");
+  if (S == 0) {
+    *bytes = 0;
+    return PKV_OK;
+  }
   DecodePlan plan;
-  plan_decode(S, Hq, Hkv, D, B, max_context_len, &plan);
+  const pkv_status st = plan_decode(S, Hq, Hkv, D, B, max_context_len, &plan);
+  if (st != PKV_OK) return st;
   *bytes = plan.workspace_bytes;
   return PKV_OK;
 }
@@ -120,11 +126,14 @@ pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void
               "decode: max_context_len %d exceeds table capacity %d x %d", max_context_len,
               max_blocks_per_seq, B);
   PKV_REQUIRE(scale == scale, PKV_ERR_INVALID_ARG, "decode: scale is NaN");
+  PKV_REQUIRE((int64_t)B * Hkv * D * dt_bytes(kv_dtype) < ((int64_t)1 << 31), PKV_ERR_UNSUPPORTED,
+              "decode: one block of one pool must be smaller than 2 GiB");
   if (S == 0) return PKV_OK;
   PKV_REQUIRE(out && q && k_cache && v_cache && block_tables && context_lens, PKV_ERR_INVALID_ARG,
               "decode: null pointer");
   DecodePlan plan;
-  plan_decode(S, Hq, Hkv, D, B, max_context_len, &plan);
+  const pkv_status pst = plan_decode(S, Hq, Hkv, D, B, max_context_len, &plan);
+  if (pst != PKV_OK) return pst;
   PKV_REQUIRE(workspace_bytes >= plan.workspace_bytes && (plan.workspace_bytes == 0 || workspace),
               PKV_ERR_WORKSPACE, "decode: workspace of %zu bytes needed, %zu given",
               plan.workspace_bytes, workspace_bytes);
@@ -135,8 +144,10 @@ pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.ws_acc = static_cast<float*>(workspace);
-  a.ws_ml = a.ws_acc ? a.ws_acc + (size_t)S * Hq * plan.np_max * D : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_ps = reinterpret_cast<int32_t*>(ws + plan.ws_ps_off);
+  a.ws_ml = reinterpret_cast<float*>(ws + plan.ws_ml_off);
+  a.ws_acc = reinterpret_cast<float*>(ws + plan.ws_acc_off);
   a.max_nb = max_blocks_per_seq;
   a.S = S;
   a.Hq = Hq;
@@ -144,14 +155,14 @@ pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void
   a.D = D;
   a.B = B;
   a.log2B = ilog2(B);
-  a.max_ctx = max_context_len;
-  a.part_tokens = plan.part_tokens;
-  a.np_max = plan.np_max;
   a.gc = plan.gc;
-  a.n_hchunks = (Hq / Hkv) / plan.gc;
+  a.n_hchunks = plan.n_hchunks;
+  a.rows_per_seq = plan.rows_per_seq;
+  a.n_waves = 0;  // set per launch
+  a.max_ctx = max_context_len;
   a.out_dt = out_dtype;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return launch_decode(kv_dtype, a, static_cast<hipStream_t>(stream));
+  return launch_decode(kv_dtype, plan, a, static_cast<hipStream_t>(stream));
 }
 
 pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* q,

@@ -53,6 +53,30 @@ __device__ __forceinline__ void store_out(void* out, int out_dt, int64_t idx, fl
   }
 }
 
+// Store N consecutive fp32 results (N = 4 or 8, idx a multiple of N) into an
+// output tensor of dtype out_dt with 16- or 8-byte stores.
+template <int N>
+__device__ __forceinline__ void store_out_vec(void* out, int out_dt, int64_t idx, const float* v) {
+  static_assert(N == 4 || N == 8, "vector width");
+  if (out_dt == DT_F32) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + idx);
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) p[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  } else {
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const uint32_t lo = out_dt == DT_BF16 ? f32_to_bf16_bits(v[2 * i]) : f32_to_f16_bits(v[2 * i]);
+      const uint32_t hi =
+          out_dt == DT_BF16 ? f32_to_bf16_bits(v[2 * i + 1]) : f32_to_f16_bits(v[2 * i + 1]);
+      w[i] = lo | (hi << 16);
+    }
+    uint16_t* base = static_cast<uint16_t*>(out) + idx;
+    if constexpr (N == 8) *reinterpret_cast<uint4*>(base) = make_uint4(w[0], w[1], w[2], w[3]);
+    else *reinterpret_cast<uint2*>(base) = make_uint2(w[0], w[1]);
+  }
+}
+
 // ---- launchers (one per kernel family) -------------------------------------------
 pkv_status launch_reshape_and_cache(const void* key, const void* value, void* k_cache,
                                     void* v_cache, const int64_t* slot_mapping, int32_t T,
@@ -63,9 +87,12 @@ pkv_status launch_copy_blocks(void* const* k_caches, void* const* v_caches, int3
                               hipStream_t stream);
 
 struct DecodePlan {
-  int part_tokens;  // tokens per partition (multiple of 64)
-  int np_max;       // partitions of the longest sequence
-  int gc;           // query heads per workgroup (divides G)
+  int gc;               // query heads per row (divides G)
+  int n_hchunks;        // G / gc
+  int rows_per_seq;     // Hkv * n_hchunks
+  int max_waves;        // waves of the largest split launch (sizes the workspace)
+  int seqs_per_launch;  // sequences handled by one split + merge launch pair
+  size_t ws_ps_off, ws_ml_off, ws_acc_off;  // workspace layout (bytes)
   size_t workspace_bytes;
 };
 pkv_status plan_decode(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
@@ -78,16 +105,17 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_acc;  // [S, Hq, np_max, D]
-  float* ws_ml;   // [S, Hq, np_max, 2]  (running max in log2 units, sum)
+  int32_t* ws_ps;   // [S + 1] prefix of tile counts (written by the split kernel)
+  float* ws_ml;     // [2 * n_waves, gc, 2] partial (c * max, sum) in log2 units
+  float* ws_acc;    // [2 * n_waves, gc, D] partial accumulators
   int32_t max_nb;
   int32_t S, Hq, Hkv, D, B, log2B;
-  int32_t part_tokens, np_max, n_hchunks, gc;
-  int32_t max_ctx;   // context lengths are clamped to this (<= max_nb * B)
+  int32_t gc, n_hchunks, rows_per_seq, n_waves;
+  int32_t max_ctx;       // context lengths are clamped to this (<= max_nb * B)
   int32_t out_dt;
-  float scale_log2;  // softmax scale * log2(e)
+  float scale_log2;      // softmax scale * log2(e)
 };
-pkv_status launch_decode(int kv_dt, const DecodeArgs& a, hipStream_t stream);
+pkv_status launch_decode(int kv_dt, const DecodePlan& plan, DecodeArgs a, hipStream_t stream);
 
 struct PrefillArgs {
   void* out;
