@@ -194,8 +194,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "paged_attention_decode (partition + reduce launches)",
+            "traffic": measured_traffic(),
+            "kernel": "paged_attention_decode (decode_split_kernel + decode_merge_kernel launches)",
             "ms_per_launch": round(dec_ms, 5),
         },
     }
@@ -210,11 +210,13 @@ def main():
 
     if not args.headline_only:
         rows = {}
-        # decode with an L2/MALL flush before every launch
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # decode with cold caches: before every launch a 2 GiB buffer is READ
+        # (larger than L2 + the 256 MB Infinity Cache), which evicts the KV
+        # without leaving dirty lines whose write-back would be charged to decode
+        flush = torch.ones(1 << 29, dtype=torch.float32, device=dev)
         fl = []
         for _ in range(10):
-            flush.random_(0, 255)
+            flush.sum()
             a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             d.decode()
@@ -276,6 +278,22 @@ def main():
         result["cpu_baseline"] = cpu_baseline(b, args.cpu_sample_tokens)
 
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per decode step from the committed rocprofv3 counter runs, if
+    they were taken on the decode source as it is now (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_llama3_8b_bf16_traffic.json")
+    src = os.path.join(ROOT, "paged_kv_cache_71_amd", "csrc", "decode.hip")
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("decode_hip_sha256") != digest:
+        return None
+    return rec.get("traffic_bytes_per_step")
 
 
 def cpu_baseline(b, sample_tokens):
