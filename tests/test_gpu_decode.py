@@ -75,6 +75,20 @@ def test_partition_boundaries_and_edges(gpu_lib):
     assert torch.all(out[0] == 0) and torch.all(out[13] == 0)        # empty context -> zeros
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_long_rows_span_many_waves(gpu_lib, dtype):
+    """One 8192-token sequence: each of its 8 rows (KV heads) is cut across
+    about a hundred waves, so the merge runs many batches of partial states."""
+    check(gpu_lib, W.decode_batch(5, [8192], 32, 8, 128, 16, dtype))
+
+
+def test_more_sequences_than_one_launch(gpu_lib):
+    """4100 short sequences (some empty): more than one split + merge launch pair."""
+    lengths = np.random.default_rng(3).integers(0, 40, 4100)
+    out, _ = check(gpu_lib, W.decode_batch(6, lengths, 8, 2, 64, 4, "f32"))
+    assert torch.all(out[torch.from_numpy(lengths == 0).cuda()] == 0)
+
+
 def test_single_token_context_returns_value_exactly(gpu_lib):
     b = W.decode_batch(3, [1, 1, 1], 8, 2, 128, 16, "bf16")
     db = DevBatch(b)
