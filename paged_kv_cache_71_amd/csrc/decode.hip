@@ -307,7 +307,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
   const int N = rfl(sm_ps[S]);
   const int NW = gridDim.x * kWaves;
   const int C = (N + NW - 1) / NW;
-  const int w = blockIdx.x * kWaves + wave;
+  // XCD-aware range order: workgroups are dispatched round-robin over the 8
+  // XCDs (blockIdx % 8), so consecutive ranges -- neighbouring rows, e.g. the
+  // samples of one prompt aliasing the same prefix blocks -- go to workgroups
+  // of the same XCD and share its L2 (measured 3-5% faster on aliased batches,
+  // neutral otherwise).
+  const int nwg = gridDim.x;
+  const int wg_rank = (nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int w = wg_rank * kWaves + wave;
   const int x0 = w * C;
   const int x1 = min(x0 + C, N);
   if (x0 >= x1) return;
