@@ -44,15 +44,23 @@ def parse():
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other rows and the CPU baseline (used under the profilers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill row (used under the profilers)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="context tokens of the bounded oracle sample (0: the whole batch)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE run and a "
+                         "WRITE_SIZE run (both with --calibrate-copy) into the traffic record under profiles/")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(sharding is by sequence, KV head or context; see the design notes). "
@@ -129,6 +137,27 @@ def main():
         torch.cuda.synchronize()
         t = np.array([a.elapsed_time(z) for a, z in evs])
         return float(t.mean()), float(np.median(t))
+
+    def prefill_row():
+        """Chunked causal prefill of 8 sequences x 512 new tokens (bf16)."""
+        pb = W.prefill_bf16(args.seed)
+        pd = Dev(pb)
+        ms, _ = time_fn(pd.prefill, 5, warm=2)
+        flops = 0
+        for s in range(pb.S):
+            Q = int(pb.cu_seqlens_q[s + 1] - pb.cu_seqlens_q[s])
+            L = int(pb.context_lens[s])
+            flops += 4 * pb.Hq * pb.D * sum(L - Q + i + 1 for i in range(Q))
+        log(f"[bench] prefill: {ms:.3f} ms, {flops / ms / 1e9:.0f} TFLOP/s")
+        pd.free()
+        del pd
+        torch.cuda.empty_cache()
+        return {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 1),
+                "frac_of_bf16_peak": round(flops / ms / 1e9 / BF16_DENSE_TFLOPS, 4)}
+
+    if args.prefill_only:
+        print(json.dumps({"prefill_bf16_8x512": prefill_row()}), flush=True)
+        return
 
     # ------------------------------------------------------------ headline
     t0 = time.time()
@@ -259,19 +288,7 @@ def main():
         del kc, vc
         torch.cuda.empty_cache()
 
-        pb = W.prefill_bf16(args.seed)
-        pd = Dev(pb)
-        ms, _ = time_fn(pd.prefill, 5, warm=2)
-        flops = 0
-        for s in range(pb.S):
-            Q = int(pb.cu_seqlens_q[s + 1] - pb.cu_seqlens_q[s])
-            L = int(pb.context_lens[s])
-            flops += 4 * pb.Hq * pb.D * sum(L - Q + i + 1 for i in range(Q))
-        rows["prefill_bf16_8x512"] = {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 1),
-                                      "frac_of_bf16_peak": round(flops / ms / 1e9 / BF16_DENSE_TFLOPS, 4)}
-        log(f"[bench] prefill: {ms:.3f} ms, {flops / ms / 1e9:.0f} TFLOP/s")
-        pd.free()
-        del pd
+        rows["prefill_bf16_8x512"] = prefill_row()
         result["rows"] = rows
 
     if not args.headline_only and not args.no_cpu_baseline:
@@ -280,15 +297,64 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "decode_llama3_8b_bf16_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_71_amd", "csrc", "decode.hip")
+COPY_BYTES = 1 << 30
+
+
+def _counter_means(path):
+    """Per-kernel mean of one rocprofv3 counter (KiB per dispatch), and the
+    value the largest __amd_rocclr_copyBuffer dispatch (the 1 GiB copy) read."""
+    import csv
+    per, copy = {}, 0.0
+    for r in csv.DictReader(open(path)):
+        name, val = r["Kernel_Name"], float(r["Counter_Value"])
+        if "__amd_rocclr_copyBuffer" in name:
+            copy = max(copy, val)
+        for k in ("decode_split_kernel", "decode_merge_kernel", "reshape_and_cache_kernel"):
+            if k in name:
+                per.setdefault(k, []).append(val)
+    if copy <= 0:
+        raise SystemExit(f"{path}: no 1 GiB copy dispatch (run the counter pass with --calibrate-copy)")
+    return {k: float(np.mean(v)) for k, v in per.items()}, copy
+
+
+def record_traffic(fetch_csv, write_csv):
+    """Scale FETCH_SIZE / WRITE_SIZE so that the 1 GiB copy reads and writes
+    exactly 1 GiB, then store bytes per dispatch of the decode kernels together
+    with the sha256 of the decode source they were measured on."""
+    import hashlib
+    from paged_kv_cache_71_amd import workloads as W
+    fetch, fcopy = _counter_means(fetch_csv)
+    write, wcopy = _counter_means(write_csv)
+    fs, ws = COPY_BYTES / 1024 / fcopy, COPY_BYTES / 1024 / wcopy
+    per = {}
+    for k, short in (("decode_split_kernel", "split"), ("decode_merge_kernel", "merge"),
+                     ("reshape_and_cache_kernel", "reshape")):
+        per[short] = {"read": round(fetch[k] * 1024 * fs), "write": round(write[k] * 1024 * ws)}
+    step = sum(per[k]["read"] + per[k]["write"] for k in ("split", "merge"))
+    rec = {
+        "workload": "Llama-3-8B-shaped decode, bf16 KV, 256 sequences, 32 q / 8 kv heads, head_dim 128, block 16",
+        "decode_hip_sha256": hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest(),
+        "traffic_bytes_per_step": step,
+        "algorithmic_kv_bytes_per_step": int(W.llama3_8b_bf16(0).kv_read_bytes()),
+        "fetch_scale": round(fs, 5),
+        "write_scale": round(ws, 5),
+        "per_kernel_bytes": per,
+    }
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def measured_traffic():
     """HBM bytes per decode step from the committed rocprofv3 counter runs, if
     they were taken on the decode source as it is now (else None)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "decode_llama3_8b_bf16_traffic.json")
-    src = os.path.join(ROOT, "paged_kv_cache_71_amd", "csrc", "decode.hip")
     try:
-        rec = json.load(open(path))
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        rec = json.load(open(TRAFFIC_JSON))
+        digest = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
     except (OSError, ValueError):
         return None
     if rec.get("decode_hip_sha256") != digest:

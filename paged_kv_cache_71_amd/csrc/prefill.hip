@@ -65,17 +65,35 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t a, const u32x4_t b, f32
   }
 }
 
-// fp32 -> 16-bit storage value of dtype DT (round to nearest even).
+// Two fp32 values -> one word of two 16-bit values of dtype DT (x in the low
+// half), round to nearest even, with one packed hardware conversion.
 template <int DT>
-__device__ __forceinline__ uint32_t to16(float x) {
-  if constexpr (DT == DT_BF16) return f32_to_bf16_bits(x);
-  else return f32_to_f16_bits(x);
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  if constexpr (DT == DT_BF16) {
+    typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{x, y}), b16x2_t));
+  } else {
+    typedef _Float16 h16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{x, y}), h16x2_t));
+  }
+}
+// The two 16-bit values of a word back in fp32 (exact).
+template <int DT>
+__device__ __forceinline__ float lo16(uint32_t w) {
+  if constexpr (DT == DT_BF16) return __uint_as_float(w << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)w);
 }
 template <int DT>
-__device__ __forceinline__ float from16(uint32_t bits) {
-  if constexpr (DT == DT_BF16) return __uint_as_float(bits << 16);
-  else return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+__device__ __forceinline__ float hi16(uint32_t w) {
+  if constexpr (DT == DT_BF16) return __uint_as_float(w & 0xffff0000u);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
+
+template <bool V>
+struct BoolTag {
+  static constexpr bool value = V;
+};
 
 __device__ __forceinline__ u32x4_t as_v(uint4 x) { return u32x4_t{x.x, x.y, x.z, x.w}; }
 
@@ -256,13 +274,9 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
       const float p0 = fast_exp2(sc[v] - mu);
       const float p1 = fast_exp2(sc[v + 1] - mu);
       lsum += p0 + p1;
-      const uint32_t h0 = to16<DT>(p0), h1 = to16<DT>(p1);
-      ph[v / 2] = h0 | (h1 << 16);
-      if constexpr (PSPLIT) {
-        const uint32_t l0 = to16<DT>(p0 - from16<DT>(h0));
-        const uint32_t l1 = to16<DT>(p1 - from16<DT>(h1));
-        pl[v / 2] = l0 | (l1 << 16);
-      }
+      const uint32_t h = pack2<DT>(p0, p1);
+      ph[v / 2] = h;
+      if constexpr (PSPLIT) pl[v / 2] = pack2<DT>(p0 - lo16<DT>(h), p1 - hi16<DT>(h));
     }
     // O^T += V^T P^T over the tile's 32 tokens (two MFMAs of 16 tokens each)
 #pragma unroll
@@ -542,7 +556,9 @@ __global__ __launch_bounds__(kThreads) void prefill_tile_kernel(const PrefillArg
   }
   lds_barrier();
 
-  for (int j = 0; j < ntiles; ++j) {
+  // one KV tile; MASK: some token of the tile lies after some row's position
+  auto tile = [&](const int j, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = j & 1;
     const int kv0 = j * kTileKV;
     const char* K = lk[buf];
@@ -560,7 +576,6 @@ __global__ __launch_bounds__(kThreads) void prefill_tile_kernel(const PrefillArg
         for (int c = 0; c < QB; ++c) st[mb][c] = mfma16<DT>(ka, qf[c][kk], st[mb][c]);
       }
     }
-    const bool need_mask = kv0 + kTileKV - 1 > pos_min;
     u32x4_t ph[QB], pl[QB];
     bool grow_any = false;
     float sc[QB][8], mnew[QB];
@@ -572,7 +587,7 @@ __global__ __launch_bounds__(kThreads) void prefill_tile_kernel(const PrefillArg
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v = st[mb][c][i] * a.scale_log2;
-          if (need_mask) {
+          if constexpr (MASK) {
             const int kv = kv0 + 16 * mb + 4 * g4 + i;
             v = kv <= pos[c] ? v : -__builtin_inff();
           }
@@ -605,13 +620,9 @@ __global__ __launch_bounds__(kThreads) void prefill_tile_kernel(const PrefillArg
         const float p0 = fast_exp2(sc[c][k] - mu);
         const float p1 = fast_exp2(sc[c][k + 1] - mu);
         lsum[c] += p0 + p1;
-        const uint32_t h0 = to16<DT>(p0), h1 = to16<DT>(p1);
-        hw[k / 2] = h0 | (h1 << 16);
-        if constexpr (PSPLIT) {
-          const uint32_t l0 = to16<DT>(p0 - from16<DT>(h0));
-          const uint32_t l1 = to16<DT>(p1 - from16<DT>(h1));
-          lw[k / 2] = l0 | (l1 << 16);
-        }
+        const uint32_t h = pack2<DT>(p0, p1);
+        hw[k / 2] = h;
+        if constexpr (PSPLIT) lw[k / 2] = pack2<DT>(p0 - lo16<DT>(h), p1 - hi16<DT>(h));
       }
       ph[c] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
       if constexpr (PSPLIT) pl[c] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
@@ -637,7 +648,12 @@ __global__ __launch_bounds__(kThreads) void prefill_tile_kernel(const PrefillArg
       }
     }
     lds_barrier();
-  }
+  };
+  // tiles wholly at or before every row's position need no causal mask (a
+  // wave without valid rows has pos_min = INT_MAX: no tile needs it)
+  const int nfree = pos_min == 0x7fffffff ? ntiles : min(ntiles, (pos_min + 1) / kTileKV);
+  for (int j = 0; j < nfree; ++j) tile(j, BoolTag<false>{});
+  for (int j = nfree; j < ntiles; ++j) tile(j, BoolTag<true>{});
 
   // total weight of each row (the four lane groups hold different tokens)
 #pragma unroll
