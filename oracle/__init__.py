@@ -15,6 +15,9 @@ names the passage of the pages that the underlying C function follows:
 * causal chunked prefill: same book, ch. 13 sec. 2; CS349D lecture 3 sec. 7.2.
 * reshape_and_cache (slot writes): same book, ch. 13 sec. 1 (slot_mapping).
 * copy_blocks (copy-on-write): CS349D lecture 3 sec. 3.2 and sec. 4.1.
+* FP8 (OCP E4M3) KV cache -- quantizing reshape_and_cache and decode over
+  dequantized values: "LLM inference, part 3: single node", ch. 10 (scale and
+  clip on write, scale back on read).
 """
 from __future__ import annotations
 
@@ -28,7 +31,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpkv_oracle.so")
 _SRC_PATH = os.path.join(_HERE, "pkv_oracle.c")
 
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
 
 _lib = None
 
@@ -65,6 +68,15 @@ def _load(path: str | None = None):
         lib.pkvo_reshape_and_cache.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, ci]
         lib.pkvo_copy_blocks.restype = ci
         lib.pkvo_copy_blocks.argtypes = [P, P, i32, P, i32, i32, i32, i32, i64, ci]
+        lib.pkvo_e4m3_to_f64.restype = dbl
+        lib.pkvo_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        lib.pkvo_e4m3_from_f32.restype = ctypes.c_uint8
+        lib.pkvo_e4m3_from_f32.argtypes = [ctypes.c_float]
+        lib.pkvo_reshape_and_cache_fp8.restype = ci
+        lib.pkvo_reshape_and_cache_fp8.argtypes = [P, P, ci, P, P, P, i32, i32, i32, i32, i64, P, P]
+        lib.pkvo_decode_fp8.restype = ci
+        lib.pkvo_decode_fp8.argtypes = [P, P, ci, P, P, P, P, P, i32, P, i64, i32, i32, i32, i32,
+                                        i32, dbl]
         if path is not None:
             return lib
         _lib = lib
@@ -217,3 +229,61 @@ def copy_blocks(k_caches, v_caches, pairs, dtype: str) -> None:
     _check(lib.pkvo_copy_blocks(ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp, ctypes.c_void_p),
                                 L, _ptr(pairs) if pairs.size else 0, pairs.shape[0], B, Hkv, D, NB,
                                 DTYPE_CODE[dtype]), "copy_blocks")
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Exact fp64 value of every OCP E4M3 code (uint8 array)."""
+    lib = _load()
+    codes = _c(codes, np.uint8)
+    flat = codes.reshape(-1)
+    out = np.array([lib.pkvo_e4m3_to_f64(int(c)) for c in flat], np.float64)
+    return out.reshape(codes.shape)
+
+
+def e4m3_from_f32(x) -> np.ndarray:
+    """OCP E4M3 code of every fp32 value: nearest finite value, ties to even."""
+    lib = _load()
+    x = _c(x, np.float32)
+    flat = x.reshape(-1)
+    out = np.array([lib.pkvo_e4m3_from_f32(float(v)) for v in flat], np.uint8)
+    return out.reshape(x.shape)
+
+
+def reshape_and_cache_fp8(key, value, in_dtype: str, k_cache, v_cache, slot_mapping, k_scale,
+                          v_scale) -> None:
+    """In place: quantize each token's K/V row (code = e4m3(fp32(x) / scale of
+    its KV head)) into its slot of the uint8 pools (negative slot = skip)."""
+    lib = _load()
+    key, value = _c(key), _c(value)
+    slot_mapping = _c(slot_mapping, np.int64)
+    k_scale, v_scale = _c(k_scale, np.float32), _c(v_scale, np.float32)
+    assert k_cache.dtype == np.uint8 and v_cache.dtype == np.uint8
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    NB, B, Hkv, D = k_cache.shape
+    assert k_scale.shape == (Hkv,) and v_scale.shape == (Hkv,)
+    T = key.shape[0]
+    _check(lib.pkvo_reshape_and_cache_fp8(_ptr(key), _ptr(value), DTYPE_CODE[in_dtype],
+                                          _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, Hkv,
+                                          D, B, NB, _ptr(k_scale), _ptr(v_scale)),
+           "reshape_and_cache_fp8")
+
+
+def decode_fp8(q, q_dtype: str, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+               scale: float) -> np.ndarray:
+    """fp64 decode output [S, Hq, D] over an FP8 pool read as code * scale."""
+    lib = _load()
+    q, k_cache, v_cache = _c(q), _c(k_cache, np.uint8), _c(v_cache, np.uint8)
+    k_scale, v_scale = _c(k_scale, np.float32), _c(v_scale, np.float32)
+    block_tables = _c(block_tables, np.int32)
+    context_lens = _c(context_lens, np.int32)
+    S, Hq, D = q.shape
+    NB, B, Hkv, Dk = k_cache.shape
+    assert Dk == D and v_cache.shape == k_cache.shape
+    assert k_scale.shape == (Hkv,) and v_scale.shape == (Hkv,)
+    max_nb = block_tables.shape[1] if block_tables.size else 0
+    bt = block_tables if block_tables.size else np.zeros((max(S, 1), 1), np.int32)
+    out = np.zeros((S, Hq, D), np.float64)
+    _check(lib.pkvo_decode_fp8(_ptr(out), _ptr(q), DTYPE_CODE[q_dtype], _ptr(k_cache),
+                               _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(bt), max_nb,
+                               _ptr(context_lens), NB, S, Hq, Hkv, D, B, scale), "decode_fp8")
+    return out

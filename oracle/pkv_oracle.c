@@ -44,6 +44,16 @@
  *    copy-on-write (CS349D lecture 3 sec. 3.2 and sec. 4.1: many small CoW
  *    copies are merged into one launch; the copy is made before the write).
  *
+ *  - FP8 KV cache ("LLM inference, part 3: single node", ch. 10: on write a
+ *    16-bit K/V value is scaled and clipped into 8 bits; on read it is scaled
+ *    back).  Format: OCP FP8 E4M3 (1 sign bit, 4 exponent bits with bias 7, 3
+ *    mantissa bits; subnormals; no infinities; 0x7F / 0xFF are NaN; largest
+ *    finite value 448).  Reading of the pages: one fp32 scale per KV head for
+ *    K and one for V; stored code = nearest finite E4M3 value to
+ *    fp32(x) / scale (ties to the even code, so anything beyond 448 clips to
+ *    448); the attended value is code * scale.  The division is done in fp32
+ *    because it decides an integer code.
+ *
  * Precision: every floating-point operation is IEEE binary64, compiled without
  * fast-math and with FP contraction off.  Stored elements are widened exactly
  * (fp32 directly; fp16 by its IEEE definition including subnormals; bf16 as the
@@ -62,6 +72,7 @@
 #define PKVO_F32 0
 #define PKVO_F16 1
 #define PKVO_BF16 2
+#define PKVO_FP8 3 /* OCP E4M3 codes */
 
 #define PKVO_OK 0
 #define PKVO_EINVAL -1
@@ -73,6 +84,7 @@ static int elem_bytes(int dtype) {
     case PKVO_F32: return 4;
     case PKVO_F16: return 2;
     case PKVO_BF16: return 2;
+    case PKVO_FP8: return 1;
     default: return 0;
   }
 }
@@ -101,6 +113,42 @@ static double bf16_bits_to_f64(uint16_t b) {
   return (double)f;
 }
 
+/* OCP FP8 E4M3 code -> binary64, exact.  Exponent field e, mantissa m:
+ * e == 0: m * 2^-9 (zero or subnormal); otherwise (8 + m) * 2^(e - 10), i.e.
+ * (1 + m/8) * 2^(e - 7); e == 15 with m == 7 is NaN. */
+double pkvo_e4m3_to_f64(uint8_t code) {
+  int sign = code >> 7;
+  int e = (code >> 3) & 0xf;
+  int m = code & 0x7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp((double)(8 + m), e - 10);
+  return sign ? -v : v;
+}
+
+/* binary32 -> OCP FP8 E4M3 code: the finite E4M3 value nearest to x, ties
+ * to the code with an even mantissa (IEEE round-to-nearest-even over the
+ * finite values only, so |x| beyond 448 -- infinities included -- clips to
+ * 448); NaN gives the NaN code of x's sign.  Plain search over all 127
+ * non-negative finite codes. */
+uint8_t pkvo_e4m3_from_f32(float x) {
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x)) return (uint8_t)(sign | 0x7f);
+  if (isinf(x)) return (uint8_t)(sign | 0x7e);
+  const double a = fabs((double)x);
+  int best = 0;
+  double best_d = a; /* distance to +0 (code 0) */
+  for (int c = 1; c <= 0x7e; ++c) {
+    const double d = fabs(pkvo_e4m3_to_f64((uint8_t)c) - a);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
 /* Widen element idx of a stored array of the given dtype to binary64. */
 double pkvo_load_elem(const void* base, int dtype, int64_t idx) {
   switch (dtype) {
@@ -119,6 +167,8 @@ double pkvo_load_elem(const void* base, int dtype, int64_t idx) {
       memcpy(&b, (const char*)base + 2 * idx, 2);
       return bf16_bits_to_f64(b);
     }
+    case PKVO_FP8:
+      return pkvo_e4m3_to_f64(((const uint8_t*)base)[idx]);
     default:
       return NAN;
   }
@@ -366,4 +416,90 @@ int pkvo_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_l
   }
   free(snap);
   return PKVO_OK;
+}
+
+/* Exact binary32 value of element idx of a 16- or 32-bit stored array (every
+ * fp16 and bf16 value is exactly representable in binary32). */
+static float load_f32(const void* base, int dtype, int64_t idx) {
+  return (float)pkvo_load_elem(base, dtype, idx);
+}
+
+/*
+ * Quantizing reshape_and_cache for an FP8 pool: token t's K row [Hkv, D] (in
+ * in_dtype) goes to slot slot_mapping[t] of the pool [NB, B, Hkv, D] of E4M3
+ * codes, element (h, d) stored as e4m3(fp32(key) / k_scale[h]); V likewise
+ * with v_scale.  Slots < 0 are skipped.
+ */
+int pkvo_reshape_and_cache_fp8(const void* key, const void* value, int in_dtype, uint8_t* k_cache,
+                               uint8_t* v_cache, const int64_t* slot_mapping, int32_t T,
+                               int32_t Hkv, int32_t D, int32_t B, int64_t NB,
+                               const float* k_scale, const float* v_scale) {
+  if (in_dtype == PKVO_FP8 || !elem_bytes(in_dtype) || T < 0 || Hkv <= 0 || D <= 0 || B <= 0 ||
+      NB <= 0)
+    return PKVO_EINVAL;
+  for (int32_t t = 0; t < T; ++t) {
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    if (slot >= NB * B) return PKVO_ERANGE;
+    for (int32_t h = 0; h < Hkv; ++h) {
+      for (int32_t d = 0; d < D; ++d) {
+        const int64_t src = ((int64_t)t * Hkv + h) * D + d;
+        const int64_t dst = (slot * Hkv + h) * D + d;
+        const float kq = load_f32(key, in_dtype, src) / k_scale[h];
+        const float vq = load_f32(value, in_dtype, src) / v_scale[h];
+        k_cache[dst] = pkvo_e4m3_from_f32(kq);
+        v_cache[dst] = pkvo_e4m3_from_f32(vq);
+      }
+    }
+  }
+  return PKVO_OK;
+}
+
+/*
+ * Decode over an FP8 pool: as pkvo_decode, with q in q_dtype and every cached
+ * element read as code * scale of its KV head (k_scale for K, v_scale for V;
+ * the products are exact in binary64).
+ */
+int pkvo_decode_fp8(double* out, const void* q, int q_dtype, const uint8_t* k_cache,
+                    const uint8_t* v_cache, const float* k_scale, const float* v_scale,
+                    const int32_t* block_tables, int32_t max_nb, const int32_t* context_lens,
+                    int64_t NB, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                    double scale) {
+  if (q_dtype == PKVO_FP8) return PKVO_EINVAL;
+  int rc = check_shapes(q_dtype, S, Hq, Hkv, D, B, max_nb);
+  if (rc) return rc;
+  const int32_t G = Hq / Hkv;
+  int32_t maxL = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    int32_t L = context_lens[s];
+    if (L < 0 || (int64_t)L > (int64_t)max_nb * B) return PKVO_ERANGE;
+    if (L > maxL) maxL = L;
+  }
+  double* K = (double*)malloc(sizeof(double) * ((size_t)maxL * D + 1));
+  double* V = (double*)malloc(sizeof(double) * ((size_t)maxL * D + 1));
+  double* qd = (double*)malloc(sizeof(double) * (size_t)D);
+  if (!K || !V || !qd) {
+    free(K); free(V); free(qd);
+    return PKVO_ENOMEM;
+  }
+  for (int32_t s = 0; s < S && rc == PKVO_OK; ++s) {
+    const int32_t L = context_lens[s];
+    const int32_t* table = block_tables + (int64_t)s * max_nb;
+    for (int32_t g = 0; g < Hkv && rc == PKVO_OK; ++g) {
+      rc = pkvo_gather(K, k_cache, PKVO_FP8, table, L, NB, Hkv, D, B, g);
+      if (rc == PKVO_OK) rc = pkvo_gather(V, v_cache, PKVO_FP8, table, L, NB, Hkv, D, B, g);
+      for (int64_t i = 0; i < (int64_t)L * D; ++i) {
+        K[i] *= (double)k_scale[g];
+        V[i] *= (double)v_scale[g];
+      }
+      for (int32_t j = 0; j < G && rc == PKVO_OK; ++j) {
+        const int32_t h = g * G + j;
+        const int64_t base = ((int64_t)s * Hq + h) * D;
+        for (int32_t d = 0; d < D; ++d) qd[d] = pkvo_load_elem(q, q_dtype, base + d);
+        rc = pkvo_attend(out + base, qd, K, V, L, D, scale);
+      }
+    }
+  }
+  free(K); free(V); free(qd);
+  return rc;
 }

@@ -15,8 +15,16 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "pkv_oracle.c")
 MUTATIONS = [
     ("gather_offset_off_by_one", "int64_t off = t % B;", "int64_t off = (t + 1) % B;"),
     ("gather_block_index", "int64_t blk = table[t / B];", "int64_t blk = table[t / B + (t >= B)];"),
-    ("gqa_strided_grouping", "const int32_t h = g * G + j;\n        const int64_t base = ((int64_t)s * Hq + h) * D;",
-     "const int32_t h = j * Hkv + g;\n        const int64_t base = ((int64_t)s * Hq + h) * D;"),
+    ("gqa_strided_grouping",
+     "const int32_t h = g * G + j;\n        const int64_t base = ((int64_t)s * Hq + h) * D;\n"
+     "        for (int32_t d = 0; d < D; ++d) qd[d] = pkvo_load_elem(q, dtype, base + d);",
+     "const int32_t h = j * Hkv + g;\n        const int64_t base = ((int64_t)s * Hq + h) * D;\n"
+     "        for (int32_t d = 0; d < D; ++d) qd[d] = pkvo_load_elem(q, dtype, base + d);"),
+    ("fp8_gqa_strided_grouping",
+     "const int32_t h = g * G + j;\n        const int64_t base = ((int64_t)s * Hq + h) * D;\n"
+     "        for (int32_t d = 0; d < D; ++d) qd[d] = pkvo_load_elem(q, q_dtype, base + d);",
+     "const int32_t h = j * Hkv + g;\n        const int64_t base = ((int64_t)s * Hq + h) * D;\n"
+     "        for (int32_t d = 0; d < D; ++d) qd[d] = pkvo_load_elem(q, q_dtype, base + d);"),
     ("scale_dropped", "z[t] = scale * acc;", "z[t] = acc;"),
     ("no_normalisation", "double p = z[t] / denom;", "double p = z[t];"),
     ("values_from_keys", "if (rc == PKVO_OK) rc = pkvo_gather(V, v_cache, dtype, table, L, NB, Hkv, D, B, g);\n      for (int32_t j = 0; j < G",
@@ -26,10 +34,26 @@ MUTATIONS = [
     ("f16_subnormal_exponent", "v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
     ("f16_normal_bias", "v = ldexp((double)(m | 0x400), e - 25);", "v = ldexp((double)(m | 0x400), e - 24);"),
     ("bf16_shift", "uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
-    ("reshape_skips_slot_zero", "if (slot < 0) continue;", "if (slot <= 0) continue;"),
+    ("reshape_skips_slot_zero",
+     "if (slot < 0) continue;\n    if (slot >= NB * B) return PKVO_ERANGE;\n    const int64_t blk",
+     "if (slot <= 0) continue;\n    if (slot >= NB * B) return PKVO_ERANGE;\n    const int64_t blk"),
+    ("fp8_reshape_skips_slot_zero",
+     "if (slot < 0) continue;\n    if (slot >= NB * B) return PKVO_ERANGE;\n    for (int32_t h",
+     "if (slot <= 0) continue;\n    if (slot >= NB * B) return PKVO_ERANGE;\n    for (int32_t h"),
     ("reshape_k_into_v", "memcpy((char*)v_cache + dst, (const char*)value", "memcpy((char*)v_cache + dst, (const char*)key"),
     ("copy_reads_destination", "memcpy(snap + (size_t)(2 * i) * blk_bytes, kc + (size_t)pairs[2 * i] * blk_bytes",
      "memcpy(snap + (size_t)(2 * i) * blk_bytes, kc + (size_t)pairs[2 * i + 1] * blk_bytes"),
+    ("e4m3_exponent_bias", "else v = ldexp((double)(8 + m), e - 10);", "else v = ldexp((double)(8 + m), e - 9);"),
+    ("e4m3_subnormal_scale", "if (e == 0) v = ldexp((double)m, -9);", "if (e == 0) v = ldexp((double)m, -10);"),
+    ("e4m3_ties_to_odd", "(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
+    ("e4m3_ties_away", "(d == best_d && (c & 1) == 0)", "(d == best_d)"),
+    ("e4m3_inf_to_nan", "if (isinf(x)) return (uint8_t)(sign | 0x7e);", "if (isinf(x)) return (uint8_t)(sign | 0x7f);"),
+    ("fp8_quantize_multiplies", "const float kq = load_f32(key, in_dtype, src) / k_scale[h];",
+     "const float kq = load_f32(key, in_dtype, src) * k_scale[h];"),
+    ("fp8_v_uses_k_scale", "const float vq = load_f32(value, in_dtype, src) / v_scale[h];",
+     "const float vq = load_f32(value, in_dtype, src) / k_scale[h];"),
+    ("fp8_decode_drops_k_scale", "        K[i] *= (double)k_scale[g];\n", ""),
+    ("fp8_decode_v_scale_of_k", "V[i] *= (double)v_scale[g];", "V[i] *= (double)k_scale[g];"),
 ]
 
 # the pins, called directly (parametrised ones with representative arguments)
@@ -46,6 +70,14 @@ CASES = [
     (pins.test_prefill_matches_causal_sdpa_on_whole_sequences, {"dtype": "f32"}),
     (pins.test_reshape_and_cache_matches_numpy_scatter, {"dtype": "f32"}),
     (pins.test_copy_blocks_matches_numpy_indexing, {}),
+    (pins.test_e4m3_decode_matches_torch_for_every_code, {}),
+    (pins.test_e4m3_spec_constants, {}),
+    (pins.test_e4m3_encode_matches_torch_inside_range, {}),
+    (pins.test_e4m3_encode_clips_beyond_range_and_keeps_nan, {}),
+    (pins.test_e4m3_round_trip_every_finite_code, {}),
+    (pins.test_reshape_and_cache_fp8_matches_torch_quantization, {"in_dtype": "bf16"}),
+    (pins.test_decode_fp8_matches_sdpa_on_dequantized_values, {"q_dtype": "bf16"}),
+    (pins.test_decode_fp8_single_token_returns_code_times_scale, {}),
 ]
 
 

@@ -320,3 +320,137 @@ def test_copy_blocks_matches_numpy_indexing():
     oracle.copy_blocks(ks, vs, pairs, "f32")
     for a, b in zip(ks + vs, refk + refv):
         assert a.tobytes() == b.tobytes()
+
+
+# ---------------------------------------------------------------- FP8 (OCP E4M3) KV cache
+def _torch_e4m3_to_f64(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn) \
+        .to(torch.float64).numpy()
+
+
+def _torch_e4m3_from_f32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ours, ref = oracle.e4m3_to_f64(codes), _torch_e4m3_to_f64(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 2
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+def test_e4m3_spec_constants():
+    """OCP 8-bit floating point spec, E4M3: max normal 448 (S.1111.110), min
+    normal 2^-6, min subnormal 2^-9, 1.0 = S.0111.000, NaN = S.1111.111."""
+    v = oracle.e4m3_to_f64(np.array([0x7E, 0x08, 0x01, 0x38, 0x80, 0xFE, 0x07], np.uint8))
+    assert v.tolist() == [448.0, 2.0**-6, 2.0**-9, 1.0, 0.0, -448.0, 7 * 2.0**-9]
+    assert math.copysign(1.0, v[4]) == -1.0
+    assert np.isnan(oracle.e4m3_to_f64(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def _encode_probe_values():
+    """Every finite E4M3 value, every midpoint between neighbours (the ties),
+    the fp32 neighbours of each midpoint, and log-uniform random magnitudes,
+    all with both signs, limited to |x| <= 464 (where torch does not give NaN)."""
+    fin = np.unique(np.abs(_torch_e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))))
+    mids = (fin[1:] + fin[:-1]) / 2
+    mids = np.append(mids, 464.0)  # the tie between 448 and the first value past it
+    m32 = mids.astype(np.float32)
+    near = np.concatenate([np.nextafter(m32, np.float32(0)), np.nextafter(m32, np.float32(1e9))])
+    rnd = np.exp2(np.random.default_rng(5).uniform(-13, np.log2(464), 4000)).astype(np.float32)
+    x = np.concatenate([fin.astype(np.float32), m32, near, rnd, np.float32([0, 2.0**-10, 3 * 2.0**-11])])
+    x = x[np.abs(x) <= 464]
+    return np.concatenate([x, -x]).astype(np.float32)
+
+
+def test_e4m3_encode_matches_torch_inside_range():
+    x = _encode_probe_values()
+    assert np.array_equal(oracle.e4m3_from_f32(x), _torch_e4m3_from_f32(x))
+
+
+def test_e4m3_encode_clips_beyond_range_and_keeps_nan():
+    """Reading of the pages' "scale, then clip to 8 bits": beyond the largest
+    finite value everything clips to +-448 (0x7E / 0xFE); NaN stays NaN."""
+    x = np.float32([464.0001, 479.9, 480, 1e6, 3.4e38, np.inf])
+    assert np.all(oracle.e4m3_from_f32(x) == 0x7E)
+    assert np.all(oracle.e4m3_from_f32(-x) == 0xFE)
+    assert oracle.e4m3_from_f32(np.float32([np.nan]))[0] & 0x7F == 0x7F
+
+
+def test_e4m3_round_trip_every_finite_code():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    vals = oracle.e4m3_to_f64(codes).astype(np.float32)
+    assert np.array_equal(oracle.e4m3_from_f32(vals), codes)
+
+
+def _fp8_pool(rng, NB, B, Hkv, D):
+    """Random finite codes (no NaN) for K and V pools."""
+    k = rng.integers(0, 256, (NB, B, Hkv, D)).astype(np.uint8)
+    v = rng.integers(0, 256, (NB, B, Hkv, D)).astype(np.uint8)
+    k[(k & 0x7F) == 0x7F] = 0x3C
+    v[(v & 0x7F) == 0x7F] = 0x44
+    return k, v
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "f16", "bf16"])
+def test_reshape_and_cache_fp8_matches_torch_quantization(in_dtype):
+    rng = np.random.default_rng(6)
+    NB, B, Hkv, D, T = 9, 4, 3, 16, 11
+    k0, v0 = _fp8_pool(rng, NB, B, Hkv, D)
+    key = W.to_storage(rng.standard_normal((T, Hkv, D), dtype=np.float32) * 3, in_dtype)
+    val = W.to_storage(rng.standard_normal((T, Hkv, D), dtype=np.float32) * 3, in_dtype)
+    ks = np.float32([0.05, 0.013, 0.3])
+    vs = np.float32([0.021, 0.4, 0.07])
+    slots = np.concatenate([[0, NB * B - 1], 1 + rng.permutation(NB * B - 2)[:T - 2]]).astype(np.int64)
+    slots[[3, 8]] = -1
+    k, v = k0.copy(), v0.copy()
+    oracle.reshape_and_cache_fp8(key, val, in_dtype, k, v, slots, ks, vs)
+    kf = torch.from_numpy(W.storage_to_f32(key, in_dtype))
+    vf = torch.from_numpy(W.storage_to_f32(val, in_dtype))
+    # torch's conversion after clipping to +-448 (the 0.013 head clips some elements)
+    kd = kf / torch.from_numpy(ks)[None, :, None]
+    vd = vf / torch.from_numpy(vs)[None, :, None]
+    assert (kd.abs() > 464).any()
+    kq = kd.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    vq = vd.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    kr, vr = k0.reshape(NB * B, Hkv, D).copy(), v0.reshape(NB * B, Hkv, D).copy()
+    keep = slots >= 0
+    kr[slots[keep]] = kq[keep]
+    vr[slots[keep]] = vq[keep]
+    assert k.tobytes() == kr.tobytes() and v.tobytes() == vr.tobytes()
+
+
+@pytest.mark.parametrize("q_dtype", ["f16", "bf16"])
+def test_decode_fp8_matches_sdpa_on_dequantized_values(q_dtype):
+    """Single sequence with table [0, 1, ...]: attention over code * head scale."""
+    rng = np.random.default_rng(8)
+    Hq, Hkv, B, D, L = 8, 2, 4, 16, 21
+    nb = -(-L // B)
+    k, v = _fp8_pool(rng, nb, B, Hkv, D)
+    ks, vs = np.float32([0.02, 0.11]), np.float32([0.5, 0.003])
+    q = W.to_storage(rng.standard_normal((1, Hq, D), dtype=np.float32), q_dtype)
+    out = oracle.decode_fp8(q, q_dtype, k, v, ks, vs, np.arange(nb, dtype=np.int32)[None],
+                            np.array([L]), 0.4)
+    Kc = (_torch_e4m3_to_f64(k).reshape(nb * B, Hkv, D)[:L] * ks.astype(np.float64)[None, :, None])
+    Vc = (_torch_e4m3_to_f64(v).reshape(nb * B, Hkv, D)[:L] * vs.astype(np.float64)[None, :, None])
+    qc = W.storage_to_f32(q, q_dtype).astype(np.float64)[0][:, None, :]
+    ref = _sdpa_fp64(qc, Kc.transpose(1, 0, 2), Vc.transpose(1, 0, 2), 0.4)[:, 0, :]
+    np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-15)
+
+
+def test_decode_fp8_single_token_returns_code_times_scale():
+    rng = np.random.default_rng(9)
+    Hq, Hkv, B, D = 4, 2, 16, 32
+    k, v = _fp8_pool(rng, 3, B, Hkv, D)
+    ks, vs = np.float32([0.7, 0.25]), np.float32([0.125, 3.0])
+    q = W.to_storage(rng.standard_normal((2, Hq, D), dtype=np.float32), "bf16")
+    tables = np.array([[2], [0]], np.int32)
+    out = oracle.decode_fp8(q, "bf16", k, v, ks, vs, tables, np.array([1, 1]), 0.2)
+    for s, blk in enumerate([2, 0]):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            want = _torch_e4m3_to_f64(v[blk, 0, g]) * float(vs[g])
+            assert np.array_equal(out[s, h], want)
