@@ -25,6 +25,8 @@
  *  - A slot is an absolute row index of a pool: slot = block * B + offset.
  *  - Supported instantiations: kv dtype {f32, f16, bf16}; D in {64, 128};
  *    B in {1, 2, 4, 8, 16, 32}; any Hkv >= 1 and Hq a multiple of Hkv.
+ *    FP8 pools (PKV_FP8_E4M3) are written by pkv_reshape_and_cache_fp8, read
+ *    by pkv_paged_attention_decode_fp8 and copied by pkv_copy_blocks.
  *    Anything else returns PKV_ERR_UNSUPPORTED.
  */
 #ifndef PKV_H_
@@ -46,7 +48,10 @@ typedef enum {
   PKV_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
 } pkv_status;
 
-typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+/* PKV_FP8_E4M3: OCP 8-bit float E4M3 (sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, subnormals, no infinities, 0x7F/0xFF NaN, max 448); KV pools
+ * only. */
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 } pkv_dtype;
 
 /* Human-readable name of a status code (static storage). */
 const char* pkv_status_string(pkv_status s);
@@ -115,6 +120,46 @@ pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void
                                       int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
                                       float scale, void* workspace, size_t workspace_bytes,
                                       void* stream);
+
+/* ------------------------------------------------------------------------
+ * FP8 KV cache -- the pools hold OCP E4M3 codes, one byte per element, with
+ * one fp32 scale per KV head for K and one for V.
+ *
+ * Defined by "LLM inference, part 3: single node", ch. 10 (KV-cache
+ * quantization: on write each 16-bit K/V value is scaled and clipped into 8
+ * bits, halving the bytes that decode must read; on read it is scaled back;
+ * FP8 keeps sign, exponent and mantissa, i.e. it is still a float).
+ *
+ * pkv_reshape_and_cache_fp8: as pkv_reshape_and_cache, but element (h, d) of
+ * token t is stored as the E4M3 code nearest to fp32(x) / scale[h] (fp32
+ * division, round to nearest even; |x / scale| >= 448 and infinities clip to
+ * +-448; NaN stays NaN).
+ *   key, value       : device [T, Hkv, D] of in_dtype (f32, f16 or bf16)
+ *   k_cache, v_cache : device pools [NB, B, Hkv, D] of E4M3 codes (uint8)
+ *   k_scale, v_scale : device fp32 [Hkv]; positive and finite (caller's
+ *                      contract, like the other device contents)
+ *
+ * pkv_paged_attention_decode_fp8: as pkv_paged_attention_decode, with q of
+ * q_dtype (f16 or bf16) and every cached element read as code * scale of its
+ * KV head:  out[s,h,:] = sum_t softmax_t(scale * q . K_t) V_t with
+ * K_t = k_code * k_scale[h / G], V_t = v_code * v_scale[h / G].  The codes
+ * are widened exactly; the K scale is folded into the score scale and the V
+ * scale into the result (fp32).  The workspace is the same as for
+ * pkv_paged_attention_decode (pkv_decode_workspace_size).
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_reshape_and_cache_fp8(const void* key, const void* value, pkv_dtype in_dtype,
+                                     void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                                     int32_t T, int32_t Hkv, int32_t D, int32_t B, int64_t NB,
+                                     const float* k_scale, const float* v_scale, void* stream);
+
+pkv_status pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype, const void* q,
+                                          pkv_dtype q_dtype, const void* k_cache,
+                                          const void* v_cache, const float* k_scale,
+                                          const float* v_scale, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                          int32_t max_context_len, int32_t S, int32_t Hq,
+                                          int32_t Hkv, int32_t D, int32_t B, float scale,
+                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * paged_attention_prefill -- a causal query chunk per sequence over its

@@ -8,10 +8,11 @@ library and raises if it has not been built.
 """
 from ._binding import (BlockManager, PkvError, PkvOOM, copy_blocks, declared_symbols,
                        decode_workspace_size, load_library, paged_attention_decode,
-                       paged_attention_prefill, reshape_and_cache)
+                       paged_attention_decode_fp8, paged_attention_prefill, reshape_and_cache,
+                       reshape_and_cache_fp8)
 
 __all__ = [
     "BlockManager", "PkvError", "PkvOOM", "copy_blocks", "declared_symbols",
-    "decode_workspace_size", "load_library", "paged_attention_decode", "paged_attention_prefill",
-    "reshape_and_cache",
+    "decode_workspace_size", "load_library", "paged_attention_decode", "paged_attention_decode_fp8",
+    "paged_attention_prefill", "reshape_and_cache", "reshape_and_cache_fp8",
 ]

@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "pkv.h")
 PKV_OK = 0
 STATUS = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_UNSUPPORTED", 3: "PKV_ERR_WORKSPACE",
           4: "PKV_ERR_OOM", 5: "PKV_ERR_HIP"}
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
 
 
 class PkvError(RuntimeError):
@@ -61,6 +61,9 @@ def load_library(path: str | None = None):
         "pkv_paged_attention_prefill": (st, [P, st, P, P, i32, i32, P, P, st, P, i32, P, i32, i32,
                                              i32, i32, i32, i32, f32, P]),
         "pkv_copy_blocks": (st, [P, P, i32, P, i32, i32, i32, i32, st, P]),
+        "pkv_reshape_and_cache_fp8": (st, [P, P, st, P, P, P, i32, i32, i32, i32, i64, P, P, P]),
+        "pkv_paged_attention_decode_fp8": (st, [P, st, P, st, P, P, P, P, P, i32, P, i32, i32, i32,
+                                                i32, i32, i32, f32, P, sz, P]),
         "pkv_bm_create": (st, [i32, i32, P, ctypes.POINTER(P)]),
         "pkv_bm_destroy": (None, [P]),
         "pkv_bm_add_seq": (st, [P, i32, I32P]),
@@ -103,8 +106,10 @@ def _torch():
 
 
 def dtype_code(t) -> int:
+    """Library dtype of a tensor; uint8 and float8_e4m3fn tensors are FP8 (E4M3) pools."""
     torch = _torch()
-    m = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    m = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.uint8: 3,
+         torch.float8_e4m3fn: 3}
     if t.dtype not in m:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return m[t.dtype]
@@ -234,6 +239,63 @@ def copy_blocks(k_caches, v_caches, block_pairs, stream=None) -> None:
     _check(lib.pkv_copy_blocks(ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp, ctypes.c_void_p),
                                L, pairs_ptr, N, B, Hkv, D, dtype_code(k_caches[0]),
                                _stream(stream)), "copy_blocks")
+
+
+def _fp8_pool(t, name):
+    if dtype_code(t) != 3:
+        raise TypeError(f"{name} must be an FP8 pool (uint8 or float8_e4m3fn), got {t.dtype}")
+    return _dev(t, name)
+
+
+def reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale,
+                          stream=None) -> None:
+    """Quantize each new token's K/V row ([T, Hkv, D], f32/f16/bf16) into its
+    slot of the FP8 pools: code = e4m3(x / scale of the row's KV head)."""
+    torch = _torch()
+    lib = load_library()
+    T, Hkv, D = key.shape
+    NB, B, Hkv2, D2 = k_cache.shape
+    if (Hkv2, D2) != (Hkv, D) or value.shape != key.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("reshape_and_cache_fp8: shape mismatch")
+    if key.dtype != value.dtype:
+        raise TypeError("reshape_and_cache_fp8: key/value dtype mismatch")
+    if slot_mapping.shape != (T,) or k_scale.shape != (Hkv,) or v_scale.shape != (Hkv,):
+        raise ValueError("reshape_and_cache_fp8: slot_mapping [T], scales [Hkv]")
+    _check(lib.pkv_reshape_and_cache_fp8(
+        _dev(key, "key"), _dev(value, "value"), dtype_code(key), _fp8_pool(k_cache, "k_cache"),
+        _fp8_pool(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int64), T, Hkv, D,
+        B, NB, _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+        _stream(stream)), "reshape_and_cache_fp8")
+
+
+def paged_attention_decode_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                               context_lens, max_context_len: int, scale: float, workspace=None,
+                               stream=None):
+    """Decode attention over FP8 pools read as code * scale of the KV head; q
+    is f16 or bf16.  ``workspace`` as for paged_attention_decode."""
+    torch = _torch()
+    lib = load_library()
+    S, Hq, D = q.shape
+    NB, B, Hkv, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("paged_attention_decode_fp8: shape mismatch")
+    if k_scale.shape != (Hkv,) or v_scale.shape != (Hkv,):
+        raise ValueError("paged_attention_decode_fp8: scales must be [Hkv]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("paged_attention_decode_fp8: block_tables [S, max_nb] / context_lens [S]")
+    need = decode_workspace_size(S, Hq, Hkv, D, B, max_context_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pkv_paged_attention_decode_fp8(
+        _dev(out, "out"), dtype_code(out), _dev(q, "q"), dtype_code(q),
+        _fp8_pool(k_cache, "k_cache"), _fp8_pool(v_cache, "v_cache"),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B,
+        float(scale), ws_ptr, ws_bytes, _stream(stream)), "paged_attention_decode_fp8")
+    return out
 
 
 # ---------------------------------------------------------------- host block manager

@@ -86,6 +86,26 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
                                   static_cast<hipStream_t>(stream));
 }
 
+pkv_status pkv_reshape_and_cache_fp8(const void* key, const void* value, pkv_dtype in_dtype,
+                                     void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                                     int32_t T, int32_t Hkv, int32_t D, int32_t B, int64_t NB,
+                                     const float* k_scale, const float* v_scale, void* stream) {
+  g_last_error[0] = 0;
+  PKV_REQUIRE(T >= 0, PKV_ERR_INVALID_ARG, "reshape_and_cache_fp8: T = %d", T);
+  PKV_REQUIRE(Hkv > 0 && D > 0 && B > 0 && NB > 0, PKV_ERR_INVALID_ARG,
+              "reshape_and_cache_fp8: Hkv=%d D=%d B=%d NB=%lld must be positive", Hkv, D, B,
+              (long long)NB);
+  PKV_REQUIRE(supported_dtype(in_dtype), PKV_ERR_UNSUPPORTED,
+              "reshape_and_cache_fp8: input dtype %d", (int)in_dtype);
+  PKV_REQUIRE(supported_head_dim(D), PKV_ERR_UNSUPPORTED, "reshape_and_cache_fp8: head_dim %d", D);
+  PKV_REQUIRE(supported_block(B), PKV_ERR_UNSUPPORTED, "reshape_and_cache_fp8: block_size %d", B);
+  if (T == 0) return PKV_OK;
+  PKV_REQUIRE(key && value && k_cache && v_cache && slot_mapping && k_scale && v_scale,
+              PKV_ERR_INVALID_ARG, "reshape_and_cache_fp8: null pointer");
+  return launch_reshape_and_cache_fp8(key, value, in_dtype, k_cache, v_cache, slot_mapping, T, Hkv,
+                                      D, k_scale, v_scale, static_cast<hipStream_t>(stream));
+}
+
 pkv_status pkv_decode_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
                                      int32_t max_context_len, size_t* bytes) {
   g_last_error[0] = 0;
@@ -104,13 +124,17 @@ pkv_status pkv_decode_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t
   return PKV_OK;
 }
 
-pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
-                                      const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
-                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                      const int32_t* context_lens, int32_t max_context_len,
-                                      int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
-                                      float scale, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
+}  // extern "C"
+
+// Both decode entry points: q_dtype is the dtype of q (and of the pools unless
+// fp8, where the pools hold E4M3 codes with per-KV-head scales).
+static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype kv_dtype,
+                              bool fp8, const void* k_cache, const void* v_cache,
+                              const float* k_scale, const float* v_scale,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t max_context_len, int32_t S,
+                              int32_t Hq, int32_t Hkv, int32_t D, int32_t B, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
   PKV_REQUIRE(S >= 0 && Hq > 0 && Hkv > 0 && D > 0 && B > 0, PKV_ERR_INVALID_ARG,
               "decode: S=%d Hq=%d Hkv=%d D=%d B=%d", S, Hq, Hkv, D, B);
@@ -120,17 +144,21 @@ pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void
               "decode: negative max_context_len or max_blocks_per_seq");
   PKV_REQUIRE(supported_dtype(kv_dtype) && supported_dtype(out_dtype), PKV_ERR_UNSUPPORTED,
               "decode: dtypes kv=%d out=%d", (int)kv_dtype, (int)out_dtype);
+  PKV_REQUIRE(!fp8 || kv_dtype != PKV_F32, PKV_ERR_UNSUPPORTED,
+              "decode_fp8: q must be f16 or bf16");
   PKV_REQUIRE(supported_head_dim(D), PKV_ERR_UNSUPPORTED, "decode: head_dim %d", D);
   PKV_REQUIRE(supported_block(B), PKV_ERR_UNSUPPORTED, "decode: block_size %d", B);
   PKV_REQUIRE((int64_t)max_context_len <= (int64_t)max_blocks_per_seq * B, PKV_ERR_INVALID_ARG,
               "decode: max_context_len %d exceeds table capacity %d x %d", max_context_len,
               max_blocks_per_seq, B);
   PKV_REQUIRE(scale == scale, PKV_ERR_INVALID_ARG, "decode: scale is NaN");
-  PKV_REQUIRE((int64_t)B * Hkv * D * dt_bytes(kv_dtype) < ((int64_t)1 << 31), PKV_ERR_UNSUPPORTED,
+  PKV_REQUIRE((int64_t)B * Hkv * D * dt_bytes(fp8 ? (int)DT_FP8 : (int)kv_dtype) < ((int64_t)1 << 31),
+              PKV_ERR_UNSUPPORTED,
               "decode: one block of one pool must be smaller than 2 GiB");
   if (S == 0) return PKV_OK;
   PKV_REQUIRE(out && q && k_cache && v_cache && block_tables && context_lens, PKV_ERR_INVALID_ARG,
               "decode: null pointer");
+  PKV_REQUIRE(!fp8 || (k_scale && v_scale), PKV_ERR_INVALID_ARG, "decode_fp8: null scale array");
   DecodePlan plan;
   const pkv_status pst = plan_decode(S, Hq, Hkv, D, B, max_context_len, &plan);
   if (pst != PKV_OK) return pst;
@@ -162,7 +190,36 @@ pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void
   a.max_ctx = max_context_len;
   a.out_dt = out_dtype;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return launch_decode(kv_dtype, plan, a, static_cast<hipStream_t>(stream));
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return launch_decode(kv_dtype, fp8, plan, a, static_cast<hipStream_t>(stream));
+}
+
+extern "C" {
+
+pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
+                                      const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t max_context_len,
+                                      int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                      float scale, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  return decode_impl(out, out_dtype, q, kv_dtype, false, k_cache, v_cache, nullptr, nullptr,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, S, Hq, Hkv,
+                     D, B, scale, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype, const void* q,
+                                          pkv_dtype q_dtype, const void* k_cache,
+                                          const void* v_cache, const float* k_scale,
+                                          const float* v_scale, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                          int32_t max_context_len, int32_t S, int32_t Hq,
+                                          int32_t Hkv, int32_t D, int32_t B, float scale,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, out_dtype, q, q_dtype, true, k_cache, v_cache, k_scale, v_scale,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, S, Hq, Hkv,
+                     D, B, scale, workspace, workspace_bytes, stream);
 }
 
 pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* q,
@@ -221,8 +278,8 @@ pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t
   g_last_error[0] = 0;
   PKV_REQUIRE(num_layers >= 0 && N >= 0 && B > 0 && Hkv > 0 && D > 0, PKV_ERR_INVALID_ARG,
               "copy_blocks: layers=%d N=%d B=%d Hkv=%d D=%d", num_layers, N, B, Hkv, D);
-  PKV_REQUIRE(supported_dtype(kv_dtype), PKV_ERR_UNSUPPORTED, "copy_blocks: dtype %d",
-              (int)kv_dtype);
+  PKV_REQUIRE(supported_dtype(kv_dtype) || kv_dtype == PKV_FP8_E4M3, PKV_ERR_UNSUPPORTED,
+              "copy_blocks: dtype %d", (int)kv_dtype);
   PKV_REQUIRE(supported_head_dim(D), PKV_ERR_UNSUPPORTED, "copy_blocks: head_dim %d", D);
   PKV_REQUIRE(supported_block(B), PKV_ERR_UNSUPPORTED, "copy_blocks: block_size %d", B);
   if (N == 0 || num_layers == 0) return PKV_OK;

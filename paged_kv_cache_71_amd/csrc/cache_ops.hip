@@ -9,6 +9,9 @@
 //    kernel for split + reorder + block write).
 //  * copy_blocks: all copy-on-write block copies of a step, for every layer,
 //    in one launch (CS349D lecture 3 sec. 3.2 and sec. 4.1).
+//  * reshape_and_cache_fp8: the same scatter into an FP8 pool, each element
+//    scaled by its KV head's scale and rounded into an OCP E4M3 code
+//    ("LLM inference, part 3", ch. 10: scale and clip into 8 bits on write).
 //
 // Both are HBM copies: 16-byte lanes, fully coalesced, one workgroup per row
 // (or per block and layer), no LDS.
@@ -36,6 +39,66 @@ __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_kernel(
     const uint4 vv = vs[i];
     kd[i] = kk;
     vd[i] = vv;
+  }
+}
+
+// fp32 -> OCP E4M3 code, written from the format: 4 exponent bits with bias 7,
+// 3 mantissa bits, subnormals (steps of 2^-9 below 2^-6), largest finite
+// value 448 = 1.75 * 2^8.  Round to nearest even; anything at or beyond 448
+// (infinities too) clips to +-448; NaN gives the NaN code of its sign.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;  // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;  // |x| >= 448: clip
+  if (a < 0x3c800000u) {
+    // |x| < 2^-6: code = |x| / 2^-9 rounded to an integer 0..8 (8 is the
+    // smallest normal, 2^-6); the power-of-two product is exact
+    return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  // normal: keep 3 of fp32's 23 mantissa bits, round to nearest even (a carry
+  // into the exponent is the correct rounding), then rebias 127 -> 7
+  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+  return sign | (r - (120u << 3));
+}
+
+template <int IDT>
+__device__ __forceinline__ float elem_f32(const void* row, int64_t i) {
+  if constexpr (IDT == DT_F32) return static_cast<const float*>(row)[i];
+  else if constexpr (IDT == DT_BF16)
+    return __uint_as_float((uint32_t) static_cast<const uint16_t*>(row)[i] << 16);
+  else return (float)__builtin_bit_cast(_Float16, static_cast<const uint16_t*>(row)[i]);
+}
+
+// One workgroup per token; thread i quantizes 8-element groups i, i+256, ...
+// of the token's K row and V row (one group = 8 code bytes, one 8-byte store;
+// D is a multiple of 8, so a group lies in one KV head).
+template <int IDT>
+__global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_fp8_kernel(
+    const void* __restrict__ key, const void* __restrict__ value, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int32_t Hkv,
+    int32_t D) {
+  const int64_t t = blockIdx.x;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0) return;
+  const int64_t row = (int64_t)Hkv * D;
+  const int64_t ngroups = row / 8;
+  for (int64_t gi = threadIdx.x; gi < ngroups; gi += kCopyThreads) {
+    const int64_t e0 = gi * 8;
+    const int h = (int)(e0 / D);
+    const float ks = k_scale[h], vs = v_scale[h];
+    uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float kx = elem_f32<IDT>(key, t * row + e0 + j) / ks;
+      const float vx = elem_f32<IDT>(value, t * row + e0 + j) / vs;
+      kw[j >> 2] |= e4m3_code(kx) << (8 * (j & 3));
+      vw[j >> 2] |= e4m3_code(vx) << (8 * (j & 3));
+    }
+    *reinterpret_cast<uint2*>(k_cache + slot * row + e0) = make_uint2(kw[0], kw[1]);
+    *reinterpret_cast<uint2*>(v_cache + slot * row + e0) = make_uint2(vw[0], vw[1]);
   }
 }
 
@@ -79,6 +142,32 @@ pkv_status launch_reshape_and_cache(const void* key, const void* value, void* k_
                      static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), slot_mapping,
                      row_bytes / 16);
   return check_launch("reshape_and_cache");
+}
+
+pkv_status launch_reshape_and_cache_fp8(const void* key, const void* value, int in_dt,
+                                        void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                                        int32_t T, int32_t Hkv, int32_t D, const float* k_scale,
+                                        const float* v_scale, hipStream_t stream) {
+  if (T == 0) return PKV_OK;
+  uint8_t* kc = static_cast<uint8_t*>(k_cache);
+  uint8_t* vc = static_cast<uint8_t*>(v_cache);
+  switch (in_dt) {
+    case DT_F32:
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DT_F32>, dim3(T), dim3(kCopyThreads), 0,
+                         stream, key, value, kc, vc, slot_mapping, k_scale, v_scale, Hkv, D);
+      break;
+    case DT_F16:
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DT_F16>, dim3(T), dim3(kCopyThreads), 0,
+                         stream, key, value, kc, vc, slot_mapping, k_scale, v_scale, Hkv, D);
+      break;
+    case DT_BF16:
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DT_BF16>, dim3(T), dim3(kCopyThreads), 0,
+                         stream, key, value, kc, vc, slot_mapping, k_scale, v_scale, Hkv, D);
+      break;
+    default:
+      return fail(PKV_ERR_UNSUPPORTED, "reshape_and_cache_fp8: input dtype %d", in_dt);
+  }
+  return check_launch("reshape_and_cache_fp8");
 }
 
 pkv_status launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,

@@ -42,6 +42,14 @@
 //  * Rows past context_lens[s] and table entries past the last block are never
 //    used (clamped loads read valid rows only), so stale or poisoned memory
 //    there cannot reach the output.
+//  * FP8 pools ("LLM inference, part 3", ch. 10): the F8 instantiations keep
+//    every lane's element assignment of the 16-bit path but load 8 code bytes
+//    where that path loads 16 data bytes, so a tile costs half the HBM bytes;
+//    the codes are widened exactly in registers (gfx950 conversions) right
+//    before use, the K scale of the row's KV head is folded into the score
+//    scale and the V scale into the finished accumulator.
+#include <type_traits>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -171,6 +179,41 @@ __device__ __forceinline__ uint4 ld16_stream(const char* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ld8_stream(const char* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+// 8 OCP E4M3 codes (one lane's K load) -> 8 elements of the 16-bit dtype DT,
+// in order; every E4M3 value is exact in bf16 and in fp16 (unit scale).
+template <int DT>
+__device__ __forceinline__ uint4 fp8x8_to16(const uint2 v) {
+  if constexpr (DT == DT_BF16) {
+    return make_uint4(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, true)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, true)));
+  } else {
+    return make_uint4(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 1.f, true)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 1.f, true)));
+  }
+}
+
+// 8 OCP E4M3 codes (one lane's V load) -> 8 fp32 values, exact.
+__device__ __forceinline__ void fp8x8_to_f32(const uint2 v, float* f) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(v.x, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(v.x, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(v.y, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(v.y, true);
+  f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+  f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+}
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -204,6 +247,7 @@ __device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlan
 // with a wave-uniform address becomes a scalar (SMEM) load, which is counted
 // apart from the vector loads of the K/V pipeline.
 typedef const __attribute__((address_space(4))) int32_t cint32_t;
+typedef const __attribute__((address_space(4))) float cfloat_t;
 
 // Tile geometry of a (dtype, head_dim) pair.
 template <int DT, int D>
@@ -242,17 +286,25 @@ struct Cursor {
   int L;    // context length of the sequence
   int kvh;  // KV head of the row
   int h0;   // first query head of the row
+  float zs; // FP8 pools: score scale of the row (softmax scale * log2 e * K scale)
+  float vs; // FP8 pools: V scale of the row
 };
 
 // Split kernel.  UNI: every wave-load lies in one block (B >= RPW), so its
 // table entry is one scalar; otherwise each lane looks up its own row's block.
 // MF (16-bit KV, D = 128, a GQA group of 4 query heads, B >= 16): q . k runs on
 // the matrix cores; everything else as in the vector path (see below).
-template <int DT, int D, int GC, bool UNI, bool MF>
+// F8: the pools hold E4M3 codes (DT is then the dtype of q and of the widened
+// elements); the lane layout is DT's, with 8-byte instead of 16-byte loads.
+template <int DT, int D, int GC, bool UNI, bool MF, bool F8>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs a) {
   using Gm = Geo<DT, D>;
   constexpr int ES = Gm::ES, EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
   constexpr int NLD = Gm::NLD, TILE = Gm::TILE;
+  static_assert(!F8 || DT != DT_F32, "FP8 pools pair with a 16-bit q");
+  constexpr int KS = F8 ? 1 : ES;   // bytes per cached element
+  constexpr int LB = 16 * KS / ES;  // bytes of K or V per lane per load
+  using KVT = std::conditional_t<F8, uint2, uint4>;
   static_assert(!MF || (DT != DT_F32 && D == 128 && GC == 4 && UNI && TILE == 16),
                 "matrix-core path: 16-bit KV, D = 128, GQA group of 4, one block per tile");
   constexpr int QN = MF ? D / 32 : GC;  // q registers: k-steps of 32 (MF) or heads
@@ -323,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
   const int nhc = a.n_hchunks;
   const int log2B = a.log2B;
   const int bmask = a.B - 1;
-  const int64_t row_stride = (int64_t)a.Hkv * D * ES;  // bytes between consecutive slots
+  const int64_t row_stride = (int64_t)a.Hkv * D * KS;  // bytes between consecutive slots
   const int64_t blk_stride = row_stride * a.B;
   const int row_stride32 = (int)row_stride;  // B * row_stride < 2^31 (checked on the host)
   const char* const kpool = static_cast<const char*>(a.k_cache);
@@ -333,6 +385,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
   auto set_row = [&](Cursor& c) __attribute__((always_inline)) {
     c.kvh = c.rho / nhc;
     c.h0 = c.kvh * G + (c.rho - c.kvh * nhc) * GC;
+    if constexpr (F8) {  // scalar loads (uniform address, constant space)
+      c.zs = c_scale * ((cfloat_t*)a.k_scale)[c.kvh];
+      c.vs = ((cfloat_t*)a.v_scale)[c.kvh];
+    }
   };
   auto set_seq = [&](Cursor& c) __attribute__((always_inline)) {
     c.L = rfl(sm_len[c.s]);
@@ -394,25 +450,29 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
   };
 
   // K/V loads of one tile; rows past the context read the last valid row
-  auto issue = [&](const Cursor& c, const Ent& en, uint4 (&kb)[NLD], uint4 (&vb)[NLD]) __attribute__((always_inline)) {
+  auto ldkv = [&](const char* p) __attribute__((always_inline)) -> KVT {
+    if constexpr (F8) return ld8_stream(p);
+    else return ld16_stream(p);
+  };
+  auto issue = [&](const Cursor& c, const Ent& en, KVT (&kb)[NLD], KVT (&vb)[NLD]) __attribute__((always_inline)) {
     const int ts = c.j * TILE;
-    const int head_off = c.kvh * D * ES + col * 16;
+    const int head_off = c.kvh * D * KS + col * LB;
     if constexpr (MF) {
       // the whole tile lies in one block.  K as the MFMA A operand: lane l
       // holds token l % 16, elements 32 kk + 8 (l / 16) .. + 7.  V rows as in
       // the vector path but with token 4 * row + i in load i, which is where
       // the MFMA result leaves that token's scores.
       const int64_t base = (int64_t)en.e[0] * blk_stride;  // wave-uniform
-      const int kvoff = c.kvh * D * ES;
+      const int kvoff = c.kvh * D * KS;
       const int tk = min(ts + col, c.L - 1);
-      const unsigned koff = (unsigned)((tk & bmask) * row_stride32 + kvoff + row * 16);
+      const unsigned koff = (unsigned)((tk & bmask) * row_stride32 + kvoff + row * LB);
 #pragma unroll
-      for (int kk = 0; kk < NLD; ++kk) kb[kk] = ld16_stream(kpool + base + koff + kk * 64);
+      for (int kk = 0; kk < NLD; ++kk) kb[kk] = ldkv(kpool + base + koff + kk * 4 * LB);
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const int tv = min(ts + 4 * row + i, c.L - 1);
-        const unsigned voff = (unsigned)((tv & bmask) * row_stride32 + kvoff + col * 16);
-        vb[i] = ld16_stream(vpool + base + voff);
+        const unsigned voff = (unsigned)((tv & bmask) * row_stride32 + kvoff + col * LB);
+        vb[i] = ldkv(vpool + base + voff);
       }
     } else if constexpr (UNI) {
 #pragma unroll
@@ -420,8 +480,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
         const int tok = min(ts + i * RPW + row, c.L - 1);
         const int64_t base = (int64_t)en.e[i] * blk_stride;  // wave-uniform
         const unsigned off = (unsigned)((tok & bmask) * row_stride32 + head_off);
-        kb[i] = ld16_stream(kpool + base + off);
-        vb[i] = ld16_stream(vpool + base + off);
+        kb[i] = ldkv(kpool + base + off);
+        vb[i] = ldkv(vpool + base + off);
       }
     } else {
       const int32_t* tb = a.block_tables + (int64_t)c.s * a.max_nb;
@@ -431,8 +491,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
         const int ph = tb[tok >> log2B];
         const int64_t off =
             (int64_t)ph * blk_stride + (int64_t)(tok & bmask) * row_stride + head_off;
-        kb[i] = ld16_stream(kpool + off);
-        vb[i] = ld16_stream(vpool + off);
+        kb[i] = ldkv(kpool + off);
+        vb[i] = ldkv(vpool + off);
       }
     }
   };
@@ -467,10 +527,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
   };
 
   // One tile.  FULL: every row of the tile is a valid token.
-  auto compute = [&](const Cursor& c, const uint4 (&qv)[QN], const uint4 (&kb)[NLD],
-                     const uint4 (&vb)[NLD], auto full_tag) __attribute__((always_inline)) {
+  // K as 16-bit elements and V as fp32 (FP8 codes widened exactly)
+  auto kfrag = [&](const KVT& x) __attribute__((always_inline)) -> uint4 {
+    if constexpr (F8) return fp8x8_to16<DT>(x);
+    else return x;
+  };
+  auto vwiden = [&](const KVT& x, float* vf) __attribute__((always_inline)) {
+    if constexpr (F8) fp8x8_to_f32(x, vf);
+    else widen16<DT>(x, vf);
+  };
+  auto compute = [&](const Cursor& c, const uint4 (&qv)[QN], const KVT (&kb)[NLD],
+                     const KVT (&vb)[NLD], auto full_tag) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int ts = c.j * TILE;
+    float zsc;
+    if constexpr (F8) zsc = c.zs;
+    else zsc = c_scale;
     if constexpr (MF) {
       // S = K q^T on the matrix cores: lane (row, col) receives the scores of
       // tokens 4 * row + i (i < 4) for head col % GC.  The running max m[0] of
@@ -478,11 +550,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
       // across lane rows); l[0] is this lane's partial sum over its 4 tokens.
       f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < NLD; ++kk) sacc = mfma16<DT>(kb[kk], qv[kk], sacc);
+      for (int kk = 0; kk < NLD; ++kk) sacc = mfma16<DT>(kfrag(kb[kk]), qv[kk], sacc);
       float z[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float zz = sacc[i] * c_scale;
+        const float zz = sacc[i] * zsc;
         if constexpr (FULL) z[i] = zz;
         else z[i] = (ts + 4 * row + i < c.L) ? zz : -__builtin_inff();
       }
@@ -515,7 +587,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         float vf[EPL];
-        widen16<DT>(vb[i], vf);
+        vwiden(vb[i], vf);
 #pragma unroll
         for (int g = 0; g < GC; ++g) {
           const float pg = quad_bcast(p[i], g);
@@ -528,9 +600,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
     float z[NLD][GC];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
+      const uint4 kx = kfrag(kb[i]);
 #pragma unroll
       for (int g = 0; g < GC; ++g) {
-        const float zz = row_sum<LPR>(dot16<DT>(kb[i], qv[g])) * c_scale;
+        const float zz = row_sum<LPR>(dot16<DT>(kx, qv[g])) * zsc;
         if constexpr (FULL) z[i][g] = zz;
         else z[i][g] = (ts + i * RPW + row < c.L) ? zz : -__builtin_inff();
       }
@@ -574,7 +647,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       float vf[EPL];
-      widen16<DT>(vb[i], vf);
+      vwiden(vb[i], vf);
 #pragma unroll
       for (int g = 0; g < GC; ++g)
 #pragma unroll
@@ -652,6 +725,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
     // is written directly, otherwise its state goes to the row's own slot.  A
     // row cut by the range leaves its state in slot 2w (the row holding x0) or
     // 2w + 1 (the row holding x1 - 1) for the merge kernel.
+    if constexpr (F8) {  // V scale of the row's KV head (common to all its partial states)
+#pragma unroll
+      for (int g = 0; g < GC; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] *= c.vs;
+    }
     const bool complete = row_xb >= x0 && row_xb + c.nt <= x1;
     if (complete && a.out_dt == DT_F32) {
       if (row == 0) {
@@ -700,8 +779,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
   // compute tile x (cursor cc), then finish the row if it ends here.  last: x
   // is the wave's final tile (a constant false inside the main loop).  At a row
   // switch the next row's q is loaded (and waited for): once per row.
-  auto finish = [&](int x, const Cursor& cc, const Cursor& cn, const uint4 (&kbc)[NLD],
-                    const uint4 (&vbc)[NLD], uint4 (&qv)[QN], bool last) __attribute__((always_inline)) {
+  auto finish = [&](int x, const Cursor& cc, const Cursor& cn, const KVT (&kbc)[NLD],
+                    const KVT (&vbc)[NLD], uint4 (&qv)[QN], bool last) __attribute__((always_inline)) {
     if (!MF && (cc.j + 1) * TILE <= cc.L) compute(cc, qv, kbc, vbc, TrueT{});
     else compute(cc, qv, kbc, vbc, FalseT{});  // (the matrix-core path always masks: 8 selects)
     if (last || cn.j == 0) {
@@ -725,7 +804,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
   uint4 qv[QN];
   load_q(c0, qv);
   // NBUF buffer sets: tiles x + 1 .. x + NBUF - 1 load while tile x is computed.
-  uint4 kb[NBUF][NLD], vb[NBUF][NLD];
+  KVT kb[NBUF][NLD], vb[NBUF][NLD];
   Cursor cs[NBUF];  // cs[k]: cursor of tile x + k
   cs[0] = c0;
   issue(cs[0], entries(cs[0]), kb[0], vb[0]);
@@ -849,13 +928,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
 
 // ---- host side -----------------------------------------------------------------
 
-template <int DT, int D, int GC, bool UNI, bool MF>
+template <int DT, int D, int GC, bool UNI, bool MF, bool F8>
 int occupancy_of() {
   static int occ = -1;
   if (occ < 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(&decode_split_kernel<DT, D, GC, UNI, MF>), kThreads,
+            &n, reinterpret_cast<const void*>(&decode_split_kernel<DT, D, GC, UNI, MF, F8>), kThreads,
             0) != hipSuccess ||
         n < 1)
       n = 1;
@@ -877,16 +956,16 @@ int device_cu_count() {
 
 // Split launch (one resident wave set: CUs x occupancy, capped by grid_cap)
 // followed by the merge launch.
-template <int DT, int D, int GC, bool UNI, bool MF>
+template <int DT, int D, int GC, bool UNI, bool MF, bool F8>
 pkv_status launch_split(DecodeArgs a, int grid_cap, int ncu, hipStream_t stream) {
   // Matrix-core path: one workgroup (one wave per SIMD, three tiles in
   // flight each) per CU measured fastest -- 7% ahead of two per CU on the
   // Llama-3-8B batch.  Vector path: every resident workgroup.
-  int64_t grid = (int64_t)ncu * (MF ? 1 : occupancy_of<DT, D, GC, UNI, MF>());
+  int64_t grid = (int64_t)ncu * (MF ? 1 : occupancy_of<DT, D, GC, UNI, MF, F8>());
   if (grid > grid_cap) grid = grid_cap;
   if (grid < 1) grid = 1;
   a.n_waves = (int)grid * kWaves;
-  hipLaunchKernelGGL((decode_split_kernel<DT, D, GC, UNI, MF>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((decode_split_kernel<DT, D, GC, UNI, MF, F8>), dim3((unsigned)grid),
                      dim3(kThreads), 0, stream, a);
   pkv_status st = check_launch("paged_attention_decode (split)");
   if (st != PKV_OK) return st;
@@ -895,32 +974,32 @@ pkv_status launch_split(DecodeArgs a, int grid_cap, int ncu, hipStream_t stream)
   return check_launch("paged_attention_decode (merge)");
 }
 
-template <int DT, int D, int GC>
+template <int DT, int D, int GC, bool F8>
 pkv_status launch_typed(const DecodeArgs& a, int grid_cap, int ncu, bool uni, hipStream_t stream) {
-  // matrix cores for q . k: 16-bit KV, D = 128, GQA groups of 4, a tile in one block
+  // matrix cores for q . k: 16-bit q, D = 128, GQA groups of 4, a tile in one block
   if constexpr (DT != DT_F32 && D == 128 && GC == 4) {
-    if (a.B >= 16) return launch_split<DT, D, GC, true, true>(a, grid_cap, ncu, stream);
+    if (a.B >= 16) return launch_split<DT, D, GC, true, true, F8>(a, grid_cap, ncu, stream);
   }
-  if (uni) return launch_split<DT, D, GC, true, false>(a, grid_cap, ncu, stream);
-  return launch_split<DT, D, GC, false, false>(a, grid_cap, ncu, stream);
+  if (uni) return launch_split<DT, D, GC, true, false, F8>(a, grid_cap, ncu, stream);
+  return launch_split<DT, D, GC, false, false, F8>(a, grid_cap, ncu, stream);
 }
 
-template <int DT, int D>
+template <int DT, int D, bool F8>
 pkv_status launch_gc(const DecodeArgs& a, int grid_cap, int ncu, bool uni, hipStream_t stream) {
   switch (a.gc) {
-    case 1: return launch_typed<DT, D, 1>(a, grid_cap, ncu, uni, stream);
-    case 2: return launch_typed<DT, D, 2>(a, grid_cap, ncu, uni, stream);
-    case 4: return launch_typed<DT, D, 4>(a, grid_cap, ncu, uni, stream);
-    case 8: return launch_typed<DT, D, 8>(a, grid_cap, ncu, uni, stream);
+    case 1: return launch_typed<DT, D, 1, F8>(a, grid_cap, ncu, uni, stream);
+    case 2: return launch_typed<DT, D, 2, F8>(a, grid_cap, ncu, uni, stream);
+    case 4: return launch_typed<DT, D, 4, F8>(a, grid_cap, ncu, uni, stream);
+    case 8: return launch_typed<DT, D, 8, F8>(a, grid_cap, ncu, uni, stream);
   }
   return fail(PKV_ERR_UNSUPPORTED, "decode: head chunk %d", a.gc);
 }
 
-template <int DT>
+template <int DT, bool F8>
 pkv_status launch_d(const DecodeArgs& a, int grid_cap, int ncu, bool uni, hipStream_t stream) {
   switch (a.D) {
-    case 64: return launch_gc<DT, 64>(a, grid_cap, ncu, uni, stream);
-    case 128: return launch_gc<DT, 128>(a, grid_cap, ncu, uni, stream);
+    case 64: return launch_gc<DT, 64, F8>(a, grid_cap, ncu, uni, stream);
+    case 128: return launch_gc<DT, 128, F8>(a, grid_cap, ncu, uni, stream);
   }
   return fail(PKV_ERR_UNSUPPORTED, "decode: head_dim %d", a.D);
 }
@@ -976,7 +1055,9 @@ pkv_status plan_decode(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t /*
   return PKV_OK;
 }
 
-pkv_status launch_decode(int kv_dt, const DecodePlan& plan, DecodeArgs a, hipStream_t stream) {
+pkv_status launch_decode(int kv_dt, bool fp8, const DecodePlan& plan, DecodeArgs a,
+                         hipStream_t stream) {
+  // (kv_dt: the dtype of q; the lane layout follows it, also over FP8 pools)
   int tile = 0, rpw = 0;
   tile_geometry(kv_dt, a.D, &tile, &rpw);
   const bool uni = a.B >= rpw;
@@ -999,11 +1080,19 @@ pkv_status launch_decode(int kv_dt, const DecodePlan& plan, DecodeArgs a, hipStr
     if (cap > plan.max_waves / kWaves) cap = plan.max_waves / kWaves;
     if (cap < 1) cap = 1;
     pkv_status st;
-    switch (kv_dt) {
-      case DT_F32: st = launch_d<DT_F32>(b, (int)cap, ncu, uni, stream); break;
-      case DT_F16: st = launch_d<DT_F16>(b, (int)cap, ncu, uni, stream); break;
-      case DT_BF16: st = launch_d<DT_BF16>(b, (int)cap, ncu, uni, stream); break;
-      default: return fail(PKV_ERR_UNSUPPORTED, "decode: kv dtype %d", kv_dt);
+    if (fp8) {
+      switch (kv_dt) {
+        case DT_F16: st = launch_d<DT_F16, true>(b, (int)cap, ncu, uni, stream); break;
+        case DT_BF16: st = launch_d<DT_BF16, true>(b, (int)cap, ncu, uni, stream); break;
+        default: return fail(PKV_ERR_UNSUPPORTED, "decode_fp8: q dtype %d", kv_dt);
+      }
+    } else {
+      switch (kv_dt) {
+        case DT_F32: st = launch_d<DT_F32, false>(b, (int)cap, ncu, uni, stream); break;
+        case DT_F16: st = launch_d<DT_F16, false>(b, (int)cap, ncu, uni, stream); break;
+        case DT_BF16: st = launch_d<DT_BF16, false>(b, (int)cap, ncu, uni, stream); break;
+        default: return fail(PKV_ERR_UNSUPPORTED, "decode: kv dtype %d", kv_dt);
+      }
     }
     if (st != PKV_OK) return st;
   }

@@ -13,9 +13,9 @@ pkv_status fail(pkv_status s, const char* fmt, ...) __attribute__((format(printf
 pkv_status check_launch(const char* what);
 
 // ---- dtype helpers --------------------------------------------------------------
-enum : int { DT_F32 = PKV_F32, DT_F16 = PKV_F16, DT_BF16 = PKV_BF16 };
+enum : int { DT_F32 = PKV_F32, DT_F16 = PKV_F16, DT_BF16 = PKV_BF16, DT_FP8 = PKV_FP8_E4M3 };
 
-constexpr int dt_bytes(int dt) { return dt == DT_F32 ? 4 : 2; }
+constexpr int dt_bytes(int dt) { return dt == DT_F32 ? 4 : dt == DT_FP8 ? 1 : 2; }
 
 // Reinterpretation helpers usable on host and device.
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t packed) {
@@ -79,6 +79,11 @@ pkv_status launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     void* v_cache, const int64_t* slot_mapping, int32_t T,
                                     int64_t row_bytes, int32_t B, hipStream_t stream);
 
+pkv_status launch_reshape_and_cache_fp8(const void* key, const void* value, int in_dt,
+                                        void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                                        int32_t T, int32_t Hkv, int32_t D, const float* k_scale,
+                                        const float* v_scale, hipStream_t stream);
+
 pkv_status launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
                               const int64_t* pairs, int32_t N, int64_t block_bytes,
                               hipStream_t stream);
@@ -111,8 +116,12 @@ struct DecodeArgs {
   int32_t max_ctx;       // context lengths are clamped to this (<= max_nb * B)
   int32_t out_dt;
   float scale_log2;      // softmax scale * log2(e)
+  const float* k_scale;  // FP8 pools: per-KV-head scales (device, [Hkv]); else unused
+  const float* v_scale;
 };
-pkv_status launch_decode(int kv_dt, const DecodePlan& plan, DecodeArgs a, hipStream_t stream);
+// q_dt: dtype of q (and of the pools unless fp8); fp8: the pools hold E4M3 codes
+pkv_status launch_decode(int q_dt, bool fp8, const DecodePlan& plan, DecodeArgs a,
+                         hipStream_t stream);
 
 struct PrefillArgs {
   void* out;

@@ -21,6 +21,9 @@ which are not available here):
                       uniform [1, 512] tokens.
 * ``prefill_bf16``  - 8 sequences, each a 512-token query chunk after a paged prior
                       context of uniform [4096, 32768] tokens.
+* ``fp8_pools``     - FP8 (OCP E4M3) K/V codes for any of the batches above: random
+                      codes drawn directly (no quantization is computed here) and
+                      one random scale per KV head for K and for V.
 
 Draw order for every workload: lengths -> free-list permutation -> q -> K/V.
 Rows of a block past the sequence's fill, unreferenced pool blocks and table
@@ -430,3 +433,85 @@ def cu_seqlens(counts) -> np.ndarray:
     out = np.zeros(len(counts) + 1, np.int32)
     out[1:] = np.cumsum(counts)
     return out
+
+
+# ---------------------------------------------------------------- FP8 (E4M3) pools
+FP8_NAN = np.uint8(0x7F)
+
+
+def _fp8_code_table() -> np.ndarray:
+    """Code for each 16-bit random draw u: bit 15 is the sign; t = u & 0x7FFF
+    picks the magnitude code -- t < 3328 (about 10%) cycles through all 127
+    finite magnitudes (zeros, subnormals and 448 included), the rest spread
+    over exponent fields 10..14 with all 8 mantissas (magnitudes 4..240, like
+    quantized N(0, 1) / scale data).  No NaN code."""
+    u = np.arange(65536, dtype=np.int64)
+    t = u & 0x7FFF
+    j = t - 3328
+    mag = np.where(t < 3328, t % 127, ((10 + (j * 5) // (32768 - 3328)) << 3) | (j % 8))
+    return (mag | ((u >> 8) & 0x80)).astype(np.uint8)
+
+
+_FP8_TABLE = _fp8_code_table()
+
+
+def fp8_codes(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
+    """Random finite OCP E4M3 codes (table lookup of uniform 16-bit draws,
+    chunked over threads like ``_normal``; depends only on ``rng`` and shape)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, np.uint8)
+    starts = list(range(0, n, chunk)) or [0]
+    seeds = rng.integers(0, 2**63 - 1, size=len(starts))
+
+    def fill(i):
+        lo = starts[i]
+        m = min(chunk, n - lo)
+        g = np.random.default_rng(int(seeds[i]))
+        out[lo:lo + m] = _FP8_TABLE[g.integers(0, 65536, m, dtype=np.uint16)]
+
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        list(ex.map(fill, range(len(starts))))
+    return out.reshape(shape)
+
+
+@dataclass
+class Fp8Pools:
+    """E4M3 contents for a PagedBatch's data blocks (same indexing as
+    ``k_blocks`` / ``v_blocks``; stale rows hold the NaN code), the new-token
+    rows of this step, and fp32 scales [Hkv]."""
+    k_blocks: np.ndarray   # uint8 [n, B, Hkv, D]
+    v_blocks: np.ndarray
+    new_k: np.ndarray      # uint8 [T, Hkv, D]: the codes already at this step's slots
+    new_v: np.ndarray
+    k_scale: np.ndarray    # float32 [Hkv]
+    v_scale: np.ndarray
+
+    def full_pool(self, batch: "PagedBatch"):
+        shape = (batch.NB, batch.B, batch.Hkv, batch.D)
+        k = np.full(shape, FP8_NAN, np.uint8)
+        v = np.full(shape, FP8_NAN, np.uint8)
+        k[batch.block_ids], v[batch.block_ids] = self.k_blocks, self.v_blocks
+        return k, v
+
+
+def fp8_pools(batch: "PagedBatch", seed: int) -> Fp8Pools:
+    """FP8 codes for ``batch``'s data blocks: rows the batch marks stale (NaN in
+    its 16-bit blocks) stay NaN codes; scales uniform on [0.004, 0.02]."""
+    rng = np.random.default_rng(seed)
+    shape = batch.k_blocks.shape
+    kc = fp8_codes(rng, shape)
+    vc = fp8_codes(rng, shape)
+    stale = np.isnan(storage_to_f32(batch.k_blocks[:, :, 0, 0], batch.dtype))  # [n, B]
+    kc[stale] = FP8_NAN
+    vc[stale] = FP8_NAN
+    ks = rng.uniform(0.004, 0.02, batch.Hkv).astype(np.float32)
+    vs = rng.uniform(0.004, 0.02, batch.Hkv).astype(np.float32)
+    where = {int(b): i for i, b in enumerate(batch.block_ids)}
+    if batch.new_slots.size:
+        idx = np.array([where[int(x)] for x in batch.new_slots // batch.B])
+        off = batch.new_slots % batch.B
+        nk, nv = kc[idx, off], vc[idx, off]
+    else:
+        nk = np.zeros((0, batch.Hkv, batch.D), np.uint8)
+        nv = nk.copy()
+    return Fp8Pools(k_blocks=kc, v_blocks=vc, new_k=nk, new_v=nv, k_scale=ks, v_scale=vs)
