@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prefill row (used under the profilers)")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="time only the FP8 decode row (used under the profilers)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="context tokens of the bounded oracle sample (0: the whole batch)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -159,6 +161,43 @@ def main():
         print(json.dumps({"prefill_bf16_8x512": prefill_row()}), flush=True)
         return
 
+    def fp8_row(b, d, bf16_ms):
+        """The Llama-3-8B batch over FP8 (E4M3) pools with per-KV-head scales:
+        half the KV bytes of the bf16 step."""
+        t0 = time.time()
+        f8 = W.fp8_pools(b, args.seed + 1)
+        shape = (b.NB, b.B, b.Hkv, b.D)
+        idx = torch.from_numpy(b.block_ids).to(dev)
+        k8 = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
+        v8 = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
+        k8.index_copy_(0, idx, torch.from_numpy(f8.k_blocks).to(dev))
+        v8.index_copy_(0, idx, torch.from_numpy(f8.v_blocks).to(dev))
+        ks8 = torch.from_numpy(f8.k_scale).to(dev)
+        vs8 = torch.from_numpy(f8.v_scale).to(dev)
+        del f8
+        log(f"[bench] fp8 pools generated in {time.time() - t0:.1f}s")
+
+        def dec8():
+            pkv.paged_attention_decode_fp8(d.out, d.q, k8, v8, ks8, vs8, d.tables, d.lens,
+                                           b.max_context_len, b.scale, workspace=d.ws)
+
+        ms8, _ = time_fn(dec8, 20)
+        b8 = b.kv_read_bytes() // 2
+        log(f"[bench] decode_llama3_8b_fp8: {ms8 * 1e3:.1f} us, {b8 / ms8 / 1e6:.0f} GB/s of FP8 KV")
+        row = {"ms": round(ms8, 5), "GB/s": round(b8 / ms8 / 1e6, 1),
+               "frac_of_hbm_peak": round(b8 / ms8 / 1e6 / HBM_PEAK_GBS, 4)}
+        if bf16_ms:
+            row["speedup_vs_bf16"] = round(bf16_ms / ms8, 3)
+        del k8, v8
+        return row
+
+    if args.fp8_only:
+        b = W.llama3_8b_bf16(args.seed)
+        d = Dev(b)
+        d.free()
+        print(json.dumps({"decode_llama3_8b_fp8": fp8_row(b, d, None)}), flush=True)
+        return
+
     # ------------------------------------------------------------ headline
     t0 = time.time()
     b = W.llama3_8b_bf16(args.seed)
@@ -259,31 +298,7 @@ def main():
         rb = 2 * 2 * b.new_k.size * 2   # read + write of K and V rows
         rows["reshape_and_cache_256_tokens"] = {"ms": round(rms, 5), "GB/s": round(rb / rms / 1e6, 1)}
 
-        # the same batch over FP8 (E4M3) pools with per-KV-head scales: half the bytes
-        t0 = time.time()
-        f8 = W.fp8_pools(b, args.seed + 1)
-        shape = (b.NB, b.B, b.Hkv, b.D)
-        idx = torch.from_numpy(b.block_ids).to(dev)
-        k8 = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
-        v8 = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
-        k8.index_copy_(0, idx, torch.from_numpy(f8.k_blocks).to(dev))
-        v8.index_copy_(0, idx, torch.from_numpy(f8.v_blocks).to(dev))
-        ks8 = torch.from_numpy(f8.k_scale).to(dev)
-        vs8 = torch.from_numpy(f8.v_scale).to(dev)
-        log(f"[bench] fp8 pools generated in {time.time() - t0:.1f}s")
-
-        def dec8():
-            pkv.paged_attention_decode_fp8(d.out, d.q, k8, v8, ks8, vs8, d.tables, d.lens,
-                                           b.max_context_len, b.scale, workspace=d.ws)
-
-        ms8, _ = time_fn(dec8, 20)
-        b8 = kv_bytes // 2
-        rows["decode_llama3_8b_fp8"] = {
-            "ms": round(ms8, 5), "GB/s": round(b8 / ms8 / 1e6, 1),
-            "frac_of_hbm_peak": round(b8 / ms8 / 1e6 / HBM_PEAK_GBS, 4),
-            "speedup_vs_bf16": round(dec_ms / ms8, 3)}
-        log(f"[bench] decode_llama3_8b_fp8: {ms8 * 1e3:.1f} us, {b8 / ms8 / 1e6:.0f} GB/s of FP8 KV")
-        del k8, v8, f8
+        rows["decode_llama3_8b_fp8"] = fp8_row(b, d, dec_ms)
         d.free()
         del d
         torch.cuda.empty_cache()

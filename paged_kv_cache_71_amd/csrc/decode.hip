@@ -465,9 +465,24 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
       const int64_t base = (int64_t)en.e[0] * blk_stride;  // wave-uniform
       const int kvoff = c.kvh * D * KS;
       const int tk = min(ts + col, c.L - 1);
-      const unsigned koff = (unsigned)((tk & bmask) * row_stride32 + kvoff + row * LB);
+      if constexpr (F8) {
+        // FP8: lane (token col, group row) takes the 32 contiguous codes
+        // 32 row .. 32 row + 31 of its token in two 16-byte loads; k-step kk
+        // uses codes 32 row + 8 kk .. + 7 (q is loaded with the same order).
+        // Each load instruction then reads half of every token's 128-byte
+        // line instead of a quarter: half the cache-line requests.
+        const unsigned koff = (unsigned)((tk & bmask) * row_stride32 + kvoff + row * 32);
+        const uint4 k0 = ld16_stream(kpool + base + koff);
+        const uint4 k1 = ld16_stream(kpool + base + koff + 16);
+        kb[0] = make_uint2(k0.x, k0.y);
+        kb[1] = make_uint2(k0.z, k0.w);
+        kb[2] = make_uint2(k1.x, k1.y);
+        kb[3] = make_uint2(k1.z, k1.w);
+      } else {
+        const unsigned koff = (unsigned)((tk & bmask) * row_stride32 + kvoff + row * LB);
 #pragma unroll
-      for (int kk = 0; kk < NLD; ++kk) kb[kk] = ldkv(kpool + base + koff + kk * 4 * LB);
+        for (int kk = 0; kk < NLD; ++kk) kb[kk] = ldkv(kpool + base + koff + kk * 4 * LB);
+      }
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const int tv = min(ts + 4 * row + i, c.L - 1);
@@ -501,10 +516,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
     if constexpr (MF) {
       // q^T as the MFMA B operand, the GC heads repeated across the 16
       // columns: lane l holds head (l % 16) % GC, elements 32 kk + 8 (l / 16) ..
+      // (FP8 pools: elements 32 (l / 16) + 8 kk .., the order of the K loads)
       const char* qp = static_cast<const char*>(a.q) +
-                       (((int64_t)c.s * a.Hq + c.h0 + (col % GC)) * D) * ES + row * 16;
+                       (((int64_t)c.s * a.Hq + c.h0 + (col % GC)) * D) * ES + row * (F8 ? 64 : 16);
 #pragma unroll
-      for (int kk = 0; kk < QN; ++kk) qv[kk] = ld16(qp + kk * 64);
+      for (int kk = 0; kk < QN; ++kk) qv[kk] = ld16(qp + kk * (F8 ? 16 : 64));
     } else {
       const char* qp = static_cast<const char*>(a.q) +
                        (((int64_t)c.s * a.Hq + c.h0) * D) * ES + col * 16;
