@@ -161,6 +161,28 @@ def main():
         print(json.dumps({"prefill_bf16_8x512": prefill_row()}), flush=True)
         return
 
+    def cascade_row(bb, dd, plain_ms):
+        """The shared-prefix batch through the cascade path: each prompt's
+        prefix blocks read once per 4-sample group, merged with the suffixes."""
+        n = bb.meta["n"]
+        cu = torch.arange(0, bb.S + 1, n, dtype=torch.int32, device=dev)
+        plen = (bb.meta["prompt_len"] // bb.B) * bb.B
+        plens = torch.full((bb.S // n,), plen, dtype=torch.int32, device=dev)
+        ws = torch.empty(max(pkv.decode_cascade_workspace_size(
+            bb.S, bb.Hq, bb.Hkv, bb.D, bb.B, bb.max_context_len, bb.S // n, n, plen, bb.dtype), 1),
+            dtype=torch.uint8, device=dev)
+
+        def run():
+            pkv.paged_attention_decode_cascade(dd.out, dd.q, dd.k, dd.v, dd.tables, dd.lens,
+                                               bb.max_context_len, bb.scale, cu, plens, n, plen,
+                                               workspace=ws)
+
+        ms, _ = time_fn(run, 20)
+        log(f"[bench] decode_shared_prefix_bf16_cascade: {ms * 1e3:.1f} us")
+        return {"ms": round(ms, 5), "logical_GB/s": round(bb.kv_read_bytes() / ms / 1e6, 1),
+                "unique_GB/s": round(bb.unique_kv_bytes() / ms / 1e6, 1),
+                "speedup_vs_plain": round(plain_ms / ms, 3)}
+
     def fp8_row(b, d, bf16_ms):
         """The Llama-3-8B batch over FP8 (E4M3) pools with per-KV-head scales:
         half the KV bytes of the bf16 step."""
@@ -311,6 +333,8 @@ def main():
             rows[name] = {"ms": round(ms, 5), "logical_GB/s": round(bb.kv_read_bytes() / ms / 1e6, 1),
                           "unique_GB/s": round(bb.unique_kv_bytes() / ms / 1e6, 1)}
             log(f"[bench] {name}: {ms * 1e3:.1f} us")
+            if name == "decode_shared_prefix_bf16":
+                rows[name + "_cascade"] = cascade_row(bb, dd, ms)
             dd.free()
             del dd
             torch.cuda.empty_cache()

@@ -122,6 +122,51 @@ pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void
                                       void* stream);
 
 /* ------------------------------------------------------------------------
+ * paged_attention_decode_cascade -- decode for a batch whose sequences come
+ * in groups that share a prefix of blocks (the samples forked from one
+ * prompt), reading each group's prefix once instead of once per member.
+ *
+ * Defined by the S06 PagedAttention chapter ("in production" section: a
+ * cascade path batches the shared prefix apart from the forked suffixes),
+ * CMU 11-868 lecture 24 sec. 7.3 and further reading (cascade attention /
+ * cascade inference for shared-prefix batch decode) and CS349D lecture 3 sec.
+ * 4.1 (forked sequences share the parent's blocks).  The result is that of
+ * pkv_paged_attention_decode on the same arguments (one softmax over every
+ * cached token of each sequence); only the summation order differs: the
+ * prefix and the suffix are attended separately and their two softmax states
+ * merged (log-sum-exp), so the output agrees with the plain decode to fp32
+ * rounding, not bit for bit.
+ *
+ *   (arguments as for pkv_paged_attention_decode, 16- or 32-bit pools)
+ *   cu_group_seqs     : device int32 [n_groups + 1]; group g is sequences
+ *                       cu[g] .. cu[g+1]-1 (consecutive, every sequence in
+ *                       exactly one group: cu[0] = 0, cu[n_groups] = S)
+ *   group_prefix_lens : device int32 [n_groups]; tokens every member of the
+ *                       group holds in the same physical blocks (a multiple
+ *                       of B; longer values are cut to the shortest member and
+ *                       to max_prefix_len, then rounded down to a multiple of
+ *                       B); 0 for a group that shares nothing
+ *   n_groups          : host, >= 1 when S > 0
+ *   max_group_size    : host bound >= every group's size
+ *   max_prefix_len    : host bound >= every prefix length used (values above
+ *                       max_context_len act as max_context_len)
+ *   workspace         : device scratch of pkv_decode_cascade_workspace_size()
+ *                       bytes (depends on the arguments only)
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_decode_cascade_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                                             int32_t B, int32_t max_context_len, int32_t n_groups,
+                                             int32_t max_group_size, int32_t max_prefix_len,
+                                             pkv_dtype kv_dtype, size_t* bytes);
+
+pkv_status pkv_paged_attention_decode_cascade(
+    void* out, pkv_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,
+    pkv_dtype kv_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t max_context_len, int32_t S, int32_t Hq, int32_t Hkv,
+    int32_t D, int32_t B, float scale, const int32_t* cu_group_seqs,
+    const int32_t* group_prefix_lens, int32_t n_groups, int32_t max_group_size,
+    int32_t max_prefix_len, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * FP8 KV cache -- the pools hold OCP E4M3 codes, one byte per element, with
  * one fp32 scale per KV head for K and one for V.
  *

@@ -7,12 +7,14 @@ benchmark.  Loading is lazy: ``load_library()`` (or the first call) loads the
 library and raises if it has not been built.
 """
 from ._binding import (BlockManager, PkvError, PkvOOM, copy_blocks, declared_symbols,
-                       decode_workspace_size, load_library, paged_attention_decode,
+                       decode_cascade_workspace_size, decode_workspace_size, load_library,
+                       paged_attention_decode, paged_attention_decode_cascade,
                        paged_attention_decode_fp8, paged_attention_prefill, reshape_and_cache,
                        reshape_and_cache_fp8)
 
 __all__ = [
     "BlockManager", "PkvError", "PkvOOM", "copy_blocks", "declared_symbols",
-    "decode_workspace_size", "load_library", "paged_attention_decode", "paged_attention_decode_fp8",
+    "decode_cascade_workspace_size", "decode_workspace_size", "load_library",
+    "paged_attention_decode_cascade", "paged_attention_decode", "paged_attention_decode_fp8",
     "paged_attention_prefill", "reshape_and_cache", "reshape_and_cache_fp8",
 ]

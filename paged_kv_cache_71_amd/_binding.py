@@ -62,6 +62,11 @@ def load_library(path: str | None = None):
                                              i32, i32, i32, i32, f32, P]),
         "pkv_copy_blocks": (st, [P, P, i32, P, i32, i32, i32, i32, st, P]),
         "pkv_reshape_and_cache_fp8": (st, [P, P, st, P, P, P, i32, i32, i32, i32, i64, P, P, P]),
+        "pkv_decode_cascade_workspace_size": (st, [i32, i32, i32, i32, i32, i32, i32, i32, i32, st,
+                                                   SZP]),
+        "pkv_paged_attention_decode_cascade": (st, [P, st, P, P, P, st, P, i32, P, i32, i32, i32,
+                                                    i32, i32, i32, f32, P, P, i32, i32, i32, P, sz,
+                                                    P]),
         "pkv_paged_attention_decode_fp8": (st, [P, st, P, st, P, P, P, P, P, i32, P, i32, i32, i32,
                                                 i32, i32, i32, f32, P, sz, P]),
         "pkv_bm_create": (st, [i32, i32, P, ctypes.POINTER(P)]),
@@ -239,6 +244,56 @@ def copy_blocks(k_caches, v_caches, block_pairs, stream=None) -> None:
     _check(lib.pkv_copy_blocks(ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp, ctypes.c_void_p),
                                L, pairs_ptr, N, B, Hkv, D, dtype_code(k_caches[0]),
                                _stream(stream)), "copy_blocks")
+
+
+def decode_cascade_workspace_size(S: int, Hq: int, Hkv: int, D: int, B: int, max_context_len: int,
+                                  n_groups: int, max_group_size: int, max_prefix_len: int,
+                                  dtype: str) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    _check(lib.pkv_decode_cascade_workspace_size(S, Hq, Hkv, D, B, max_context_len, n_groups,
+                                                 max_group_size, max_prefix_len, DTYPE_CODE[dtype],
+                                                 ctypes.byref(out)), "decode_cascade_workspace_size")
+    return out.value
+
+
+def paged_attention_decode_cascade(out, q, k_cache, v_cache, block_tables, context_lens,
+                                   max_context_len: int, scale: float, cu_group_seqs,
+                                   group_prefix_lens, max_group_size: int, max_prefix_len: int,
+                                   workspace=None, stream=None):
+    """Decode for consecutive groups of sequences sharing a prefix of blocks
+    (``cu_group_seqs`` [n_groups + 1], ``group_prefix_lens`` [n_groups], device
+    int32): each group's prefix is read once and merged with every member's
+    suffix.  Same result as paged_attention_decode up to fp32 rounding."""
+    torch = _torch()
+    lib = load_library()
+    S, Hq, D = q.shape
+    NB, B, Hkv, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("paged_attention_decode_cascade: shape mismatch")
+    if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("paged_attention_decode_cascade: q/k/v dtype mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("paged_attention_decode_cascade: block_tables [S, max_nb] / context_lens [S]")
+    n_groups = cu_group_seqs.shape[0] - 1
+    if group_prefix_lens.shape != (n_groups,):
+        raise ValueError("paged_attention_decode_cascade: group_prefix_lens must be [n_groups]")
+    kdt = {0: "f32", 1: "f16", 2: "bf16"}[dtype_code(k_cache)]
+    need = decode_cascade_workspace_size(S, Hq, Hkv, D, B, max_context_len, n_groups,
+                                         max_group_size, max_prefix_len, kdt)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pkv_paged_attention_decode_cascade(
+        _dev(out, "out"), dtype_code(out), _dev(q, "q"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), dtype_code(k_cache),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B,
+        float(scale), _dev(cu_group_seqs, "cu_group_seqs", torch.int32),
+        _dev(group_prefix_lens, "group_prefix_lens", torch.int32), n_groups, int(max_group_size),
+        int(max_prefix_len), ws_ptr, ws_bytes, _stream(stream)), "paged_attention_decode_cascade")
+    return out
 
 
 def _fp8_pool(t, name):

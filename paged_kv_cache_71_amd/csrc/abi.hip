@@ -128,14 +128,24 @@ pkv_status pkv_decode_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t
 
 // Both decode entry points: q_dtype is the dtype of q (and of the pools unless
 // fp8, where the pools hold E4M3 codes with per-KV-head scales).
+// Groups of sequences sharing a prefix (cascade decode), if on.
+struct CascadeGroups {
+  bool on = false;
+  const int32_t* cu = nullptr;
+  const int32_t* prefix_lens = nullptr;
+  int32_t n_groups = 0, max_group_size = 0, max_prefix_len = 0;
+};
+
 static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype kv_dtype,
                               bool fp8, const void* k_cache, const void* v_cache,
                               const float* k_scale, const float* v_scale,
                               const int32_t* block_tables, int32_t max_blocks_per_seq,
                               const int32_t* context_lens, int32_t max_context_len, int32_t S,
                               int32_t Hq, int32_t Hkv, int32_t D, int32_t B, float scale,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              const CascadeGroups& cg = CascadeGroups()) {
   g_last_error[0] = 0;
+  const bool cascade = cg.on;
   PKV_REQUIRE(S >= 0 && Hq > 0 && Hkv > 0 && D > 0 && B > 0, PKV_ERR_INVALID_ARG,
               "decode: S=%d Hq=%d Hkv=%d D=%d B=%d", S, Hq, Hkv, D, B);
   PKV_REQUIRE(Hq % Hkv == 0, PKV_ERR_INVALID_ARG, "decode: Hq (%d) not a multiple of Hkv (%d)",
@@ -155,16 +165,28 @@ static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv
   PKV_REQUIRE((int64_t)B * Hkv * D * dt_bytes(fp8 ? (int)DT_FP8 : (int)kv_dtype) < ((int64_t)1 << 31),
               PKV_ERR_UNSUPPORTED,
               "decode: one block of one pool must be smaller than 2 GiB");
+  if (cascade) {
+    PKV_REQUIRE(!fp8, PKV_ERR_UNSUPPORTED, "decode_cascade: FP8 pools not supported");
+    PKV_REQUIRE(cg.n_groups >= (S > 0 ? 1 : 0) && cg.n_groups <= S && cg.max_group_size >= 1 &&
+                    cg.max_group_size <= S + (S == 0),
+                PKV_ERR_INVALID_ARG, "decode_cascade: n_groups=%d max_group_size=%d for S=%d",
+                cg.n_groups, cg.max_group_size, S);
+    PKV_REQUIRE(cg.max_prefix_len >= 0, PKV_ERR_INVALID_ARG,
+                "decode_cascade: negative max_prefix_len %d", cg.max_prefix_len);
+  }
   if (S == 0) return PKV_OK;
   PKV_REQUIRE(out && q && k_cache && v_cache && block_tables && context_lens, PKV_ERR_INVALID_ARG,
               "decode: null pointer");
   PKV_REQUIRE(!fp8 || (k_scale && v_scale), PKV_ERR_INVALID_ARG, "decode_fp8: null scale array");
+  PKV_REQUIRE(!cascade || (cg.cu && cg.prefix_lens), PKV_ERR_INVALID_ARG,
+              "decode_cascade: null pointer");
   DecodePlan plan;
   const pkv_status pst = plan_decode(S, Hq, Hkv, D, B, max_context_len, &plan);
   if (pst != PKV_OK) return pst;
-  PKV_REQUIRE(workspace_bytes >= plan.workspace_bytes && (plan.workspace_bytes == 0 || workspace),
-              PKV_ERR_WORKSPACE, "decode: workspace of %zu bytes needed, %zu given",
-              plan.workspace_bytes, workspace_bytes);
+  if (!cascade)
+    PKV_REQUIRE(workspace_bytes >= plan.workspace_bytes && (plan.workspace_bytes == 0 || workspace),
+                PKV_ERR_WORKSPACE, "decode: workspace of %zu bytes needed, %zu given",
+                plan.workspace_bytes, workspace_bytes);
   DecodeArgs a;
   a.out = out;
   a.q = q;
@@ -192,6 +214,12 @@ static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv
   a.scale_log2 = scale * 1.4426950408889634f;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.seq_start = nullptr;
+  a.lse = nullptr;
+  if (cascade)
+    return launch_decode_cascade(kv_dtype, a, cg.cu, cg.prefix_lens, cg.n_groups,
+                                 cg.max_group_size, cg.max_prefix_len, workspace, workspace_bytes,
+                                 static_cast<hipStream_t>(stream));
   return launch_decode(kv_dtype, fp8, plan, a, static_cast<hipStream_t>(stream));
 }
 
@@ -207,6 +235,45 @@ pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void
   return decode_impl(out, out_dtype, q, kv_dtype, false, k_cache, v_cache, nullptr, nullptr,
                      block_tables, max_blocks_per_seq, context_lens, max_context_len, S, Hq, Hkv,
                      D, B, scale, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_decode_cascade_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                                             int32_t B, int32_t max_context_len, int32_t n_groups,
+                                             int32_t max_group_size, int32_t max_prefix_len,
+                                             pkv_dtype kv_dtype, size_t* bytes) {
+  g_last_error[0] = 0;
+  PKV_REQUIRE(bytes, PKV_ERR_INVALID_ARG, "decode_cascade_workspace_size: null output");
+  PKV_REQUIRE(S >= 0 && Hq > 0 && Hkv > 0 && D > 0 && B > 0 && max_context_len >= 0 &&
+                  n_groups >= 0 && max_group_size >= 1 && max_prefix_len >= 0,
+              PKV_ERR_INVALID_ARG, "decode_cascade_workspace_size: bad sizes");
+  PKV_REQUIRE(Hq % Hkv == 0, PKV_ERR_INVALID_ARG, "decode_cascade_workspace_size: Hq %% Hkv != 0");
+  PKV_REQUIRE(supported_dtype(kv_dtype), PKV_ERR_UNSUPPORTED,
+              "decode_cascade_workspace_size: dtype %d", (int)kv_dtype);
+  if (S == 0) {
+    *bytes = 0;
+    return PKV_OK;
+  }
+  return cascade_workspace_size(S, Hq, Hkv, D, B, max_context_len, n_groups, max_group_size,
+                                max_prefix_len, kv_dtype, bytes);
+}
+
+pkv_status pkv_paged_attention_decode_cascade(
+    void* out, pkv_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,
+    pkv_dtype kv_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t max_context_len, int32_t S, int32_t Hq, int32_t Hkv,
+    int32_t D, int32_t B, float scale, const int32_t* cu_group_seqs,
+    const int32_t* group_prefix_lens, int32_t n_groups, int32_t max_group_size,
+    int32_t max_prefix_len, void* workspace, size_t workspace_bytes, void* stream) {
+  CascadeGroups cg;
+  cg.on = true;
+  cg.cu = cu_group_seqs;
+  cg.prefix_lens = group_prefix_lens;
+  cg.n_groups = n_groups;
+  cg.max_group_size = max_group_size;
+  cg.max_prefix_len = max_prefix_len;
+  return decode_impl(out, out_dtype, q, kv_dtype, false, k_cache, v_cache, nullptr, nullptr,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, S, Hq, Hkv,
+                     D, B, scale, workspace, workspace_bytes, stream, cg);
 }
 
 pkv_status pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype, const void* q,

@@ -283,7 +283,8 @@ struct Cursor {
   int rho;  // row of the sequence: kv head * n_hchunks + head chunk
   int j;    // tile within the row
   int nt;   // tiles per row of this sequence
-  int L;    // context length of the sequence
+  int st;   // first token attended (0 unless a start per sequence is given)
+  int L;    // context length of the sequence (one past the last token attended)
   int kvh;  // KV head of the row
   int h0;   // first query head of the row
   float zs; // FP8 pools: score scale of the row (softmax scale * log2 e * K scale)
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
   constexpr int NBUF = (MF || GC <= 2) ? 3 : 2;
 
   __shared__ int sm_ps[kMaxSeqPerLaunch + 1];  // prefix of tile counts over sequences
-  __shared__ int sm_len[kMaxSeqPerLaunch];     // clamped context lengths
+  __shared__ int sm_len[kMaxSeqPerLaunch];     // tokens to attend per sequence
   __shared__ int sm_wsum[kWaves];
 
   const int tid = threadIdx.x;
@@ -331,8 +332,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
     int local = 0;
     for (int i = b; i < e; ++i) {
       const int L = min(max(a.context_lens[i], 0), a.max_ctx);
-      const int c = ((L + TILE - 1) / TILE) * R;
-      sm_len[i] = L;
+      // tokens start .. L - 1 (start = 0 unless a start per sequence is given)
+      const int n = a.seq_start ? max(L - a.seq_start[i], 0) : L;
+      const int c = ((n + TILE - 1) / TILE) * R;
+      sm_len[i] = n;
       sm_ps[i + 1] = c;
       local += c;
     }
@@ -391,8 +394,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
     }
   };
   auto set_seq = [&](Cursor& c) __attribute__((always_inline)) {
-    c.L = rfl(sm_len[c.s]);
-    c.nt = (c.L + TILE - 1) / TILE;
+    const int n = rfl(sm_len[c.s]);
+    c.st = a.seq_start ? ((cint32_t*)a.seq_start)[c.s] : 0;  // scalar load, uniform
+    c.L = c.st + n;
+    c.nt = (n + TILE - 1) / TILE;
   };
   auto advance = [&](Cursor c) __attribute__((always_inline)) -> Cursor {
     if (++c.j == c.nt) {
@@ -434,12 +439,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
     Ent r;
     if constexpr (MF) {
       const cint32_t* tb = (const cint32_t*)(a.block_tables + (int64_t)c.s * a.max_nb);
-      r.e[0] = tb[(c.j * TILE) >> log2B];
+      r.e[0] = tb[(c.st + c.j * TILE) >> log2B];
 #pragma unroll
       for (int i = 1; i < NLD; ++i) r.e[i] = r.e[0];
     } else if constexpr (UNI) {
       const cint32_t* tb = (const cint32_t*)(a.block_tables + (int64_t)c.s * a.max_nb);
-      const int ts = c.j * TILE;
+      const int ts = c.st + c.j * TILE;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) r.e[i] = tb[min(ts + i * RPW, c.L - 1) >> log2B];
     } else {
@@ -455,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
     else return ld16_stream(p);
   };
   auto issue = [&](const Cursor& c, const Ent& en, KVT (&kb)[NLD], KVT (&vb)[NLD]) __attribute__((always_inline)) {
-    const int ts = c.j * TILE;
+    const int ts = c.st + c.j * TILE;
     const int head_off = c.kvh * D * KS + col * LB;
     if constexpr (MF) {
       // the whole tile lies in one block.  K as the MFMA A operand: lane l
@@ -555,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
   auto compute = [&](const Cursor& c, const uint4 (&qv)[QN], const KVT (&kb)[NLD],
                      const KVT (&vb)[NLD], auto full_tag) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
-    const int ts = c.j * TILE;
+    const int ts = c.st + c.j * TILE;
     float zsc;
     if constexpr (F8) zsc = c.zs;
     else zsc = c_scale;
@@ -749,6 +754,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
     }
     const bool complete = row_xb >= x0 && row_xb + c.nt <= x1;
     if (complete && a.out_dt == DT_F32) {
+      if (a.lse && row == 0) {  // log2-sum-exp of the scaled scores, per head
+        if constexpr (MF) {
+          if (col < GC) a.lse[(int64_t)c.s * a.Hq + c.h0 + col] = m[0] + __log2f(l[0]);
+        } else if (col == 0) {
+#pragma unroll
+          for (int g = 0; g < GC; ++g) a.lse[(int64_t)c.s * a.Hq + c.h0 + g] = m[g] + __log2f(l[g]);
+        }
+      }
       if (row == 0) {
 #pragma unroll
         for (int g = 0; g < GC; ++g) {
@@ -797,7 +810,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
   // switch the next row's q is loaded (and waited for): once per row.
   auto finish = [&](int x, const Cursor& cc, const Cursor& cn, const KVT (&kbc)[NLD],
                     const KVT (&vbc)[NLD], uint4 (&qv)[QN], bool last) __attribute__((always_inline)) {
-    if (!MF && (cc.j + 1) * TILE <= cc.L) compute(cc, qv, kbc, vbc, TrueT{});
+    if (!MF && cc.st + (cc.j + 1) * TILE <= cc.L) compute(cc, qv, kbc, vbc, TrueT{});
     else compute(cc, qv, kbc, vbc, FalseT{});  // (the matrix-core path always masks: 8 selects)
     if (last || cn.j == 0) {
       epilogue(cc, row_xb);
@@ -879,6 +892,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
   const int64_t obase = ((int64_t)s * a.Hq + h0) * D;
   if (nt == 0) {  // empty context: defined as an all-zero output row
     for (int j = threadIdx.x; j < GC * D; j += kMergeThreads) store_out(a.out, a.out_dt, obase + j, 0.f);
+    if (a.lse)
+      for (int g = threadIdx.x; g < GC; g += kMergeThreads)
+        a.lse[(int64_t)s * a.Hq + h0 + g] = -__builtin_inff();
     return;
   }
   const int NW = a.n_waves;
@@ -939,6 +955,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
   for (int k = 0; k < NPT; ++k) {
     const int j = threadIdx.x + k * kMergeThreads;
     if (j < GC * D) store_out(a.out, a.out_dt, obase + j, num[k] / den[k]);
+    if (a.lse && j < GC * D && j % D == 0)
+      a.lse[(int64_t)s * a.Hq + h0 + j / D] = M[k] + __log2f(den[k]);
   }
 }
 
@@ -1089,6 +1107,8 @@ pkv_status launch_decode(int kv_dt, bool fp8, const DecodePlan& plan, DecodeArgs
     b.out = static_cast<char*>(a.out) + (int64_t)s0 * a.Hq * a.D * oes;
     b.block_tables = a.block_tables + (int64_t)s0 * a.max_nb;
     b.context_lens = a.context_lens + s0;
+    if (a.seq_start) b.seq_start = a.seq_start + s0;
+    if (a.lse) b.lse = a.lse + (int64_t)s0 * a.Hq;
     // no more waves than the batch could ever use, nor than the workspace
     // has slots for (the launch also caps at one resident wave set)
     const int64_t max_tiles = (int64_t)b.S * a.rows_per_seq * nt_max;

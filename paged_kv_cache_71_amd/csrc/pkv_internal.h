@@ -118,10 +118,24 @@ struct DecodeArgs {
   float scale_log2;      // softmax scale * log2(e)
   const float* k_scale;  // FP8 pools: per-KV-head scales (device, [Hkv]); else unused
   const float* v_scale;
+  // optional (null = off): first token attended per sequence (device [S],
+  // 0 <= start <= context length; a multiple of B), and a log2-sum-exp output
+  // per (sequence, head) (device [S, Hq]; -inf for an empty range)
+  const int32_t* seq_start;
+  float* lse;
 };
 // q_dt: dtype of q (and of the pools unless fp8); fp8: the pools hold E4M3 codes
 pkv_status launch_decode(int q_dt, bool fp8, const DecodePlan& plan, DecodeArgs a,
                          hipStream_t stream);
+
+// Cascade decode (cascade.hip): groups of sequences sharing a prefix.
+pkv_status cascade_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                  int32_t max_context_len, int32_t n_groups, int32_t max_group_size,
+                                  int32_t max_prefix_len, int kv_dt, size_t* bytes);
+pkv_status launch_decode_cascade(int kv_dt, const DecodeArgs& base, const int32_t* cu_group_seqs,
+                                 const int32_t* group_prefix_lens, int32_t n_groups,
+                                 int32_t max_group_size, int32_t max_prefix_len, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 struct PrefillArgs {
   void* out;

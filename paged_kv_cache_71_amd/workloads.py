@@ -389,6 +389,55 @@ def shared_prefix_bf16(seed: int = 0, prompts: int = 64, n: int = 4, prompt_len:
     return batch
 
 
+def grouped_batch(seed: int, group_sizes, prefix_blocks, suffix_lens, Hq: int, Hkv: int, D: int,
+                  B: int, dtype: str, NB: int | None = None, name: str = "grouped") -> PagedBatch:
+    """Decode batch whose sequences come in consecutive groups: group g has
+    ``group_sizes[g]`` members that all alias its ``prefix_blocks[g]`` full
+    blocks, then hold private blocks for their ``suffix_lens`` tokens (one
+    entry per sequence, 0 allowed).  ``meta`` records ``cu_group_seqs`` and
+    ``group_prefix_lens`` (tokens)."""
+    rng = np.random.default_rng(seed)
+    group_sizes = [int(x) for x in group_sizes]
+    prefix_blocks = [int(x) for x in prefix_blocks]
+    suffix_lens = np.asarray(suffix_lens, np.int64)
+    S = sum(group_sizes)
+    assert len(prefix_blocks) == len(group_sizes) and suffix_lens.shape == (S,)
+    lengths = np.zeros(S, np.int32)
+    s = 0
+    for g, n in enumerate(group_sizes):
+        lengths[s:s + n] = prefix_blocks[g] * B + suffix_lens[s:s + n]
+        s += n
+    need = sum(prefix_blocks) + int(sum(-(-int(x) // B) for x in suffix_lens))
+    NB = max(64, 2 * need) if NB is None else NB
+    free_order = rng.permutation(NB)
+    pos, seq_blocks, block_fill = 0, [], {}
+
+    def take(c):
+        nonlocal pos
+        r = free_order[pos:pos + c].astype(np.int64)
+        pos += c
+        return r
+
+    s = 0
+    for g, n in enumerate(group_sizes):
+        prefix = take(prefix_blocks[g])
+        for b in prefix:
+            block_fill[int(b)] = B
+        for _ in range(n):
+            suf = int(suffix_lens[s])
+            extra = take(-(-suf // B))
+            for k, b in enumerate(extra):
+                block_fill[int(b)] = min(B, suf - k * B)
+            seq_blocks.append(np.concatenate([prefix, extra]).astype(np.int64))
+            s += 1
+    cu = np.zeros(len(group_sizes) + 1, np.int32)
+    cu[1:] = np.cumsum(group_sizes)
+    return _build(name, rng, lengths, Hq, Hkv, D, B, NB, dtype, q_rows=S, seq_blocks=seq_blocks,
+                  block_fill=block_fill,
+                  meta={"cu_group_seqs": cu,
+                        "group_prefix_lens": np.array(prefix_blocks, np.int32) * B})
+
+
 def prefill_bf16(seed: int = 0, S: int = 8, chunk: int = 512, prior_lo: int = 4096,
                  prior_hi: int = 32768, Hq: int = 32, Hkv: int = 8, D: int = 128, B: int = 16,
                  NB: int | None = None) -> PagedBatch:
