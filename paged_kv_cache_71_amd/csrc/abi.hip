@@ -205,9 +205,7 @@ static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv
   a.D = D;
   a.B = B;
   a.log2B = ilog2(B);
-  a.gc = plan.gc;
-  a.n_hchunks = plan.n_hchunks;
-  a.rows_per_seq = plan.rows_per_seq;
+  a.gc = a.n_hchunks = a.rows_per_seq = 0;  // chosen per path by launch_decode
   a.n_waves = 0;  // set per launch
   a.max_ctx = max_context_len;
   a.out_dt = out_dtype;

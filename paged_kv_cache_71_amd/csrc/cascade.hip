@@ -206,9 +206,6 @@ pkv_status launch_decode_cascade(int kv_dt, const DecodeArgs& base, const int32_
   p.S = n_groups;
   p.Hq = NM * base.Hq;
   p.max_ctx = L.max_prefix_len;
-  p.gc = L.plan_p.gc;
-  p.n_hchunks = L.plan_p.n_hchunks;
-  p.rows_per_seq = L.plan_p.rows_per_seq;
   p.ws_ps = reinterpret_cast<int32_t*>(ws + L.ws_p + L.plan_p.ws_ps_off);
   p.ws_ml = reinterpret_cast<float*>(ws + L.ws_p + L.plan_p.ws_ml_off);
   p.ws_acc = reinterpret_cast<float*>(ws + L.ws_p + L.plan_p.ws_acc_off);
@@ -223,9 +220,6 @@ pkv_status launch_decode_cascade(int kv_dt, const DecodeArgs& base, const int32_
   DecodeArgs sf = base;
   sf.out = o_s;
   sf.out_dt = DT_F32;
-  sf.gc = L.plan_s.gc;
-  sf.n_hchunks = L.plan_s.n_hchunks;
-  sf.rows_per_seq = L.plan_s.rows_per_seq;
   sf.ws_ps = reinterpret_cast<int32_t*>(ws + L.ws_s + L.plan_s.ws_ps_off);
   sf.ws_ml = reinterpret_cast<float*>(ws + L.ws_s + L.plan_s.ws_ml_off);
   sf.ws_acc = reinterpret_cast<float*>(ws + L.ws_s + L.plan_s.ws_acc_off);

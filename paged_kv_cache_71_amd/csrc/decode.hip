@@ -231,14 +231,52 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4 a, const uint4 b, f32x4_t 
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// Value of lane g of this lane's quad (DPP quad_perm [g, g, g, g]).
-__device__ __forceinline__ float quad_bcast(float x, int g) {
-  switch (g) {
-    case 0: return dpp<0x00>(x);
-    case 1: return dpp<0x55>(x);
-    case 2: return dpp<0xAA>(x);
-    default: return dpp<0xFF>(x);
-  }
+// C += A B on the matrix cores, 16 x 16 x 16 with 16-bit operands: lane l
+// holds A[l % 16][4 (l / 16) + 0..3], B[4 (l / 16) + 0..3][l % 16] and
+// receives C[4 (l / 16) + i][l % 16], i < 4.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma16k16(const uint2 a, const uint2 b, f32x4_t c) {
+  if constexpr (DT == DT_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                     __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+}
+
+// gfx950 transposed LDS read of 16-bit elements: within each 16-lane group,
+// lane j addresses 4 consecutive elements; lane i receives element i % 4 of
+// lanes 4k + i / 4 (k < 4).  Pointing lane j at row r0 + j / 4, column
+// c0 + 4 (j % 4) of a row-major tile gives lane i the column c0 + i of rows
+// r0 .. r0 + 3.
+typedef short i16x4lds_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
+  const i16x4lds_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4lds_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Two fp32 values -> one word of two 16-bit values of dtype DT (x low),
+// round to nearest even; and the two halves of such a word back to fp32.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  if constexpr (DT == DT_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{x, y}), bf16x2_t));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{x, y}), f16x2_t));
+}
+template <int DT>
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  if constexpr (DT == DT_BF16) return __uint_as_float(w << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)w);
+}
+template <int DT>
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  if constexpr (DT == DT_BF16) return __uint_as_float(w & 0xffff0000u);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
 __device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -306,8 +344,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
   constexpr int KS = F8 ? 1 : ES;   // bytes per cached element
   constexpr int LB = 16 * KS / ES;  // bytes of K or V per lane per load
   using KVT = std::conditional_t<F8, uint2, uint4>;
-  static_assert(!MF || (DT != DT_F32 && D == 128 && GC == 4 && UNI && TILE == 16),
-                "matrix-core path: 16-bit KV, D = 128, GQA group of 4, one block per tile");
+  static_assert(!MF || (DT != DT_F32 && D == 128 && (GC == 4 || GC == 8 || GC == 16) && UNI &&
+                        TILE == 16),
+                "matrix-core path: 16-bit q, D = 128, 4, 8 or 16 query heads, one block per tile");
   constexpr int QN = MF ? D / 32 : GC;  // q registers: k-steps of 32 (MF) or heads
   // tiles in flight per wave: three where the registers allow it
   constexpr int NBUF = (MF || GC <= 2) ? 3 : 2;
@@ -536,16 +575,33 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
 
   // online-softmax state of this lane's token row (m: running max of the
   // scaled scores, log2 units)
-  float m[GC], l[GC], acc[GC][EPL];
+  // Matrix-core path: one query column per lane (col % GC), m and l of that
+  // column, and oacc[db][i] = output element 16 db + 4 row + i of the column.
+  constexpr int NS = MF ? 1 : GC;
+  float m[NS], l[NS], acc[MF ? 1 : GC][EPL];
+  f32x4_t oacc[MF ? D / 16 : 1];
   auto reset_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int g = 0; g < GC; ++g) {
+    for (int g = 0; g < NS; ++g) {
       m[g] = -__builtin_inff();
       l[g] = 0.f;
+    }
+    if constexpr (MF) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+      for (int db = 0; db < D / 16; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    } else {
+#pragma unroll
+      for (int g = 0; g < GC; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
     }
   };
+  // Matrix-core path: this wave's rows of LDS, the V tile (16 tokens x D,
+  // 16-bit) staged for transposed reads; rows padded by 32 bytes so the four
+  // rows one read touches fall on distinct banks.
+  constexpr int kVP = D * 2 + 32;
+  __shared__ __attribute__((aligned(16))) char sm_v[MF ? kWaves * 16 * kVP : 16];
+  char* const vs = sm_v + (MF ? wave * 16 * kVP : 0);
 
   // One tile.  FULL: every row of the tile is a valid token.
   // K as 16-bit elements and V as fp32 (FP8 codes widened exactly)
@@ -566,9 +622,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
     else zsc = c_scale;
     if constexpr (MF) {
       // S = K q^T on the matrix cores: lane (row, col) receives the scores of
-      // tokens 4 * row + i (i < 4) for head col % GC.  The running max m[0] of
-      // that head is shared by all lanes (max over the 16 tokens of the tile,
-      // across lane rows); l[0] is this lane's partial sum over its 4 tokens.
+      // tokens 4 * row + i (i < 4) for query column col (head h0 + col % GC).
+      // The running max m[0] of the column is shared by its four lanes (max
+      // over the 16 tokens of the tile, across lane rows); l[0] is this lane's
+      // partial sum over its 4 tokens.
       f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NLD; ++kk) sacc = mfma16<DT>(kfrag(kb[kk]), qv[kk], sacc);
@@ -587,14 +644,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
       t = fmaxf(lo, hi);
       const float mn = fmaxf(m[0], t);  // finite: a tile holds at least one valid token
       if (__builtin_amdgcn_ballot_w64(mn > m[0])) {
-        const float alpha = fast_exp2(m[0] - mn);
+        const float alpha = fast_exp2(m[0] - mn);  // this lane's own column
         l[0] *= alpha;
 #pragma unroll
-        for (int g = 0; g < GC; ++g) {
-          const float ag = quad_bcast(alpha, g);
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[g][e] *= ag;
-        }
+        for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
         m[0] = mn;
       }
       float p[4];
@@ -605,16 +658,24 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
         else p[i] = (ts + 4 * row + i < c.L) ? pe : 0.f;
       }
       l[0] += (p[0] + p[1]) + (p[2] + p[3]);
+      // O^T += V^T P^T on the matrix cores (16 x 16 x 16 per 16 output
+      // elements): B = P^T is this lane's p (tokens 4 row + j, column col), in
+      // hi + lo 16-bit parts (about 16 significant bits); A = V^T comes from
+      // the tile staged in LDS through transposed reads.
+      const uint32_t h01 = pack2<DT>(p[0], p[1]), h23 = pack2<DT>(p[2], p[3]);
+      const uint2 ph = make_uint2(h01, h23);
+      const uint2 pl = make_uint2(pack2<DT>(p[0] - half_lo<DT>(h01), p[1] - half_hi<DT>(h01)),
+                                  pack2<DT>(p[2] - half_lo<DT>(h23), p[3] - half_hi<DT>(h23)));
+      // (the wave's own LDS rows, written and read in order by this wave only)
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        float vf[EPL];
-        vwiden(vb[i], vf);
+      for (int i = 0; i < NLD; ++i)
+        *reinterpret_cast<uint4*>(vs + (4 * row + i) * kVP + col * 16) = kfrag(vb[i]);
+      const char* vrd = vs + (4 * row + (col >> 2)) * kVP + (col & 3) * 8;
 #pragma unroll
-        for (int g = 0; g < GC; ++g) {
-          const float pg = quad_bcast(p[i], g);
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pg, vf[e], acc[g][e]);
-        }
+      for (int db = 0; db < D / 16; ++db) {
+        const uint2 va = lds_read_tr16(vrd + db * 32);
+        oacc[db] = mfma16k16<DT>(va, ph, oacc[db]);
+        oacc[db] = mfma16k16<DT>(va, pl, oacc[db]);
       }
       return;
     }
@@ -694,22 +755,40 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
   // x0, slot 2w+1: the row holding x1 - 1)
   auto epilogue = [&](const Cursor& c, int row_xb) __attribute__((always_inline)) {
     if constexpr (MF) {
-      // all lanes share the running max: the lane rows' partial sums add up
-#pragma unroll
-      for (int g = 0; g < GC; ++g) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          float lo, hi;
-          pair_halves<16>(acc[g][e], lo, hi);
-          pair_halves<32>(lo + hi, lo, hi);
-          acc[g][e] = lo + hi;
-        }
-      }
+      // the four lanes of a column share its running max: their partial sums
+      // add up; the matrix cores already summed the accumulators over tokens
       float lo, hi;
       pair_halves<16>(l[0], lo, hi);
       pair_halves<32>(lo + hi, lo, hi);
-      l[0] = lo + hi;  // total weight of head col % GC
-    } else if constexpr (LPR == 8) {
+      l[0] = lo + hi;  // total weight of column col
+      const bool complete = row_xb >= x0 && row_xb + c.nt <= x1;
+      if constexpr (F8) {
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) oacc[db] *= c.vs;
+      }
+      if (col < GC) {  // one of the identical copies of each query column
+        if (complete && a.out_dt == DT_F32) {
+          const int64_t o = ((int64_t)c.s * a.Hq + c.h0 + col) * D + 4 * row;
+          if (a.lse && row == 0) a.lse[(int64_t)c.s * a.Hq + c.h0 + col] = m[0] + __log2f(l[0]);
+#pragma unroll
+          for (int db = 0; db < D / 16; ++db)
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o + 16 * db) =
+                make_float4(oacc[db][0] / l[0], oacc[db][1] / l[0], oacc[db][2] / l[0],
+                            oacc[db][3] / l[0]);
+        } else {
+          const int slot = complete ? 2 * NW + c.s * R + c.rho : (row_xb <= x0 ? 2 * w : 2 * w + 1);
+          const int64_t o = ((int64_t)slot * GC + col) * D + 4 * row;
+#pragma unroll
+          for (int db = 0; db < D / 16; ++db)
+            *reinterpret_cast<float4*>(a.ws_acc + o + 16 * db) =
+                make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
+          if (row == 0)
+            *reinterpret_cast<float2*>(a.ws_ml + ((int64_t)slot * GC + col) * 2) = make_float2(m[0], l[0]);
+        }
+      }
+      reset_state();
+    } else {
+    if constexpr (LPR == 8) {
 #pragma unroll
       for (int g = 0; g < GC; ++g) {
         float accb[EPL];
@@ -720,7 +799,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
         merge_pair(m[g], l[g], acc[g], cmb, lb, accb, m[g], l[g], acc[g]);
       }
     }
-    if constexpr (!MF && LPR <= 16) {
+    if constexpr (LPR <= 16) {
 #pragma unroll
       for (int g = 0; g < GC; ++g) {
         float a0[EPL], a1[EPL], c0v, c1v, l0, l1;
@@ -731,7 +810,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
         merge_pair(c0v, l0, a0, c1v, l1, a1, m[g], l[g], acc[g]);
       }
     }
-    if constexpr (!MF) {
+    {
 #pragma unroll
       for (int g = 0; g < GC; ++g) {
         float a0[EPL], a1[EPL], c0v, c1v, l0, l1;
@@ -754,20 +833,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
     }
     const bool complete = row_xb >= x0 && row_xb + c.nt <= x1;
     if (complete && a.out_dt == DT_F32) {
-      if (a.lse && row == 0) {  // log2-sum-exp of the scaled scores, per head
-        if constexpr (MF) {
-          if (col < GC) a.lse[(int64_t)c.s * a.Hq + c.h0 + col] = m[0] + __log2f(l[0]);
-        } else if (col == 0) {
+      if (a.lse && row == 0 && col == 0) {  // log2-sum-exp of the scaled scores, per head
 #pragma unroll
-          for (int g = 0; g < GC; ++g) a.lse[(int64_t)c.s * a.Hq + c.h0 + g] = m[g] + __log2f(l[g]);
-        }
+        for (int g = 0; g < GC; ++g) a.lse[(int64_t)c.s * a.Hq + c.h0 + g] = m[g] + __log2f(l[g]);
       }
       if (row == 0) {
 #pragma unroll
         for (int g = 0; g < GC; ++g) {
-          float lg;
-          if constexpr (MF) lg = GC == 1 ? l[0] : quad_bcast(l[0], g);
-          else lg = l[g];
+          const float lg = l[g];
           float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.out) +
                                                   ((int64_t)c.s * a.Hq + c.h0 + g) * D + col * EPL);
 #pragma unroll
@@ -786,10 +859,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
           for (int e = 0; e < EPL / 4; ++e)
             dst[e] = make_float4(acc[g][4 * e], acc[g][4 * e + 1], acc[g][4 * e + 2], acc[g][4 * e + 3]);
         }
-        if constexpr (MF) {
-          if (col < GC)  // lane col holds head col
-            *reinterpret_cast<float2*>(a.ws_ml + ((int64_t)slot * GC + col) * 2) = make_float2(m[0], l[0]);
-        } else if (col == 0) {
+        if (col == 0) {
 #pragma unroll
           for (int g = 0; g < GC; ++g)
             *reinterpret_cast<float2*>(a.ws_ml + ((int64_t)slot * GC + g) * 2) = make_float2(m[g], l[g]);
@@ -797,6 +867,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
       }
     }
     reset_state();
+    }
   };
 
   using TrueT = BoolTag<true>;
@@ -1010,12 +1081,16 @@ pkv_status launch_split(DecodeArgs a, int grid_cap, int ncu, hipStream_t stream)
 
 template <int DT, int D, int GC, bool F8>
 pkv_status launch_typed(const DecodeArgs& a, int grid_cap, int ncu, bool uni, hipStream_t stream) {
-  // matrix cores for q . k: 16-bit q, D = 128, GQA groups of 4, a tile in one block
-  if constexpr (DT != DT_F32 && D == 128 && GC == 4) {
+  // matrix cores: 16-bit q, D = 128, 4, 8 or 16 query heads per row, a tile in one block
+  if constexpr (DT != DT_F32 && D == 128 && (GC == 4 || GC == 8 || GC == 16)) {
     if (a.B >= 16) return launch_split<DT, D, GC, true, true, F8>(a, grid_cap, ncu, stream);
   }
-  if (uni) return launch_split<DT, D, GC, true, false, F8>(a, grid_cap, ncu, stream);
-  return launch_split<DT, D, GC, false, false, F8>(a, grid_cap, ncu, stream);
+  if constexpr (GC == 16) {  // chunks of 16 heads exist on the matrix-core path only
+    return fail(PKV_ERR_UNSUPPORTED, "decode: 16-head rows need the matrix-core path");
+  } else {
+    if (uni) return launch_split<DT, D, GC, true, false, F8>(a, grid_cap, ncu, stream);
+    return launch_split<DT, D, GC, false, false, F8>(a, grid_cap, ncu, stream);
+  }
 }
 
 template <int DT, int D, bool F8>
@@ -1025,6 +1100,7 @@ pkv_status launch_gc(const DecodeArgs& a, int grid_cap, int ncu, bool uni, hipSt
     case 2: return launch_typed<DT, D, 2, F8>(a, grid_cap, ncu, uni, stream);
     case 4: return launch_typed<DT, D, 4, F8>(a, grid_cap, ncu, uni, stream);
     case 8: return launch_typed<DT, D, 8, F8>(a, grid_cap, ncu, uni, stream);
+    case 16: return launch_typed<DT, D, 16, F8>(a, grid_cap, ncu, uni, stream);
   }
   return fail(PKV_ERR_UNSUPPORTED, "decode: head chunk %d", a.gc);
 }
@@ -1052,20 +1128,30 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 pkv_status plan_decode(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t /*B*/,
                        int32_t max_context_len, DecodePlan* plan) {
   const int G = Hq / Hkv;
-  int gc = 1;
+  // query heads per row: the vector path takes the largest of 8, 4, 2 dividing
+  // G (else 1); the matrix-core path the largest of 16, 8, 4 (else none)
+  int gv = 1, gm = 0;
   for (int c : {8, 4, 2}) {
     if (G % c == 0) {
-      gc = c;
+      gv = c;
       break;
     }
   }
-  plan->gc = gc;
-  plan->n_hchunks = G / gc;
-  plan->rows_per_seq = Hkv * plan->n_hchunks;
+  for (int c : {16, 8, 4}) {
+    if (G % c == 0) {
+      gm = c;
+      break;
+    }
+  }
+  plan->gc_vec = gv;
+  plan->gc_mf = gm;
+  const int gc_min = gm > 0 && gm < gv ? gm : gv;
+  const int gc_max = gm > gv ? gm : gv;
+  const int64_t rows_max = (int64_t)Hkv * (G / gc_min);
   // Tiles of a row with the smallest tile of any dtype (8 tokens): an upper
   // bound of the flat tile count, so the plan depends on the arguments only.
   const int64_t nt_max = ((int64_t)max_context_len + 7) / 8;
-  const int64_t per_seq = nt_max * plan->rows_per_seq;
+  const int64_t per_seq = nt_max * rows_max;
   // Sequences per launch: the LDS prefix capacity, and the flat tile count plus
   // the wave count must stay below 2^31.
   const int64_t limit = (int64_t)0x7fffffff - (int64_t)kMaxGrid * kWaves;
@@ -1081,17 +1167,22 @@ pkv_status plan_decode(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t /*
   if (grid > kMaxGrid) grid = kMaxGrid;
   if (grid < 1) grid = 1;
   plan->max_waves = (int)grid * kWaves;
-  const size_t slots = (size_t)plan->max_waves * 2 + (size_t)sc * plan->rows_per_seq;
+  // states: two slots per wave and one per row, gc heads each (whichever path runs)
+  const size_t states = (size_t)plan->max_waves * 2 * gc_max + (size_t)sc * Hkv * G;
   plan->ws_ps_off = 0;
   plan->ws_ml_off = align_up(((size_t)sc + 1) * sizeof(int32_t));
-  plan->ws_acc_off = plan->ws_ml_off + align_up(slots * gc * 2 * sizeof(float));
-  plan->workspace_bytes = plan->ws_acc_off + slots * gc * (size_t)D * sizeof(float);
+  plan->ws_acc_off = plan->ws_ml_off + align_up(states * 2 * sizeof(float));
+  plan->workspace_bytes = plan->ws_acc_off + states * (size_t)D * sizeof(float);
   return PKV_OK;
 }
 
 pkv_status launch_decode(int kv_dt, bool fp8, const DecodePlan& plan, DecodeArgs a,
                          hipStream_t stream) {
   // (kv_dt: the dtype of q; the lane layout follows it, also over FP8 pools)
+  const bool mf = kv_dt != DT_F32 && a.D == 128 && a.B >= 16 && plan.gc_mf > 0;
+  a.gc = mf ? plan.gc_mf : plan.gc_vec;
+  a.n_hchunks = (a.Hq / a.Hkv) / a.gc;
+  a.rows_per_seq = a.Hkv * a.n_hchunks;
   int tile = 0, rpw = 0;
   tile_geometry(kv_dt, a.D, &tile, &rpw);
   const bool uni = a.B >= rpw;

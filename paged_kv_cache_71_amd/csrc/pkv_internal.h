@@ -89,9 +89,8 @@ pkv_status launch_copy_blocks(void* const* k_caches, void* const* v_caches, int3
                               hipStream_t stream);
 
 struct DecodePlan {
-  int gc;               // query heads per row (divides G)
-  int n_hchunks;        // G / gc
-  int rows_per_seq;     // Hkv * n_hchunks
+  int gc_vec;           // query heads per row on the vector path (divides G)
+  int gc_mf;            // ... on the matrix-core path (4, 8 or 16 dividing G; 0: none)
   int max_waves;        // waves of the largest split launch (sizes the workspace)
   int seqs_per_launch;  // sequences handled by one split + merge launch pair
   size_t ws_ps_off, ws_ml_off, ws_acc_off;  // workspace layout (bytes)
@@ -112,7 +111,7 @@ struct DecodeArgs {
   float* ws_acc;    // [2 * n_waves, gc, D] partial accumulators
   int32_t max_nb;
   int32_t S, Hq, Hkv, D, B, log2B;
-  int32_t gc, n_hchunks, rows_per_seq, n_waves;
+  int32_t gc, n_hchunks, rows_per_seq, n_waves;  // (set by launch_decode)
   int32_t max_ctx;       // context lengths are clamped to this (<= max_nb * B)
   int32_t out_dt;
   float scale_log2;      // softmax scale * log2(e)
