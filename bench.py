@@ -140,6 +140,46 @@ def main():
         t = np.array([a.elapsed_time(z) for a, z in evs])
         return float(t.mean()), float(np.median(t))
 
+    def mixed_row():
+        """The Llama-3-8B decode batch plus one 512-token prefill chunk (after
+        8192 cached tokens) in one batch: the mixed call (decodes and chunk run
+        concurrently) against the two launched one after the other."""
+        mb = W.llama3_8b_mixed_bf16(args.seed)
+        md = Dev(mb)
+        nd = mb.meta["num_decode"]
+        cu = md.cu
+        maxq = int(np.max(np.diff(mb.cu_seqlens_q)))
+        ws = torch.empty(max(pkv.mixed_workspace_size(mb.S, nd, mb.Hq, mb.Hkv, mb.D, mb.B,
+                                                      mb.max_context_len), 1),
+                         dtype=torch.uint8, device=dev)
+        dws = torch.empty(max(pkv.decode_workspace_size(nd, mb.Hq, mb.Hkv, mb.D, mb.B,
+                                                        mb.max_context_len), 1),
+                          dtype=torch.uint8, device=dev)
+        qd, qp = md.q[:nd], md.q[nd:].contiguous()
+        od, op = md.out[:nd], md.out[nd:]
+        tdec, tpre = md.tables[:nd].contiguous(), md.tables[nd:].contiguous()
+        ldec, lpre = md.lens[:nd].contiguous(), md.lens[nd:].contiguous()
+        cup = (cu[nd:] - nd).contiguous()
+
+        def mixed():
+            pkv.paged_attention_mixed(md.out, md.q, cu, nd, maxq, md.k, md.v, md.tables, md.lens,
+                                      mb.max_context_len, mb.scale, workspace=ws)
+
+        def serial():
+            pkv.paged_attention_decode(od, qd, md.k, md.v, tdec, ldec, mb.max_context_len,
+                                       mb.scale, workspace=dws)
+            pkv.paged_attention_prefill(op, qp, cup, maxq, md.k, md.v, tpre, lpre,
+                                        mb.max_context_len, mb.scale)
+
+        ms_m, _ = time_fn(mixed, 20)
+        ms_s, _ = time_fn(serial, 20)
+        log(f"[bench] mixed: {ms_m * 1e3:.1f} us (serial {ms_s * 1e3:.1f} us)")
+        md.free()
+        del md
+        torch.cuda.empty_cache()
+        return {"ms": round(ms_m, 5), "serial_ms": round(ms_s, 5),
+                "speedup_vs_serial": round(ms_s / ms_m, 3)}
+
     def prefill_row():
         """Chunked causal prefill of 8 sequences x 512 new tokens (bf16)."""
         pb = W.prefill_bf16(args.seed)
@@ -354,6 +394,7 @@ def main():
         torch.cuda.empty_cache()
 
         rows["prefill_bf16_8x512"] = prefill_row()
+        rows["mixed_llama3_8b_256_decodes_512_chunk"] = mixed_row()
         result["rows"] = rows
 
     if not args.headline_only and not args.no_cpu_baseline:

@@ -9,7 +9,9 @@
  *  - Ownership: every pointer is owned by the caller.  Tensor pointers are
  *    DEVICE pointers (hipMalloc'd or torch CUDA tensors on the current device);
  *    the library allocates no device memory and keeps no state beyond a
- *    thread-local error string and the host block managers the caller creates.
+ *    thread-local error string, the host block managers the caller creates,
+ *    and one auxiliary stream with two events per device that the mixed-batch
+ *    call creates on first use.
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  *    stream).  Kernel calls are asynchronous on that stream.
  *  - Errors: scalar arguments are validated on the host before any launch; a
@@ -237,6 +239,43 @@ pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const voi
                                        const int32_t* context_lens, int32_t max_context_len,
                                        int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
                                        float scale, void* stream);
+
+/* ------------------------------------------------------------------------
+ * paged_attention_mixed -- one call for a batch mixing decode requests and
+ * prefill chunks.
+ *
+ * Defined by "LLM inference, part 3: single node", ch. 13 sec. 1 (one
+ * flattened token stream; cu_seqlens separates requests of one token (decode)
+ * and of many (prefill)) and sec. 2 (a chunk of a long prompt is packed with
+ * the running decodes into one batch, so the bandwidth-bound decodes and the
+ * compute-bound chunk use the GPU together).
+ *
+ *   (arguments as for pkv_paged_attention_prefill, over the whole batch)
+ *   num_decode : host; sequences 0 .. num_decode - 1 are decodes with one
+ *                query row each (rows 0 .. num_decode - 1, so
+ *                cu_seqlens_q[i] == i for i <= num_decode); the others are
+ *                prefill chunks
+ *   workspace  : device scratch of pkv_mixed_workspace_size() bytes
+ * Every output row equals what pkv_paged_attention_decode (decode rows) or
+ * pkv_paged_attention_prefill (chunk rows) give for it, bit for bit.  The two
+ * parts run concurrently: the decodes on `stream`, the chunks on a stream the
+ * library creates once per device (default priority) and keeps until the
+ * process ends, forked from and joined back into `stream` with events, so the
+ * call is ordered on `stream` like any other.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_mixed_workspace_size(int32_t S, int32_t num_decode, int32_t Hq, int32_t Hkv,
+                                    int32_t D, int32_t B, int32_t max_context_len,
+                                    size_t* bytes);
+
+pkv_status pkv_paged_attention_mixed(void* out, pkv_dtype out_dtype, const void* q,
+                                     const int32_t* cu_seqlens_q, int32_t Tq, int32_t num_decode,
+                                     int32_t max_query_len, const void* k_cache,
+                                     const void* v_cache, pkv_dtype kv_dtype,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t max_context_len,
+                                     int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                     float scale, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /* ------------------------------------------------------------------------
  * copy_blocks -- batched whole-block copies for copy-on-write.

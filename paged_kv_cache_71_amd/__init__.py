@@ -8,13 +8,14 @@ library and raises if it has not been built.
 """
 from ._binding import (BlockManager, PkvError, PkvOOM, copy_blocks, declared_symbols,
                        decode_cascade_workspace_size, decode_workspace_size, load_library,
-                       paged_attention_decode, paged_attention_decode_cascade,
-                       paged_attention_decode_fp8, paged_attention_prefill, reshape_and_cache,
+                       mixed_workspace_size, paged_attention_decode,
+                       paged_attention_decode_cascade, paged_attention_decode_fp8,
+                       paged_attention_mixed, paged_attention_prefill, reshape_and_cache,
                        reshape_and_cache_fp8)
 
 __all__ = [
     "BlockManager", "PkvError", "PkvOOM", "copy_blocks", "declared_symbols",
     "decode_cascade_workspace_size", "decode_workspace_size", "load_library",
-    "paged_attention_decode_cascade", "paged_attention_decode", "paged_attention_decode_fp8",
+    "mixed_workspace_size", "paged_attention_decode_cascade", "paged_attention_mixed", "paged_attention_decode", "paged_attention_decode_fp8",
     "paged_attention_prefill", "reshape_and_cache", "reshape_and_cache_fp8",
 ]

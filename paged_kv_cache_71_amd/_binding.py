@@ -62,6 +62,9 @@ def load_library(path: str | None = None):
                                              i32, i32, i32, i32, f32, P]),
         "pkv_copy_blocks": (st, [P, P, i32, P, i32, i32, i32, i32, st, P]),
         "pkv_reshape_and_cache_fp8": (st, [P, P, st, P, P, P, i32, i32, i32, i32, i64, P, P, P]),
+        "pkv_mixed_workspace_size": (st, [i32, i32, i32, i32, i32, i32, i32, SZP]),
+        "pkv_paged_attention_mixed": (st, [P, st, P, P, i32, i32, i32, P, P, st, P, i32, P, i32, i32,
+                                           i32, i32, i32, i32, f32, P, sz, P]),
         "pkv_decode_cascade_workspace_size": (st, [i32, i32, i32, i32, i32, i32, i32, i32, i32, st,
                                                    SZP]),
         "pkv_paged_attention_decode_cascade": (st, [P, st, P, P, P, st, P, i32, P, i32, i32, i32,
@@ -219,6 +222,46 @@ def paged_attention_prefill(out, q, cu_seqlens_q, max_query_len: int, k_cache, v
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B,
         float(scale), _stream(stream)), "paged_attention_prefill")
+    return out
+
+
+def mixed_workspace_size(S: int, num_decode: int, Hq: int, Hkv: int, D: int, B: int,
+                         max_context_len: int) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    _check(lib.pkv_mixed_workspace_size(S, num_decode, Hq, Hkv, D, B, max_context_len,
+                                        ctypes.byref(out)), "mixed_workspace_size")
+    return out.value
+
+
+def paged_attention_mixed(out, q, cu_seqlens_q, num_decode: int, max_query_len: int, k_cache,
+                          v_cache, block_tables, context_lens, max_context_len: int, scale: float,
+                          workspace=None, stream=None):
+    """One call for a batch whose first ``num_decode`` sequences are decodes
+    (one query row each) and the rest prefill chunks; decodes and chunks run
+    concurrently.  Same rows as paged_attention_decode / _prefill, bit for bit."""
+    torch = _torch()
+    lib = load_library()
+    Tq, Hq, D = q.shape
+    NB, B, Hkv, D2 = k_cache.shape
+    S = cu_seqlens_q.shape[0] - 1
+    if D2 != D or v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("paged_attention_mixed: shape mismatch")
+    if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("paged_attention_mixed: q/k/v dtype mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("paged_attention_mixed: block_tables [S, max_nb] / context_lens [S]")
+    need = mixed_workspace_size(S, num_decode, Hq, Hkv, D, B, max_context_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.pkv_paged_attention_mixed(
+        _dev(out, "out"), dtype_code(out), _dev(q, "q"),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), Tq, int(num_decode), int(max_query_len),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), dtype_code(k_cache),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B,
+        float(scale), _dev(workspace, "workspace"), workspace.numel(), _stream(stream)),
+        "paged_attention_mixed")
     return out
 
 

@@ -27,7 +27,7 @@ HIP_FLAGS = [
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE]
 
-HIP_SOURCES = ["abi.hip", "cache_ops.hip", "cascade.hip", "decode.hip", "prefill.hip"]
+HIP_SOURCES = ["abi.hip", "cache_ops.hip", "cascade.hip", "decode.hip", "mixed.hip", "prefill.hip"]
 CXX_SOURCES = ["block_manager.cpp"]
 
 

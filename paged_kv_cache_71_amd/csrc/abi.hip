@@ -287,15 +287,17 @@ pkv_status pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype, const 
                      D, B, scale, workspace, workspace_bytes, stream);
 }
 
-pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* q,
-                                       const int32_t* cu_seqlens_q, int32_t Tq,
-                                       int32_t max_query_len, const void* k_cache,
-                                       const void* v_cache, pkv_dtype kv_dtype,
-                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                       const int32_t* context_lens, int32_t max_context_len,
-                                       int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
-                                       float scale, void* stream) {
-  g_last_error[0] = 0;
+}  // extern "C"
+
+// Validates the prefill arguments and fills *a; *empty: nothing to compute.
+static pkv_status prefill_args(void* out, pkv_dtype out_dtype, const void* q,
+                               const int32_t* cu_seqlens_q, int32_t Tq, int32_t max_query_len,
+                               const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t max_context_len, int32_t S,
+                               int32_t Hq, int32_t Hkv, int32_t D, int32_t B, float scale,
+                               PrefillArgs* a, bool* empty) {
+  *empty = true;
   PKV_REQUIRE(S >= 0 && Tq >= 0 && max_query_len >= 0 && Hq > 0 && Hkv > 0 && D > 0 && B > 0,
               PKV_ERR_INVALID_ARG, "prefill: S=%d Tq=%d max_query_len=%d Hq=%d Hkv=%d D=%d B=%d",
               S, Tq, max_query_len, Hq, Hkv, D, B);
@@ -312,30 +314,123 @@ pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const voi
               max_blocks_per_seq, B);
   PKV_REQUIRE(scale == scale, PKV_ERR_INVALID_ARG, "prefill: scale is NaN");
   if (S == 0 || Tq == 0) return PKV_OK;
+  *empty = false;
   PKV_REQUIRE(out && q && cu_seqlens_q && k_cache && v_cache && block_tables && context_lens,
               PKV_ERR_INVALID_ARG, "prefill: null pointer");
+  a->out = out;
+  a->q = q;
+  a->cu_seqlens_q = cu_seqlens_q;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->max_nb = max_blocks_per_seq;
+  a->Tq = Tq;
+  a->max_query_len = max_query_len;
+  a->S = S;
+  a->Hq = Hq;
+  a->Hkv = Hkv;
+  a->D = D;
+  a->B = B;
+  a->log2B = ilog2(B);
+  a->max_ctx = max_context_len;
+  a->out_dt = out_dtype;
+  a->scale_log2 = scale * 1.4426950408889634f;
+  return PKV_OK;
+}
+
+extern "C" {
+
+pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* q,
+                                       const int32_t* cu_seqlens_q, int32_t Tq,
+                                       int32_t max_query_len, const void* k_cache,
+                                       const void* v_cache, pkv_dtype kv_dtype,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t max_context_len,
+                                       int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                       float scale, void* stream) {
+  g_last_error[0] = 0;
   PrefillArgs a;
-  a.out = out;
-  a.q = q;
-  a.cu_seqlens_q = cu_seqlens_q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.max_nb = max_blocks_per_seq;
-  a.Tq = Tq;
-  a.max_query_len = max_query_len;
-  a.S = S;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.D = D;
-  a.B = B;
-  a.log2B = ilog2(B);
-  a.max_ctx = max_context_len;
-  a.out_dt = out_dtype;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  bool empty = true;
+  const pkv_status st = prefill_args(out, out_dtype, q, cu_seqlens_q, Tq, max_query_len, k_cache,
+                                     v_cache, kv_dtype, block_tables, max_blocks_per_seq,
+                                     context_lens, max_context_len, S, Hq, Hkv, D, B, scale, &a,
+                                     &empty);
+  if (st != PKV_OK || empty) return st;
   return launch_prefill(kv_dtype, a, static_cast<hipStream_t>(stream));
 }
+
+pkv_status pkv_mixed_workspace_size(int32_t S, int32_t num_decode, int32_t Hq, int32_t Hkv,
+                                    int32_t D, int32_t B, int32_t max_context_len,
+                                    size_t* bytes) {
+  g_last_error[0] = 0;
+  PKV_REQUIRE(bytes, PKV_ERR_INVALID_ARG, "mixed_workspace_size: null output");
+  PKV_REQUIRE(S >= 0 && num_decode >= 0 && num_decode <= S && Hq > 0 && Hkv > 0 && D > 0 &&
+                  B > 0 && max_context_len >= 0 && Hq % Hkv == 0,
+              PKV_ERR_INVALID_ARG, "mixed_workspace_size: bad sizes");
+  DecodePlan plan{};
+  if (num_decode > 0) {
+    const pkv_status st = plan_decode(num_decode, Hq, Hkv, D, B, max_context_len, &plan);
+    if (st != PKV_OK) return st;
+  }
+  *bytes = mixed_workspace_size(plan, S - num_decode);
+  return PKV_OK;
+}
+
+pkv_status pkv_paged_attention_mixed(void* out, pkv_dtype out_dtype, const void* q,
+                                     const int32_t* cu_seqlens_q, int32_t Tq, int32_t num_decode,
+                                     int32_t max_query_len, const void* k_cache,
+                                     const void* v_cache, pkv_dtype kv_dtype,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t max_context_len,
+                                     int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                     float scale, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  g_last_error[0] = 0;
+  PKV_REQUIRE(num_decode >= 0 && num_decode <= S && num_decode <= Tq, PKV_ERR_INVALID_ARG,
+              "mixed: num_decode %d outside [0, min(S=%d, Tq=%d)]", num_decode, S, Tq);
+  PrefillArgs pa;
+  bool empty = true;
+  pkv_status st = prefill_args(out, out_dtype, q, cu_seqlens_q, Tq, max_query_len, k_cache,
+                               v_cache, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
+                               max_context_len, S, Hq, Hkv, D, B, scale, &pa, &empty);
+  if (st != PKV_OK || empty) return st;
+  PKV_REQUIRE((int64_t)B * Hkv * D * dt_bytes(kv_dtype) < ((int64_t)1 << 31), PKV_ERR_UNSUPPORTED,
+              "mixed: one block of one pool must be smaller than 2 GiB");
+  DecodePlan plan{};
+  if (num_decode > 0) {
+    st = plan_decode(num_decode, Hq, Hkv, D, B, max_context_len, &plan);
+    if (st != PKV_OK) return st;
+  }
+  const size_t need = mixed_workspace_size(plan, S - num_decode);
+  PKV_REQUIRE(workspace && workspace_bytes >= need, PKV_ERR_WORKSPACE,
+              "mixed: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  DecodeArgs da{};
+  da.out = out;
+  da.q = q;
+  da.k_cache = k_cache;
+  da.v_cache = v_cache;
+  da.block_tables = block_tables;
+  da.context_lens = context_lens;
+  char* ws = static_cast<char*>(workspace);
+  da.ws_ps = reinterpret_cast<int32_t*>(ws + plan.ws_ps_off);
+  da.ws_ml = reinterpret_cast<float*>(ws + plan.ws_ml_off);
+  da.ws_acc = reinterpret_cast<float*>(ws + plan.ws_acc_off);
+  da.max_nb = max_blocks_per_seq;
+  da.S = num_decode;
+  da.Hq = Hq;
+  da.Hkv = Hkv;
+  da.D = D;
+  da.B = B;
+  da.log2B = ilog2(B);
+  da.max_ctx = max_context_len;
+  da.out_dt = out_dtype;
+  da.scale_log2 = scale * 1.4426950408889634f;
+  pa.S = S - num_decode;
+  return launch_mixed(kv_dtype, plan, da, pa, num_decode, workspace,
+                      static_cast<hipStream_t>(stream));
+}
+
 
 pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
                            const int64_t* block_pairs, int32_t N, int32_t B, int32_t Hkv,

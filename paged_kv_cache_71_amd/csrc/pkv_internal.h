@@ -152,4 +152,12 @@ struct PrefillArgs {
 };
 pkv_status launch_prefill(int kv_dt, const PrefillArgs& a, hipStream_t stream);
 
+// Mixed decode + prefill batch (mixed.hip): the decode part (dec.S sequences,
+// plan for them) and the prefill part (pre: the whole batch's pointers, pre.S =
+// number of prefill sequences after the num_decode decodes).
+size_t mixed_workspace_size(const DecodePlan& plan, int32_t S_prefill);
+pkv_status launch_mixed(int kv_dt, const DecodePlan& plan, const DecodeArgs& dec,
+                        const PrefillArgs& pre, int32_t num_decode, void* workspace,
+                        hipStream_t stream);
+
 }  // namespace pkv

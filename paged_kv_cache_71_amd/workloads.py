@@ -438,6 +438,35 @@ def grouped_batch(seed: int, group_sizes, prefix_blocks, suffix_lens, Hq: int, H
                         "group_prefix_lens": np.array(prefix_blocks, np.int32) * B})
 
 
+def mixed_batch(seed: int, decode_lens, prefill_prior, prefill_chunks, Hq: int, Hkv: int, D: int,
+                B: int, dtype: str, NB: int | None = None, name: str = "mixed") -> PagedBatch:
+    """A batch mixing decodes and prefill chunks, decodes first: sequence i <
+    len(decode_lens) has one query row over decode_lens[i] cached tokens; the
+    others a chunk of prefill_chunks[j] rows after prefill_prior[j] tokens.
+    ``meta["num_decode"]`` is the number of decodes."""
+    rng = np.random.default_rng(seed)
+    dl = np.asarray(decode_lens, np.int32)
+    prior = np.asarray(prefill_prior, np.int32)
+    chunks = np.asarray(prefill_chunks, np.int32)
+    lengths = np.concatenate([dl, prior + chunks]).astype(np.int32)
+    chunk_lens = np.concatenate([np.ones(dl.shape[0], np.int32), chunks]).astype(np.int32)
+    if NB is None:
+        NB = max(64, 2 * int(sum(-(-int(L) // B) for L in lengths)))
+    free_order = rng.permutation(NB)
+    return _build(name, rng, lengths, Hq, Hkv, D, B, NB, dtype, q_rows=int(chunk_lens.sum()),
+                  chunk_lens=chunk_lens, free_order=free_order, meta={"num_decode": int(dl.shape[0])})
+
+
+def llama3_8b_mixed_bf16(seed: int = 0, chunk: int = 512, prior: int = 8192) -> PagedBatch:
+    """The Llama-3-8B decode batch (256 sequences, log-normal lengths) plus one
+    prefill chunk of ``chunk`` tokens after ``prior`` cached tokens, in one
+    batch (decodes first), 12 GB pool."""
+    rng = np.random.default_rng(seed)
+    lengths = lognormal_lengths(rng, 256)
+    return mixed_batch(seed + 1, lengths, [prior], [chunk], 32, 8, 128, 16, "bf16",
+                       NB=pool_blocks_for(16, 8, 128, "bf16"), name="llama3_8b_mixed_bf16")
+
+
 def prefill_bf16(seed: int = 0, S: int = 8, chunk: int = 512, prior_lo: int = 4096,
                  prior_hi: int = 32768, Hq: int = 32, Hkv: int = 8, D: int = 128, B: int = 16,
                  NB: int | None = None) -> PagedBatch:
