@@ -15,6 +15,8 @@ names the passage of the pages that the underlying C function follows:
 * causal chunked prefill: same book, ch. 13 sec. 2; CS349D lecture 3 sec. 7.2.
 * reshape_and_cache (slot writes): same book, ch. 13 sec. 1 (slot_mapping).
 * copy_blocks (copy-on-write): CS349D lecture 3 sec. 3.2 and sec. 4.1.
+* swap_blocks (swap-out / swap-in of a preempted sequence): CS349D lecture 3
+  sec. 5.2.
 * FP8 (OCP E4M3) KV cache -- quantizing reshape_and_cache and decode over
   dequantized values: "LLM inference, part 3: single node", ch. 10 (scale and
   clip on write, scale back on read).
@@ -68,6 +70,8 @@ def _load(path: str | None = None):
         lib.pkvo_reshape_and_cache.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, ci]
         lib.pkvo_copy_blocks.restype = ci
         lib.pkvo_copy_blocks.argtypes = [P, P, i32, P, i32, i32, i32, i32, i64, ci]
+        lib.pkvo_swap_blocks.restype = ci
+        lib.pkvo_swap_blocks.argtypes = [P, P, i32, P, i32, i64, i64, i64]
         lib.pkvo_e4m3_to_f64.restype = dbl
         lib.pkvo_e4m3_to_f64.argtypes = [ctypes.c_uint8]
         lib.pkvo_e4m3_from_f32.restype = ctypes.c_uint8
@@ -287,3 +291,22 @@ def decode_fp8(q, q_dtype: str, k_cache, v_cache, k_scale, v_scale, block_tables
                                _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(bt), max_nb,
                                _ptr(context_lens), NB, S, Hq, Hkv, D, B, scale), "decode_fp8")
     return out
+
+
+def swap_blocks(src_pools, dst_pools, pairs) -> None:
+    """In place: for every pool index p, dst_pools[p][dst] := src_pools[p][src]
+    for each (src, dst) pair (whole blocks, any dtype)."""
+    lib = _load()
+    pairs = _c(pairs, np.int64).reshape(-1, 2)
+    n = len(src_pools)
+    assert len(dst_pools) == n
+    for a in list(src_pools) + list(dst_pools):
+        assert a.flags.c_contiguous
+    if n == 0:
+        return
+    block_bytes = src_pools[0][0].nbytes
+    sp = (ctypes.c_void_p * n)(*[a.ctypes.data for a in src_pools])
+    dp = (ctypes.c_void_p * n)(*[a.ctypes.data for a in dst_pools])
+    _check(lib.pkvo_swap_blocks(ctypes.cast(sp, ctypes.c_void_p), ctypes.cast(dp, ctypes.c_void_p),
+                                n, _ptr(pairs) if pairs.size else 0, pairs.shape[0], block_bytes,
+                                src_pools[0].shape[0], dst_pools[0].shape[0]), "swap_blocks")

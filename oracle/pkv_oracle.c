@@ -44,6 +44,10 @@
  *    copy-on-write (CS349D lecture 3 sec. 3.2 and sec. 4.1: many small CoW
  *    copies are merged into one launch; the copy is made before the write).
  *
+ *  - swap_blocks copies whole blocks between two sets of pools (device and
+ *    host) for swapping a preempted sequence out and back in (CS349D lecture
+ *    3 sec. 5.2): destination block := source block in every pool.
+ *
  *  - FP8 KV cache ("LLM inference, part 3: single node", ch. 10: on write a
  *    16-bit K/V value is scaled and clipped into 8 bits; on read it is scaled
  *    back).  Format: OCP FP8 E4M3 (1 sign bit, 4 exponent bits with bias 7, 3
@@ -502,4 +506,25 @@ int pkvo_decode_fp8(double* out, const void* q, int q_dtype, const uint8_t* k_ca
   }
   free(K); free(V); free(qd);
   return rc;
+}
+
+/*
+ * swap_blocks: for every pool p and pair i, block pairs[2i+1] of dst_pools[p]
+ * becomes a copy of block pairs[2i] of src_pools[p] (block_bytes each; the
+ * sources have NB_src blocks, the destinations NB_dst).
+ */
+int pkvo_swap_blocks(void* const* src_pools, void* const* dst_pools, int32_t num_pools,
+                     const int64_t* pairs, int32_t N, int64_t block_bytes, int64_t NB_src,
+                     int64_t NB_dst) {
+  if (num_pools < 0 || N < 0 || block_bytes <= 0) return PKVO_EINVAL;
+  for (int32_t i = 0; i < N; ++i)
+    if (pairs[2 * i] < 0 || pairs[2 * i] >= NB_src || pairs[2 * i + 1] < 0 ||
+        pairs[2 * i + 1] >= NB_dst)
+      return PKVO_ERANGE;
+  for (int32_t p = 0; p < num_pools; ++p)
+    for (int32_t i = 0; i < N; ++i)
+      memcpy((char*)dst_pools[p] + (size_t)pairs[2 * i + 1] * (size_t)block_bytes,
+             (const char*)src_pools[p] + (size_t)pairs[2 * i] * (size_t)block_bytes,
+             (size_t)block_bytes);
+  return PKVO_OK;
 }

@@ -43,6 +43,8 @@ MUTATIONS = [
     ("reshape_k_into_v", "memcpy((char*)v_cache + dst, (const char*)value", "memcpy((char*)v_cache + dst, (const char*)key"),
     ("copy_reads_destination", "memcpy(snap + (size_t)(2 * i) * blk_bytes, kc + (size_t)pairs[2 * i] * blk_bytes",
      "memcpy(snap + (size_t)(2 * i) * blk_bytes, kc + (size_t)pairs[2 * i + 1] * blk_bytes"),
+    ("swap_reads_destination_index", "(const char*)src_pools[p] + (size_t)pairs[2 * i] * (size_t)block_bytes",
+     "(const char*)src_pools[p] + (size_t)pairs[2 * i + 1] * (size_t)block_bytes"),
     ("e4m3_exponent_bias", "else v = ldexp((double)(8 + m), e - 10);", "else v = ldexp((double)(8 + m), e - 9);"),
     ("e4m3_subnormal_scale", "if (e == 0) v = ldexp((double)m, -9);", "if (e == 0) v = ldexp((double)m, -10);"),
     ("e4m3_ties_to_odd", "(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
@@ -70,6 +72,7 @@ CASES = [
     (pins.test_prefill_matches_causal_sdpa_on_whole_sequences, {"dtype": "f32"}),
     (pins.test_reshape_and_cache_matches_numpy_scatter, {"dtype": "f32"}),
     (pins.test_copy_blocks_matches_numpy_indexing, {}),
+    (pins.test_swap_blocks_matches_numpy_indexing, {}),
     (pins.test_e4m3_decode_matches_torch_for_every_code, {}),
     (pins.test_e4m3_spec_constants, {}),
     (pins.test_e4m3_encode_matches_torch_inside_range, {}),

@@ -454,3 +454,23 @@ def test_decode_fp8_single_token_returns_code_times_scale():
             g = h // (Hq // Hkv)
             want = _torch_e4m3_to_f64(v[blk, 0, g]) * float(vs[g])
             assert np.array_equal(out[s, h], want)
+
+
+# ---------------------------------------------------------------- swap_blocks
+def test_swap_blocks_matches_numpy_indexing():
+    """Device-side pools of 12 blocks, host-side pools of 7; out and back."""
+    rng = np.random.default_rng(13)
+    B, Hkv, D, layers = 4, 2, 8, 3
+    gpu = [rng.standard_normal((12, B, Hkv, D)).astype(np.float32) for _ in range(2 * layers)]
+    cpu = [np.zeros((7, B, Hkv, D), np.float32) for _ in range(2 * layers)]
+    out_pairs = np.array([[3, 0], [11, 6], [0, 2]], np.int64)
+    oracle.swap_blocks(gpu, cpu, out_pairs)
+    for g, c in zip(gpu, cpu):
+        assert np.array_equal(c[[0, 6, 2]], g[[3, 11, 0]])
+        assert not c[[1, 3, 4, 5]].any()
+    back = [np.full_like(g, 7.0) for g in gpu]
+    in_pairs = np.array([[0, 9], [6, 1], [2, 4]], np.int64)
+    oracle.swap_blocks(cpu, back, in_pairs)
+    for g, b in zip(gpu, back):
+        assert np.array_equal(b[[9, 1, 4]], g[[3, 11, 0]])
+        assert np.all(b[[0, 2, 3, 5, 6, 7, 8, 10, 11]] == 7.0)
