@@ -390,6 +390,29 @@ def main():
         ms, _ = time_fn(lambda: pkv.copy_blocks([kc], [vc], pairs), 20)
         cb = 192 * 2 * 2 * B * Hkv * D * 2
         rows["copy_blocks_192_pairs"] = {"ms": round(ms, 5), "GB/s": round(cb / ms / 1e6, 1)}
+
+        # swap-out of 1024 scattered blocks (K and V, 64 KiB per block) to a
+        # pinned host pool: one swap_blocks launch against one copy per block
+        host_k = torch.empty((1024, B, Hkv, D), dtype=torch.bfloat16).pin_memory()
+        host_v = torch.empty_like(host_k).pin_memory()
+        src = np.random.default_rng(1).permutation(NBc)[:1024]
+        sp = torch.from_numpy(np.stack([src, np.arange(1024)], 1).astype(np.int64)).to(dev)
+        ms_k, _ = time_fn(lambda: pkv.swap_blocks([kc, vc], [host_k, host_v], sp), 10)
+        src_l = src.tolist()
+
+        def per_block():
+            for i, s_ in enumerate(src_l):
+                host_k[i].copy_(kc[s_], non_blocking=True)
+                host_v[i].copy_(vc[s_], non_blocking=True)
+
+        ms_p, _ = time_fn(per_block, 3, warm=1)
+        sb = 1024 * 2 * B * Hkv * D * 2
+        rows["swap_out_1024_blocks"] = {"ms": round(ms_k, 4), "GB/s": round(sb / ms_k / 1e6, 1),
+                                        "per_block_copies_ms": round(ms_p, 4),
+                                        "speedup_vs_per_block": round(ms_p / ms_k, 2)}
+        log(f"[bench] swap_out 1024 blocks: {ms_k * 1e3:.1f} us ({sb / ms_k / 1e6:.1f} GB/s), "
+            f"per-block copies {ms_p * 1e3:.1f} us")
+        del host_k, host_v
         del kc, vc
         torch.cuda.empty_cache()
 

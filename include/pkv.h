@@ -298,6 +298,36 @@ pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t
                            int32_t D, pkv_dtype kv_dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * swap_blocks -- batched whole-block copies between two sets of pools, for
+ * swapping a preempted sequence's KV blocks out to host memory and back.
+ *
+ * Defined by CS349D lecture 3 sec. 5.2 (recovery by swapping: the blocks are
+ * copied to CPU memory, from a CPU block allocator, and copied back on
+ * resume; each separate copy has a fixed cost, so many small copies are worth
+ * batching) and "LLM inference, part 3" ch. 14 (swap-out / swap-in over the
+ * host link as the alternative to recomputation).
+ *
+ *   src_pools, dst_pools : HOST arrays of num_pools pointers; pool i of src
+ *                          pairs with pool i of dst (e.g. the K and V pools of
+ *                          every layer).  Each pointer is device memory or
+ *                          pinned host memory (hipHostMalloc, torch
+ *                          pin_memory); pageable host memory is refused with
+ *                          PKV_ERR_INVALID_ARG.  Pools are [NB_x, B, Hkv, D] of
+ *                          kv_dtype (PKV_FP8_E4M3 allowed); the two sides may
+ *                          have different block counts.
+ *   block_pairs          : device or pinned host int64 [N, 2] of (source block,
+ *                          destination block)
+ * For every pool and pair, destination block dst becomes a bit copy of source
+ * block src.  Destinations must be distinct and the two sides must not
+ * overlap.  One kernel launch (per 64 pools) on `stream` does all copies; it
+ * reads and writes the host side directly.  N == 0 or num_pools == 0 is a
+ * no-op.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_swap_blocks(const void* const* src_pools, void* const* dst_pools, int32_t num_pools,
+                           const int64_t* block_pairs, int32_t N, int32_t B, int32_t Hkv,
+                           int32_t D, pkv_dtype kv_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Host block manager (CPU only; builds block tables, slots and CoW pairs).
  *
  * Defined by the S06 PagedAttention chapter ("block manager" listing: a free
@@ -347,6 +377,26 @@ pkv_status pkv_bm_num_free(const pkv_block_manager* bm, int32_t* n);
  * blocks have refcount 0 and appear once, every table has ceil(len / B)
  * entries.  Returns PKV_OK or PKV_ERR_INVALID_ARG with detail. */
 pkv_status pkv_bm_check(const pkv_block_manager* bm);
+
+/* Swapping (CS349D lecture 3 sec. 5.2): a CPU pool of num_cpu_blocks blocks
+ * (resets the CPU free list; refused while a sequence is swapped out). */
+pkv_status pkv_bm_set_cpu_blocks(pkv_block_manager* bm, int32_t num_cpu_blocks);
+pkv_status pkv_bm_num_free_cpu(const pkv_block_manager* bm, int32_t* n);
+/* Swap a resident sequence out: every block of its table gets a CPU block;
+ * pairs (host int64 [cap, 2]) receives (GPU block, CPU block) in table order,
+ * *n their number; the GPU blocks are released (freed unless another sequence
+ * holds them).  The copies must be issued (pkv_swap_blocks) before anything
+ * writes into the released blocks.  While swapped out, the sequence has no
+ * table or slots and cannot grow or fork; free_seq returns its CPU blocks.
+ * PKV_ERR_OOM if the CPU pool is short (nothing changes). */
+pkv_status pkv_bm_swap_out(pkv_block_manager* bm, int32_t seq_id, int64_t* pairs, int32_t cap,
+                           int32_t* n);
+/* Swap a sequence back in: fresh GPU blocks for its CPU blocks, pairs =
+ * (CPU block, GPU block) in table order; the CPU blocks return to the CPU
+ * free list (issue the copies before reusing them).  PKV_ERR_OOM if the GPU
+ * pool is short (nothing changes). */
+pkv_status pkv_bm_swap_in(pkv_block_manager* bm, int32_t seq_id, int64_t* pairs, int32_t cap,
+                          int32_t* n);
 
 #ifdef __cplusplus
 }

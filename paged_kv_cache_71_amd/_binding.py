@@ -61,6 +61,11 @@ def load_library(path: str | None = None):
         "pkv_paged_attention_prefill": (st, [P, st, P, P, i32, i32, P, P, st, P, i32, P, i32, i32,
                                              i32, i32, i32, i32, f32, P]),
         "pkv_copy_blocks": (st, [P, P, i32, P, i32, i32, i32, i32, st, P]),
+        "pkv_swap_blocks": (st, [P, P, i32, P, i32, i32, i32, i32, st, P]),
+        "pkv_bm_set_cpu_blocks": (st, [P, i32]),
+        "pkv_bm_num_free_cpu": (st, [P, I32P]),
+        "pkv_bm_swap_out": (st, [P, i32, P, i32, I32P]),
+        "pkv_bm_swap_in": (st, [P, i32, P, i32, I32P]),
         "pkv_reshape_and_cache_fp8": (st, [P, P, st, P, P, P, i32, i32, i32, i32, i64, P, P, P]),
         "pkv_mixed_workspace_size": (st, [i32, i32, i32, i32, i32, i32, i32, SZP]),
         "pkv_paged_attention_mixed": (st, [P, st, P, P, i32, i32, i32, P, P, st, P, i32, P, i32, i32,
@@ -396,6 +401,36 @@ def paged_attention_decode_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block
     return out
 
 
+def swap_blocks(src_pools, dst_pools, block_pairs, stream=None) -> None:
+    """For every pool index p: dst_pools[p][dst] := src_pools[p][src] for each
+    (src, dst) pair.  Each pool is a device tensor or a pinned host tensor
+    (``pin_memory``); block_pairs [N, 2] int64 on the device or pinned host."""
+    torch = _torch()
+    lib = load_library()
+    if len(src_pools) != len(dst_pools):
+        raise ValueError("swap_blocks: as many destination pools as source pools")
+    n = len(src_pools)
+    N = block_pairs.shape[0] if block_pairs.dim() == 2 else 0
+    if block_pairs.numel() and (block_pairs.dim() != 2 or block_pairs.shape[1] != 2):
+        raise ValueError("swap_blocks: block_pairs must be [N, 2]")
+    if n == 0 or N == 0:
+        return
+    _, B, Hkv, D = src_pools[0].shape
+    for t in list(src_pools) + list(dst_pools):
+        if tuple(t.shape[1:]) != (B, Hkv, D) or t.dtype != src_pools[0].dtype:
+            raise ValueError("swap_blocks: every pool must be [NB, B, Hkv, D] of one dtype")
+        if not t.is_contiguous() or not (t.is_cuda or t.is_pinned()):
+            raise ValueError("swap_blocks: pools must be contiguous device or pinned host tensors")
+    if block_pairs.dtype != torch.int64 or not block_pairs.is_contiguous() or not (
+            block_pairs.is_cuda or block_pairs.is_pinned()):
+        raise ValueError("swap_blocks: block_pairs must be contiguous int64, device or pinned")
+    sp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in src_pools])
+    dp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in dst_pools])
+    _check(lib.pkv_swap_blocks(ctypes.cast(sp, ctypes.c_void_p), ctypes.cast(dp, ctypes.c_void_p), n,
+                               block_pairs.data_ptr(), N, B, Hkv, D, dtype_code(src_pools[0]),
+                               _stream(stream)), "swap_blocks")
+
+
 # ---------------------------------------------------------------- host block manager
 class BlockManager:
     """Host block manager (free list, tables, refcounts, copy-on-write)."""
@@ -470,3 +505,26 @@ class BlockManager:
 
     def check(self) -> None:
         _check(self._lib.pkv_bm_check(self._h), "bm_check")
+
+    def set_cpu_blocks(self, n: int) -> None:
+        _check(self._lib.pkv_bm_set_cpu_blocks(self._h, n), "bm_set_cpu_blocks")
+
+    def num_free_cpu(self) -> int:
+        n = ctypes.c_int32()
+        _check(self._lib.pkv_bm_num_free_cpu(self._h, ctypes.byref(n)), "bm_num_free_cpu")
+        return n.value
+
+    def _swap(self, fn, seq: int, where: str) -> np.ndarray:
+        cap = max(1, (self.seq_len(seq) + self.block_size - 1) // self.block_size)
+        out = np.zeros((cap, 2), np.int64)
+        n = ctypes.c_int32()
+        _check(fn(self._h, seq, out.ctypes.data, cap, ctypes.byref(n)), where)
+        return out[:n.value]
+
+    def swap_out(self, seq: int) -> np.ndarray:
+        """Pairs (GPU block, CPU block) to copy with swap_blocks; the GPU blocks are released."""
+        return self._swap(self._lib.pkv_bm_swap_out, seq, "bm_swap_out")
+
+    def swap_in(self, seq: int) -> np.ndarray:
+        """Pairs (CPU block, GPU block) to copy with swap_blocks; the CPU blocks are released."""
+        return self._swap(self._lib.pkv_bm_swap_in, seq, "bm_swap_in")

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -431,6 +433,66 @@ pkv_status pkv_paged_attention_mixed(void* out, pkv_dtype out_dtype, const void*
                       static_cast<hipStream_t>(stream));
 }
 
+
+}  // extern "C"
+
+// Address a kernel may use for p: device memory as is, pinned host memory
+// through its device mapping.  Pageable host memory (or anything HIP does not
+// know) is refused: a kernel touching it would fault.
+static pkv_status device_view(const void* p, const void** out, const char* what) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PKV_ERR_INVALID_ARG, "%s: %p is neither device nor pinned host memory", what, p);
+  }
+  if (attr.type == hipMemoryTypeHost) {
+    unsigned flags = 0;  // only page-locked (pinned) host memory has host flags
+    if (!attr.devicePointer || hipHostGetFlags(&flags, const_cast<void*>(p)) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(PKV_ERR_INVALID_ARG, "%s: %p is neither device nor pinned host memory", what, p);
+    }
+    *out = attr.devicePointer;
+  } else if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged ||
+             attr.type == hipMemoryTypeUnified) {
+    *out = p;
+  } else {
+    return fail(PKV_ERR_INVALID_ARG, "%s: %p is neither device nor pinned host memory", what, p);
+  }
+  return PKV_OK;
+}
+
+extern "C" {
+
+pkv_status pkv_swap_blocks(const void* const* src_pools, void* const* dst_pools, int32_t num_pools,
+                           const int64_t* block_pairs, int32_t N, int32_t B, int32_t Hkv,
+                           int32_t D, pkv_dtype kv_dtype, void* stream) {
+  g_last_error[0] = 0;
+  PKV_REQUIRE(num_pools >= 0 && N >= 0 && B > 0 && Hkv > 0 && D > 0, PKV_ERR_INVALID_ARG,
+              "swap_blocks: pools=%d N=%d B=%d Hkv=%d D=%d", num_pools, N, B, Hkv, D);
+  PKV_REQUIRE(supported_dtype(kv_dtype) || kv_dtype == PKV_FP8_E4M3, PKV_ERR_UNSUPPORTED,
+              "swap_blocks: dtype %d", (int)kv_dtype);
+  PKV_REQUIRE(supported_head_dim(D), PKV_ERR_UNSUPPORTED, "swap_blocks: head_dim %d", D);
+  PKV_REQUIRE(supported_block(B), PKV_ERR_UNSUPPORTED, "swap_blocks: block_size %d", B);
+  if (N == 0 || num_pools == 0) return PKV_OK;
+  PKV_REQUIRE(src_pools && dst_pools && block_pairs, PKV_ERR_INVALID_ARG, "swap_blocks: null pointer");
+  std::vector<const void*> src(num_pools);
+  std::vector<void*> dst(num_pools);
+  for (int32_t i = 0; i < num_pools; ++i) {
+    PKV_REQUIRE(src_pools[i] && dst_pools[i], PKV_ERR_INVALID_ARG, "swap_blocks: null pool %d", i);
+    const void* d = nullptr;
+    pkv_status st = device_view(src_pools[i], &src[i], "swap_blocks (source pool)");
+    if (st != PKV_OK) return st;
+    st = device_view(dst_pools[i], &d, "swap_blocks (destination pool)");
+    if (st != PKV_OK) return st;
+    dst[i] = const_cast<void*>(d);
+  }
+  const void* pairs = nullptr;
+  const pkv_status st = device_view(block_pairs, &pairs, "swap_blocks (pairs)");
+  if (st != PKV_OK) return st;
+  const int64_t block_bytes = (int64_t)B * Hkv * D * dt_bytes(kv_dtype);
+  return launch_swap_blocks(src.data(), dst.data(), num_pools, static_cast<const int64_t*>(pairs),
+                            N, block_bytes, static_cast<hipStream_t>(stream));
+}
 
 pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
                            const int64_t* block_pairs, int32_t N, int32_t B, int32_t Hkv,

@@ -16,6 +16,12 @@
 //    4.1-4.2; CMU 11-868 lecture 24 sec. 4).
 //  * Exhaustion returns PKV_ERR_OOM and changes nothing (S06 chapter: the
 //    allocator fails and the scheduler preempts).
+//  * Swapping (CS349D lecture 3 sec. 5.2; "LLM inference, part 3", ch. 14): a
+//    preempted sequence's blocks are copied to CPU blocks from a second free
+//    list and its GPU blocks released (a block other sequences still hold
+//    stays with them); swapping in takes fresh GPU blocks for its CPU blocks.
+//    The (source, destination) pairs go to pkv_swap_blocks.  The CPU pool is
+//    never larger than the caller makes it, so swap space stays bounded.
 #include <deque>
 #include <string>
 #include <vector>
@@ -32,10 +38,15 @@ struct pkv_block_manager {
   int32_t B = 0;
   std::deque<int32_t> free_list;
   std::vector<int32_t> refcount;
+  int32_t num_cpu_blocks = 0;
+  std::deque<int32_t> cpu_free;
+  std::vector<char> cpu_used;
   struct Seq {
     bool live = false;
+    bool swapped = false;  // its blocks are in cpu_table, its table is empty
     int32_t len = 0;
     std::vector<int32_t> table;
+    std::vector<int32_t> cpu_table;
   };
   std::vector<Seq> seqs;
 
@@ -44,6 +55,12 @@ struct pkv_block_manager {
     return &seqs[id];
   }
   Seq* get(int32_t id) { return const_cast<Seq*>(static_cast<const pkv_block_manager*>(this)->get(id)); }
+  // a live sequence whose blocks are on the GPU
+  const Seq* resident(int32_t id) const {
+    const Seq* sq = get(id);
+    return sq && !sq->swapped ? sq : nullptr;
+  }
+  Seq* resident(int32_t id) { return const_cast<Seq*>(static_cast<const pkv_block_manager*>(this)->resident(id)); }
   int32_t new_seq_id() {
     seqs.emplace_back();
     return (int32_t)seqs.size() - 1;
@@ -111,8 +128,8 @@ pkv_status pkv_bm_add_seq(pkv_block_manager* bm, int32_t n_tokens, int32_t* seq_
 pkv_status pkv_bm_append_token(pkv_block_manager* bm, int32_t seq_id, int64_t* slot,
                                int32_t* cow_src, int32_t* cow_dst) {
   if (!bm || !slot) return fail(PKV_ERR_INVALID_ARG, "bm_append_token: bad argument");
-  auto* sq = bm->get(seq_id);
-  if (!sq) return fail(PKV_ERR_INVALID_ARG, "bm_append_token: no sequence %d", seq_id);
+  auto* sq = bm->resident(seq_id);
+  if (!sq) return fail(PKV_ERR_INVALID_ARG, "bm_append_token: no resident sequence %d", seq_id);
   const int32_t B = bm->B;
   const int32_t pos = sq->len;  // position of the new token
   int32_t src = -1, dst = -1;
@@ -141,7 +158,7 @@ pkv_status pkv_bm_append_token(pkv_block_manager* bm, int32_t seq_id, int64_t* s
 
 pkv_status pkv_bm_fork(pkv_block_manager* bm, int32_t parent, int32_t* child) {
   if (!bm || !child) return fail(PKV_ERR_INVALID_ARG, "bm_fork: bad argument");
-  if (!bm->get(parent)) return fail(PKV_ERR_INVALID_ARG, "bm_fork: no sequence %d", parent);
+  if (!bm->resident(parent)) return fail(PKV_ERR_INVALID_ARG, "bm_fork: no resident sequence %d", parent);
   const int32_t id = bm->new_seq_id();  // may reallocate seqs: look the parent up again
   auto& p = bm->seqs[parent];
   auto& c = bm->seqs[id];
@@ -158,7 +175,13 @@ pkv_status pkv_bm_free_seq(pkv_block_manager* bm, int32_t seq_id) {
   auto* sq = bm->get(seq_id);
   if (!sq) return fail(PKV_ERR_INVALID_ARG, "bm_free_seq: no sequence %d", seq_id);
   for (int32_t b : sq->table) bm->release(b);
+  for (int32_t c : sq->cpu_table) {
+    bm->cpu_used[c] = 0;
+    bm->cpu_free.push_back(c);
+  }
   sq->table.clear();
+  sq->cpu_table.clear();
+  sq->swapped = false;
   sq->live = false;
   sq->len = 0;
   return PKV_OK;
@@ -168,8 +191,8 @@ pkv_status pkv_bm_table(const pkv_block_manager* bm, int32_t seq_id, int32_t* ou
                         int32_t* n) {
   if (!bm || !n || cap < 0 || (cap > 0 && !out))
     return fail(PKV_ERR_INVALID_ARG, "bm_table: bad argument");
-  const auto* sq = bm->get(seq_id);
-  if (!sq) return fail(PKV_ERR_INVALID_ARG, "bm_table: no sequence %d", seq_id);
+  const auto* sq = bm->resident(seq_id);
+  if (!sq) return fail(PKV_ERR_INVALID_ARG, "bm_table: no resident sequence %d", seq_id);
   *n = (int32_t)sq->table.size();
   if (*n > cap) return fail(PKV_ERR_INVALID_ARG, "bm_table: capacity %d < %d", cap, *n);
   for (int32_t i = 0; i < *n; ++i) out[i] = sq->table[i];
@@ -188,8 +211,8 @@ pkv_status pkv_bm_slots(const pkv_block_manager* bm, int32_t seq_id, int32_t sta
                         int64_t* out) {
   if (!bm || count < 0 || start < 0 || (count > 0 && !out))
     return fail(PKV_ERR_INVALID_ARG, "bm_slots: bad argument");
-  const auto* sq = bm->get(seq_id);
-  if (!sq) return fail(PKV_ERR_INVALID_ARG, "bm_slots: no sequence %d", seq_id);
+  const auto* sq = bm->resident(seq_id);
+  if (!sq) return fail(PKV_ERR_INVALID_ARG, "bm_slots: no resident sequence %d", seq_id);
   if ((int64_t)start + count > sq->len)
     return fail(PKV_ERR_INVALID_ARG, "bm_slots: positions %d..%d past length %d", start,
                 start + count - 1, sq->len);
@@ -219,6 +242,14 @@ pkv_status pkv_bm_check(const pkv_block_manager* bm) {
   for (size_t i = 0; i < bm->seqs.size(); ++i) {
     const auto& sq = bm->seqs[i];
     if (!sq.live) continue;
+    if (sq.swapped) {
+      if (!sq.table.empty() || (int32_t)sq.cpu_table.size() != blocks_for(sq.len, bm->B))
+        return fail(PKV_ERR_INVALID_ARG, "bm_check: swapped sequence %zu holds %zu / %zu blocks", i,
+                    sq.table.size(), sq.cpu_table.size());
+      continue;
+    }
+    if (!sq.cpu_table.empty())
+      return fail(PKV_ERR_INVALID_ARG, "bm_check: resident sequence %zu holds CPU blocks", i);
     if ((int32_t)sq.table.size() != blocks_for(sq.len, bm->B))
       return fail(PKV_ERR_INVALID_ARG, "bm_check: sequence %zu has %zu blocks for %d tokens", i,
                   sq.table.size(), sq.len);
@@ -241,6 +272,94 @@ pkv_status pkv_bm_check(const pkv_block_manager* bm) {
       return fail(PKV_ERR_INVALID_ARG, "bm_check: block %d free=%d with %d holders", b,
                   (int)in_free[b], holders[b]);
   }
+  // CPU blocks: each held by exactly one swapped sequence or free, never both
+  std::vector<int32_t> cpu_holders(bm->num_cpu_blocks, 0);
+  for (const auto& sq : bm->seqs)
+    if (sq.live)
+      for (int32_t c : sq.cpu_table) {
+        if (c < 0 || c >= bm->num_cpu_blocks) return fail(PKV_ERR_INVALID_ARG, "bm_check: bad CPU block %d", c);
+        cpu_holders[c] += 1;
+      }
+  std::vector<char> cpu_in_free(bm->num_cpu_blocks, 0);
+  for (int32_t c : bm->cpu_free) {
+    if (cpu_in_free[c]) return fail(PKV_ERR_INVALID_ARG, "bm_check: CPU block %d free twice", c);
+    cpu_in_free[c] = 1;
+  }
+  for (int32_t c = 0; c < bm->num_cpu_blocks; ++c)
+    if (cpu_holders[c] > 1 || (cpu_holders[c] == 0) != (cpu_in_free[c] != 0) ||
+        (cpu_holders[c] == 1) != (bm->cpu_used[c] != 0))
+      return fail(PKV_ERR_INVALID_ARG, "bm_check: CPU block %d has %d holders, free=%d", c,
+                  cpu_holders[c], (int)cpu_in_free[c]);
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_set_cpu_blocks(pkv_block_manager* bm, int32_t num_cpu_blocks) {
+  if (!bm || num_cpu_blocks < 0) return fail(PKV_ERR_INVALID_ARG, "bm_set_cpu_blocks: bad argument");
+  for (const auto& sq : bm->seqs)
+    if (sq.live && sq.swapped)
+      return fail(PKV_ERR_INVALID_ARG, "bm_set_cpu_blocks: a sequence is swapped out");
+  bm->num_cpu_blocks = num_cpu_blocks;
+  bm->cpu_free.clear();
+  for (int32_t c = 0; c < num_cpu_blocks; ++c) bm->cpu_free.push_back(c);
+  bm->cpu_used.assign(num_cpu_blocks, 0);
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_num_free_cpu(const pkv_block_manager* bm, int32_t* n) {
+  if (!bm || !n) return fail(PKV_ERR_INVALID_ARG, "bm_num_free_cpu: bad argument");
+  *n = (int32_t)bm->cpu_free.size();
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_swap_out(pkv_block_manager* bm, int32_t seq_id, int64_t* pairs, int32_t cap,
+                           int32_t* n) {
+  if (!bm || !n || cap < 0 || (cap > 0 && !pairs))
+    return fail(PKV_ERR_INVALID_ARG, "bm_swap_out: bad argument");
+  auto* sq = bm->resident(seq_id);
+  if (!sq) return fail(PKV_ERR_INVALID_ARG, "bm_swap_out: no resident sequence %d", seq_id);
+  const int32_t nb = (int32_t)sq->table.size();
+  if (nb > cap) return fail(PKV_ERR_INVALID_ARG, "bm_swap_out: capacity %d < %d", cap, nb);
+  if ((size_t)nb > bm->cpu_free.size())
+    return fail(PKV_ERR_OOM, "bm_swap_out: OOM (%d CPU blocks needed, %zu free)", nb,
+                bm->cpu_free.size());
+  for (int32_t i = 0; i < nb; ++i) {
+    const int32_t c = bm->cpu_free.front();
+    bm->cpu_free.pop_front();
+    bm->cpu_used[c] = 1;
+    pairs[2 * i] = sq->table[i];
+    pairs[2 * i + 1] = c;
+    sq->cpu_table.push_back(c);
+    bm->release(sq->table[i]);
+  }
+  sq->table.clear();
+  sq->swapped = true;
+  *n = nb;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_swap_in(pkv_block_manager* bm, int32_t seq_id, int64_t* pairs, int32_t cap,
+                          int32_t* n) {
+  if (!bm || !n || cap < 0 || (cap > 0 && !pairs))
+    return fail(PKV_ERR_INVALID_ARG, "bm_swap_in: bad argument");
+  auto* sq = bm->get(seq_id);
+  if (!sq || !sq->swapped) return fail(PKV_ERR_INVALID_ARG, "bm_swap_in: no swapped sequence %d", seq_id);
+  const int32_t nb = (int32_t)sq->cpu_table.size();
+  if (nb > cap) return fail(PKV_ERR_INVALID_ARG, "bm_swap_in: capacity %d < %d", cap, nb);
+  if ((size_t)nb > bm->free_list.size())
+    return fail(PKV_ERR_OOM, "bm_swap_in: OOM (%d blocks needed, %zu free)", nb,
+                bm->free_list.size());
+  for (int32_t i = 0; i < nb; ++i) {
+    const int32_t g = bm->take();
+    const int32_t c = sq->cpu_table[i];
+    pairs[2 * i] = c;
+    pairs[2 * i + 1] = g;
+    sq->table.push_back(g);
+    bm->cpu_used[c] = 0;
+    bm->cpu_free.push_back(c);
+  }
+  sq->cpu_table.clear();
+  sq->swapped = false;
+  *n = nb;
   return PKV_OK;
 }
 

@@ -9,6 +9,12 @@
 //    kernel for split + reorder + block write).
 //  * copy_blocks: all copy-on-write block copies of a step, for every layer,
 //    in one launch (CS349D lecture 3 sec. 3.2 and sec. 4.1).
+//  * swap_blocks: whole blocks between two sets of pools, one in device
+//    memory and one in pinned host memory (or both on the device), for every
+//    layer in one launch -- the swap-out / swap-in of a preempted sequence
+//    (CS349D lecture 3 sec. 5.2: KV blocks copied to CPU memory and back; a
+//    fixed cost per separate copy makes one batched launch pay off).  The
+//    kernel reads and writes the pinned host pages directly over the host link.
 //  * reshape_and_cache_fp8: the same scatter into an FP8 pool, each element
 //    scaled by its KV head's scale and rounded into an OCP E4M3 code
 //    ("LLM inference, part 3", ch. 10: scale and clip into 8 bits on write).
@@ -131,7 +137,51 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
   for (; i < block_chunks; i += kCopyThreads) d[i] = s[i];
 }
 
+struct PoolPairPtrs {
+  const uint4* src[kMaxLayersPerLaunch];
+  uint4* dst[kMaxLayersPerLaunch];
+};
+
+// grid = (N pairs, pools in this launch).  Each workgroup copies block src of
+// source pool y to block dst of destination pool y.
+__global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(
+    PoolPairPtrs ptrs, const int64_t* __restrict__ pairs, int64_t block_chunks) {
+  const int64_t src = pairs[2 * (int64_t)blockIdx.x];
+  const int64_t dst = pairs[2 * (int64_t)blockIdx.x + 1];
+  const uint4* s = ptrs.src[blockIdx.y] + src * block_chunks;
+  uint4* d = ptrs.dst[blockIdx.y] + dst * block_chunks;
+  int64_t i = threadIdx.x;
+  for (; i + 3 * kCopyThreads < block_chunks; i += 4 * kCopyThreads) {
+    const uint4 a = s[i], b = s[i + kCopyThreads], c = s[i + 2 * kCopyThreads],
+                e = s[i + 3 * kCopyThreads];
+    d[i] = a;
+    d[i + kCopyThreads] = b;
+    d[i + 2 * kCopyThreads] = c;
+    d[i + 3 * kCopyThreads] = e;
+  }
+  for (; i < block_chunks; i += kCopyThreads) d[i] = s[i];
+}
+
 }  // namespace
+
+pkv_status launch_swap_blocks(const void* const* src_pools, void* const* dst_pools,
+                              int32_t num_pools, const int64_t* pairs, int32_t N,
+                              int64_t block_bytes, hipStream_t stream) {
+  if (N == 0 || num_pools == 0) return PKV_OK;
+  for (int32_t p0 = 0; p0 < num_pools; p0 += kMaxLayersPerLaunch) {
+    const int32_t np = num_pools - p0 < kMaxLayersPerLaunch ? num_pools - p0 : kMaxLayersPerLaunch;
+    PoolPairPtrs ptrs{};
+    for (int32_t i = 0; i < np; ++i) {
+      ptrs.src[i] = static_cast<const uint4*>(src_pools[p0 + i]);
+      ptrs.dst[i] = static_cast<uint4*>(dst_pools[p0 + i]);
+    }
+    hipLaunchKernelGGL(swap_blocks_kernel, dim3(N, np), dim3(kCopyThreads), 0, stream, ptrs, pairs,
+                       block_bytes / 16);
+    pkv_status st = check_launch("swap_blocks");
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
+}
 
 pkv_status launch_reshape_and_cache(const void* key, const void* value, void* k_cache,
                                     void* v_cache, const int64_t* slot_mapping, int32_t T,

@@ -84,6 +84,10 @@ pkv_status launch_reshape_and_cache_fp8(const void* key, const void* value, int 
                                         int32_t T, int32_t Hkv, int32_t D, const float* k_scale,
                                         const float* v_scale, hipStream_t stream);
 
+pkv_status launch_swap_blocks(const void* const* src_pools, void* const* dst_pools,
+                              int32_t num_pools, const int64_t* pairs, int32_t N,
+                              int64_t block_bytes, hipStream_t stream);
+
 pkv_status launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
                               const int64_t* pairs, int32_t N, int64_t block_bytes,
                               hipStream_t stream);

@@ -177,3 +177,110 @@ def test_slots_follow_table():
 def test_bad_free_order_rejected():
     with pytest.raises(pkv.PkvError):
         pkv.BlockManager(4, 4, free_order=[0, 1, 1, 2])
+
+
+# ---------------------------------------------------------------- swapping (CS349D lecture 3 sec. 5.2)
+def test_swap_out_and_in_round_trip():
+    bm = pkv.BlockManager(10, 4)
+    bm.set_cpu_blocks(6)
+    a = bm.add_seq(9)
+    b = bm.fork(a)                       # a's 3 blocks shared with b
+    table_a = bm.table(a)
+    out = bm.swap_out(a)
+    assert out[:, 0].tolist() == table_a and len(set(out[:, 1].tolist())) == 3
+    assert bm.num_free() == 7 and bm.num_free_cpu() == 3    # shared blocks stay with b
+    assert all(bm.refcount(x) == 1 for x in table_a)
+    bm.check()
+    back = bm.swap_in(a)
+    assert back[:, 0].tolist() == out[:, 1].tolist()
+    assert bm.table(a) == back[:, 1].tolist() and bm.seq_len(a) == 9
+    assert bm.num_free() == 4 and bm.num_free_cpu() == 6
+    bm.check()
+    bm.free_seq(a)
+    bm.free_seq(b)
+    assert bm.num_free() == 10
+    bm.check()
+
+
+def test_swap_frees_unshared_blocks_and_swapped_sequence_is_frozen():
+    bm = pkv.BlockManager(8, 4)
+    bm.set_cpu_blocks(8)
+    a = bm.add_seq(10)
+    out = bm.swap_out(a)
+    assert len(out) == 3 and bm.num_free() == 8
+    for op in (lambda: bm.table(a), lambda: bm.append_token(a), lambda: bm.fork(a),
+               lambda: bm.slots(a, 0, 1), lambda: bm.swap_out(a)):
+        with pytest.raises(pkv.PkvError, match="INVALID_ARG"):
+            op()
+    assert bm.seq_len(a) == 10
+    with pytest.raises(pkv.PkvError, match="INVALID_ARG"):
+        bm.set_cpu_blocks(4)             # not while a sequence is swapped out
+    bm.free_seq(a)                       # returns the CPU blocks
+    assert bm.num_free_cpu() == 8
+    bm.check()
+
+
+def test_swap_oom_changes_nothing():
+    bm = pkv.BlockManager(6, 4)
+    bm.set_cpu_blocks(2)
+    a = bm.add_seq(12)                   # 3 blocks > 2 CPU blocks
+    with pytest.raises(pkv.PkvOOM):
+        bm.swap_out(a)
+    assert bm.num_free() == 3 and bm.num_free_cpu() == 2 and len(bm.table(a)) == 3
+    bm.set_cpu_blocks(3)
+    bm.swap_out(a)
+    b = bm.add_seq(20)                   # takes 5 of the 6 GPU blocks
+    with pytest.raises(pkv.PkvOOM):
+        bm.swap_in(a)                    # needs 3, 1 free
+    assert bm.num_free() == 1 and bm.num_free_cpu() == 0
+    bm.free_seq(b)
+    bm.swap_in(a)
+    bm.check()
+
+
+def test_random_beam_search_with_swapping_keeps_invariants():
+    """Beam-search-like churn: forks, frees, appends (with copy-on-write),
+    swaps out and in, against a Python model of the free counts."""
+    rng = np.random.default_rng(21)
+    NB, NC, B = 64, 48, 4
+    bm = pkv.BlockManager(NB, B, rng.permutation(NB).astype(np.int32))
+    bm.set_cpu_blocks(NC)
+    live, swapped = [], set()
+    for step in range(1500):
+        op = rng.integers(0, 6)
+        try:
+            if op == 0 or not live:
+                live.append(bm.add_seq(int(rng.integers(1, 20))))
+            elif op == 1:
+                s = live[rng.integers(len(live))]
+                if s not in swapped:
+                    live.append(bm.fork(s))
+            elif op == 2:
+                s = live.pop(rng.integers(len(live)))
+                bm.free_seq(s)
+                swapped.discard(s)
+            elif op == 3:
+                s = live[rng.integers(len(live))]
+                if s not in swapped:
+                    bm.append_token(s)
+            elif op == 4:
+                s = live[rng.integers(len(live))]
+                if s not in swapped:
+                    bm.swap_out(s)
+                    swapped.add(s)
+            else:
+                if swapped:
+                    s = sorted(swapped)[rng.integers(len(swapped))]
+                    bm.swap_in(s)
+                    swapped.discard(s)
+        except pkv.PkvOOM:
+            pass
+        bm.check()
+        # model: free GPU blocks = NB - distinct blocks of resident sequences
+        held = set()
+        for s in live:
+            if s not in swapped:
+                held.update(bm.table(s))
+        assert bm.num_free() == NB - len(held)
+        ncpu = sum(-(-bm.seq_len(s) // B) for s in swapped)
+        assert bm.num_free_cpu() == NC - ncpu
