@@ -124,10 +124,16 @@ def main():
         def free(self):
             del self.k, self.v
 
-    def time_fn(fn, iters, warm=3):
-        """Mean ms of fn() over iters launches, HIP events on the current stream."""
-        for _ in range(warm):
+    def time_fn(fn, iters, warm=3, warm_ms=300.0):
+        """Mean ms of fn() over iters launches, HIP events on the current stream,
+        after at least `warm` untimed launches and `warm_ms` of back-to-back work
+        (the clocks take tens of milliseconds of load to settle)."""
+        t0, n = time.time(), 0
+        while n < warm or (time.time() - t0) * 1e3 < warm_ms:
             fn()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
         s = torch.cuda.current_stream()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(iters)]
@@ -184,7 +190,7 @@ def main():
         """Chunked causal prefill of 8 sequences x 512 new tokens (bf16)."""
         pb = W.prefill_bf16(args.seed)
         pd = Dev(pb)
-        ms, _ = time_fn(pd.prefill, 5, warm=2)
+        ms, _ = time_fn(pd.prefill, 10)
         flops = 0
         for s in range(pb.S):
             Q = int(pb.cu_seqlens_q[s + 1] - pb.cu_seqlens_q[s])

@@ -527,11 +527,25 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
 #pragma unroll
         for (int kk = 0; kk < NLD; ++kk) kb[kk] = ldkv(kpool + base + koff + kk * 4 * LB);
       }
+      if constexpr (F8) {
+        // FP8 V goes through LDS, so its load layout is free: two 16-byte
+        // loads per lane, lane (row, col) taking codes 16 (col % 8) .. + 15 of
+        // token 8 j + 2 row + col / 8 (whole 128-byte rows per 8 lanes)
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int tv = min(ts + 4 * row + i, c.L - 1);
-        const unsigned voff = (unsigned)((tv & bmask) * row_stride32 + kvoff + col * LB);
-        vb[i] = ldkv(vpool + base + voff);
+        for (int jv = 0; jv < 2; ++jv) {
+          const int tv = min(ts + 8 * jv + 2 * row + (col >> 3), c.L - 1);
+          const unsigned voff = (unsigned)((tv & bmask) * row_stride32 + kvoff + (col & 7) * 16);
+          const uint4 v4 = ld16_stream(vpool + base + voff);
+          vb[2 * jv] = make_uint2(v4.x, v4.y);
+          vb[2 * jv + 1] = make_uint2(v4.z, v4.w);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          const int tv = min(ts + 4 * row + i, c.L - 1);
+          const unsigned voff = (unsigned)((tv & bmask) * row_stride32 + kvoff + col * LB);
+          vb[i] = ldkv(vpool + base + voff);
+        }
       }
     } else if constexpr (UNI) {
 #pragma unroll
@@ -667,9 +681,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs
       const uint2 pl = make_uint2(pack2<DT>(p[0] - half_lo<DT>(h01), p[1] - half_hi<DT>(h01)),
                                   pack2<DT>(p[2] - half_lo<DT>(h23), p[3] - half_hi<DT>(h23)));
       // (the wave's own LDS rows, written and read in order by this wave only)
+      if constexpr (F8) {
 #pragma unroll
-      for (int i = 0; i < NLD; ++i)
-        *reinterpret_cast<uint4*>(vs + (4 * row + i) * kVP + col * 16) = kfrag(vb[i]);
+        for (int jv = 0; jv < 2; ++jv) {
+          char* dst = vs + (8 * jv + 2 * row + (col >> 3)) * kVP + (col & 7) * 32;
+          *reinterpret_cast<uint4*>(dst) = kfrag(vb[2 * jv]);
+          *reinterpret_cast<uint4*>(dst + 16) = kfrag(vb[2 * jv + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+          *reinterpret_cast<uint4*>(vs + (4 * row + i) * kVP + col * 16) = kfrag(vb[i]);
+      }
       const char* vrd = vs + (4 * row + (col >> 2)) * kVP + (col & 3) * 8;
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {

@@ -327,25 +327,33 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
 // Tile kernel (16-bit KV, block size >= 16): both products on the 16x16x32
 // matrix cores with the query row in lane % 16 throughout.
 //
-//  * Workgroup = 4 waves x QB x 16 query rows of one (sequence, KV head); a row
+//  * Workgroup = 4 waves x 2 x 16 query rows of one (sequence, KV head); a row
 //    is a (token, query head of the group) pair, so the G heads sharing a KV
 //    head share every K/V tile.
-//  * Per 32-token KV tile, all 256 threads stage K and V rows (16-byte loads,
-//    the tile's one or two blocks looked up a tile ahead) into LDS,
-//    double buffered; the loads of tile j + 2 (and the table entries of tile
-//    j + 3) are in flight while tile j is computed.  Rows past the context are
-//    clamped to the last visible row.
-//  * S^T = K Q^T: K (A operand, row-major from LDS, 16-byte reads over a
-//    4-bank row skew) times Q^T (B operand, in registers for the whole loop).
-//    Lane (g, n) receives S[kv = 4g + i (+16)][q = n].
+//  * Per 32-token KV tile, all 256 threads stage K and V rows into LDS with
+//    16-byte loads.  A wave's rows of one staging chunk lie in one 16-token
+//    half of the tile, hence in one block: the address is a per-wave block
+//    base (from the table entry, fetched one step ahead) plus a per-lane
+//    offset; only the last tile clamps rows past the context to its last one.
+//  * S^T = K Q^T: K (A operand, row-major from LDS, 16-byte reads) times Q^T
+//    (B operand, in registers for the whole loop).  Lane (g, n) receives
+//    S[kv = 4g + i (+16)][q = n].  Scores stay raw; the softmax scale enters
+//    the exponent through one fma (a negative scale flips q's sign instead).
 //  * Online softmax per lane (its query row), max across the four lane groups
 //    with permlane swaps; lazy rescale (only when the max grows by 2^8).
 //  * O^T += V^T P^T: V^T is the A operand, read from row-major LDS with the
-//    gfx950 transposing read ds_read_b64_tr_b16 (8-bank row skew, conflict
-//    free); P^T is the B operand straight from the score registers.  Both use
-//    the same order of the 32 tile tokens (4g + k, then 16 + 4g + k), so the
-//    product over them is unchanged.  bf16: P is split into hi + lo bf16 parts
-//    (two MFMAs), keeping ~16 significant bits of the weights.
+//    gfx950 transposing read ds_read_b64_tr_b16; P^T is the B operand straight
+//    from the score registers.  Both use the same order of the 32 tile tokens
+//    (4g + k, then 16 + 4g + k), so the product over them is unchanged.  bf16:
+//    P is split into hi + lo bf16 parts (two MFMAs), keeping ~16 significant
+//    bits of the weights.
+//  * Software pipeline: in the step for tile j the matrix cores run
+//    O += P(j-1) V(j-1) and S(j+1) = Q K(j+1)^T while the vector ALU runs the
+//    softmax of S(j), all three independent, so each wave's instruction
+//    stream interleaves matrix and vector work.  K runs two tiles ahead of V
+//    in the LDS double buffers; one barrier per step.
+//  * LDS rows carry 32 bytes of skew, which makes the K reads, the
+//    transposing V reads and the staging writes conflict free.
 //  * Workgroups of one (sequence, KV head) are mapped to the same XCD.
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -354,6 +362,7 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kTileKV = 32;                 // KV tokens per tile
 constexpr int kWaitLgkm0 = 0xC07F;          // s_waitcnt: LDS/scalar count 0, others at max
+constexpr int kTileQB = 2;                  // q blocks of 16 rows per wave
 
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma16(const u32x4_t a, const u32x4_t b, f32x4_t c) {
@@ -395,18 +404,43 @@ __device__ __forceinline__ void pair_sum(float& x) {
   }
 }
 
-template <int DT, int D, int QB>
-__global__ __launch_bounds__(kThreads) void prefill_tile_kernel(const PrefillArgs a) {
+// Maximum of three fp32 values in one instruction.  Written as asm because
+// fmaxf on matrix-core results is preceded by a canonicalising v_max(x, x)
+// per operand (IEEE mode); no NaN reaches these maxima except through an
+// input that is NaN already, and then the row is NaN either way.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// Row max across the four lane groups (lanes n, n + 16, n + 32, n + 48).
+__device__ __forceinline__ float group_max_raw(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = max3_raw(__uint_as_float(r16[0]), __uint_as_float(r16[1]), __uint_as_float(r16[0]));
+  const unsigned w = __float_as_uint(y);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return max3_raw(__uint_as_float(r32[0]), __uint_as_float(r32[1]), __uint_as_float(r32[0]));
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_tile_kernel(
+    const PrefillArgs a) {
+  constexpr int QB = kTileQB;
   constexpr int ES = 2;
   constexpr int NKK = D / 32;                 // k-steps of S^T = K Q^T
   constexpr int NDB = D / 16;                 // 16-wide d blocks of O^T
-  constexpr int KP = D * ES + 16;             // K row pitch in LDS: 4-bank skew
-  constexpr int VP = D * ES + 32;             // V row pitch in LDS: 8-bank skew
+  // LDS row pitches: 32 bytes of skew per row make both the 16-byte K reads
+  // and the transposing V reads conflict free (measured: a 16-byte skew
+  // costs the K reads 1.6x)
+  constexpr int KP = D * ES + 32;
+  constexpr int VP = D * ES + 32;
   constexpr int CPR = D * ES / 16;            // 16-byte chunks per row
   constexpr int NCH = kTileKV * CPR / kThreads;  // chunks per thread per tile, K and V each
   constexpr int RW = kWaves * 16 * QB;        // query rows per workgroup
   constexpr bool PSPLIT = DT == DT_BF16;
   static_assert(NCH >= 1 && kTileKV * CPR % kThreads == 0, "staging split");
+  static_assert(16 % (64 / CPR) == 0, "a wave's staged rows must lie in one 16-token half");
 
   __shared__ __attribute__((aligned(16))) char lk[2][kTileKV * KP];
   __shared__ __attribute__((aligned(16))) char lv[2][kTileKV * VP];
@@ -458,7 +492,13 @@ __global__ __launch_bounds__(kThreads) void prefill_tile_kernel(const PrefillArg
   pos_min = __builtin_amdgcn_readfirstlane(pos_min);
 
   const int kv_end = L - Qs + min(tq0 + TQ, Qs);  // tokens any row of the workgroup sees
-  const int ntiles = (kv_end + kTileKV - 1) / kTileKV;
+  const int ntiles = (kv_end + kTileKV - 1) / kTileKV;  // >= 1 here
+
+  // Scores are kept as raw q.k; the softmax scale enters the exponent through
+  // one fma.  A negative scale flips the sign of q instead (exact for 16-bit
+  // values), so the factor used is |scale| and the running max stays a max.
+  const float sl = fabsf(a.scale_log2);
+  const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // Q^T fragments: lane holds Q[row][32 kk + 8 g4 .. + 7]
   u32x4_t qf[QB][NKK];
@@ -467,10 +507,10 @@ __global__ __launch_bounds__(kThreads) void prefill_tile_kernel(const PrefillArg
     const char* qp = static_cast<const char*>(a.q) + ((int64_t)orow[c] * D + 8 * g4) * ES;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      qf[c][kk] = valid[c] ? as_v(ld16(qp + kk * 64)) : u32x4_t{0, 0, 0, 0};
+      qf[c][kk] = valid[c] ? (as_v(ld16(qp + kk * 64)) ^ qflip) : u32x4_t{0, 0, 0, 0};
   }
   // q must have landed before the loop: left pending, the loop header (where
-  // the entry path meets the back edge) would wait for every load each tile
+  // the entry path meets the back edge) would wait for every load each step
 #pragma unroll
   for (int c = 0; c < QB; ++c)
 #pragma unroll
@@ -483,45 +523,55 @@ __global__ __launch_bounds__(kThreads) void prefill_tile_kernel(const PrefillArg
   const int bmask = a.B - 1;
   const char* kpool = static_cast<const char*>(a.k_cache) + (int64_t)kvh * D * ES;
   const char* vpool = static_cast<const char*>(a.v_cache) + (int64_t)kvh * D * ES;
-
-  // Table entries of a tile's one or two blocks, fetched a tile ahead through
-  // the vector queue (lane 0: first block, lane 1: second block) so their
-  // latency hides behind a whole tile instead of stalling the K/V loads.
   const int32_t* tbv = a.block_tables + (int64_t)s * a.max_nb;
-  int ent = 0;
-  auto ent_issue = [&](int j) __attribute__((always_inline)) {
-    const int kv0 = j * kTileKV;
-    const int idx = (lane & 1) ? min(kv0 + 16, kv_end - 1) >> log2B : kv0 >> log2B;
-    ent = tbv[idx];
-  };
-  // global -> registers for tile j (entries from ent_issue(j))
-  uint4 sk[NCH], sv[NCH];
-  auto gload = [&](int j) __attribute__((always_inline)) {
-    const int kv0 = j * kTileKV;
-    const int b0 = kv0 >> log2B;
-    const int64_t e0 = __builtin_amdgcn_readlane(ent, 0);
-    const int64_t e1 = __builtin_amdgcn_readlane(ent, 1);
+
+  // Staging: chunk i of a thread is 16 bytes at column ch % CPR of tile row
+  // ch / CPR (ch = tid + 256 i).  The rows a wave stages for one chunk lie in
+  // one 16-token half of the tile, and a half lies in one block (B >= 16), so
+  // a chunk's pool address is a per-wave base plus a per-lane offset.
+  int crow[NCH], ccol[NCH], chalf[NCH];
+  uint32_t loff[NCH];
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int ch = tid + kThreads * i;
-      const int row = ch / CPR;
-      const int col = ch - row * CPR;
-      const int kvc = min(kv0 + row, kv_end - 1);
-      const int64_t base = ((kvc >> log2B) == b0 ? e0 : e1) * blk_stride;
-      const unsigned off = (unsigned)((kvc & bmask) * rs32 + col * 16);
-      sk[i] = ld16(kpool + base + off);
-      sv[i] = ld16(vpool + base + off);
+  for (int i = 0; i < NCH; ++i) {
+    const int ch = tid + kThreads * i;
+    crow[i] = ch / CPR;
+    ccol[i] = ch - crow[i] * CPR;
+    chalf[i] = __builtin_amdgcn_readfirstlane(crow[i] >> 4);
+    loff[i] = (uint32_t)((crow[i] & 15) * rs32 + ccol[i] * 16);
+  }
+  // Block table entries of tile t: lane 0 the block of its first 16 tokens,
+  // lane 1 of the next 16 (clamped to the last visible token, so the table is
+  // never read past the sequence's blocks).
+  auto ent_load = [&](int t) __attribute__((always_inline)) -> int {
+    const int kv = min(t * kTileKV + 16 * (lane & 1), kv_end - 1);
+    return tbv[kv >> log2B];
+  };
+  // global -> registers: the chunks of tile t (entries e0, e1 of its halves).
+  // Rows past the visible range (last tile only) repeat its last row.
+  auto gload = [&](uint4 (&dst)[NCH], const char* pool, int t, int e0, int e1)
+      __attribute__((always_inline)) {
+    const int kv0 = t * kTileKV;
+    if (kv0 + kTileKV <= kv_end) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int h = chalf[i];
+        const char* base = pool + (int64_t)(h ? e1 : e0) * blk_stride +
+                           (int64_t)(((kv0 + 16 * h) & bmask) * rs32);
+        dst[i] = ld16(base + loff[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int h = chalf[i];
+        const int kvc = min(kv0 + crow[i], kv_end - 1);
+        const char* base = pool + (int64_t)(h ? e1 : e0) * blk_stride;
+        dst[i] = ld16(base + (uint32_t)((kvc & bmask) * rs32 + ccol[i] * 16));
+      }
     }
   };
-  auto lstore = [&](int buf) __attribute__((always_inline)) {
+  auto lstore = [&](char* buf, int pitch, const uint4 (&src)[NCH]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int ch = tid + kThreads * i;
-      const int row = ch / CPR;
-      const int col = ch - row * CPR;
-      *reinterpret_cast<uint4*>(&lk[buf][row * KP + col * 16]) = sk[i];
-      *reinterpret_cast<uint4*>(&lv[buf][row * VP + col * 16]) = sv[i];
-    }
+    for (int i = 0; i < NCH; ++i) *reinterpret_cast<uint4*>(buf + crow[i] * pitch + ccol[i] * 16) = src[i];
   };
   // LDS writes of this thread are complete and every wave has arrived; global
   // loads already issued stay in flight (no memory fence on the barrier)
@@ -544,116 +594,190 @@ __global__ __launch_bounds__(kThreads) void prefill_tile_kernel(const PrefillArg
     lsum[c] = 0.f;
   }
 
-  if (ntiles > 0) {
-    ent_issue(0);
-    gload(0);
-    lstore(0);
-    if (ntiles > 1) {
-      ent_issue(1);
-      gload(1);
-      if (ntiles > 2) ent_issue(2);
-    }
+  // Software pipeline over KV tiles.  Step j (j = -1 .. ntiles):
+  //   1. stage K(j+2) and V(j) into LDS (loaded during step j-1), then issue
+  //      the loads of K(j+3) and V(j+1) and of the table entries of tile j+4;
+  //   2. matrix cores: O^T += V(j-1)^T P(j-1)^T and S(j+1)^T = K(j+1) Q^T;
+  //   3. vector ALU, independent of 2: softmax of S(j) into P(j);
+  //   4. rare: rescale O when some row's max grew; barrier.
+  // So the softmax of one tile runs while the matrix cores work on the tiles
+  // on either side of it.  K(t) sits in LDS buffer t % 2 during steps t-2 ..
+  // t-1, V(t) in buffer t % 2 during steps t .. t+1.  Tile indices past the
+  // last tile are clamped to it (their loads repeat it and are never used).
+  uint4 sk[NCH], sv[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) sv[i] = make_uint4(0, 0, 0, 0);
+  int ea0, ea1, eb0, eb1, ent;  // entries of tiles j+1 and j+2; vector of tile j+3
+  const int tl = ntiles - 1;
+  {
+    const int en0 = ent_load(0);
+    const int en1 = ent_load(min(1, tl));
+    ent = ent_load(min(2, tl));
+    ea0 = __builtin_amdgcn_readlane(en0, 0);
+    ea1 = __builtin_amdgcn_readlane(en0, 1);
+    eb0 = __builtin_amdgcn_readlane(en1, 0);
+    eb1 = __builtin_amdgcn_readlane(en1, 1);
   }
+  gload(sk, kpool, 0, ea0, ea1);
+  lstore(lk[0], KP, sk);
+  gload(sk, kpool, min(1, tl), eb0, eb1);
   lds_barrier();
 
-  // one KV tile; MASK: some token of the tile lies after some row's position
-  auto tile = [&](const int j, auto mask_tag) __attribute__((always_inline)) {
+  f32x4_t SA[2][QB], SB[2][QB];   // S of the tile being softmaxed / of the next one
+  u32x4_t PAh[QB], PAl[QB], PBh[QB], PBl[QB];  // P of the previous tile / of this one
+
+  auto step = [&](const int j, auto ld_tag, auto pv_tag, auto qk_tag, auto sm_tag, auto mask_tag,
+                  f32x4_t (&s_cur)[2][QB], f32x4_t (&s_nxt)[2][QB], const u32x4_t (&pph)[QB],
+                  const u32x4_t (&ppl)[QB], u32x4_t (&nph)[QB], u32x4_t (&npl)[QB])
+      __attribute__((always_inline)) {
+    constexpr bool LD = decltype(ld_tag)::value;
+    constexpr bool PV = decltype(pv_tag)::value;
+    constexpr bool QK = decltype(qk_tag)::value;
+    constexpr bool SM = decltype(sm_tag)::value;
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int buf = j & 1;
-    const int kv0 = j * kTileKV;
-    const char* K = lk[buf];
-    const char* V = lv[buf];
-    // S^T blocks: st[mb][c] holds S[kv0 + 16 mb + 4 g4 + i][q col n of block c]
-    f32x4_t st[2][QB];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int c = 0; c < QB; ++c) st[mb][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const u32x4_t ka = as_v(*reinterpret_cast<const uint4*>(K + (16 * mb + n) * KP + 64 * kk + 16 * g4));
-#pragma unroll
-        for (int c = 0; c < QB; ++c) st[mb][c] = mfma16<DT>(ka, qf[c][kk], st[mb][c]);
-      }
+    if constexpr (LD) {
+      lstore(lk[j & 1], KP, sk);
+      lstore(lv[j & 1], VP, sv);
+      const int ec0 = __builtin_amdgcn_readlane(ent, 0);
+      const int ec1 = __builtin_amdgcn_readlane(ent, 1);
+      ent = ent_load(min(j + 4, tl));
+      gload(sk, kpool, min(j + 3, tl), ec0, ec1);
+      gload(sv, vpool, min(j + 1, tl), ea0, ea1);
+      ea0 = eb0;
+      ea1 = eb1;
+      eb0 = ec0;
+      eb1 = ec1;
     }
-    u32x4_t ph[QB], pl[QB];
-    bool grow_any = false;
-    float sc[QB][8], mnew[QB];
-#pragma unroll
-    for (int c = 0; c < QB; ++c) {
-      float t = -__builtin_inff();
+    if constexpr (QK) {
+      // S^T blocks: s_nxt[mb][c] holds S[16 mb + 4 g4 + i][q col n of block c]
+      const char* K = lk[(j + 1) & 1];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = st[mb][c][i] * a.scale_log2;
-          if constexpr (MASK) {
-            const int kv = kv0 + 16 * mb + 4 * g4 + i;
-            v = kv <= pos[c] ? v : -__builtin_inff();
-          }
-          sc[c][4 * mb + i] = v;
-          t = fmaxf(t, v);
+        for (int c = 0; c < QB; ++c) s_nxt[mb][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const u32x4_t ka = as_v(*reinterpret_cast<const uint4*>(K + (16 * mb + n) * KP + 64 * kk + 16 * g4));
+#pragma unroll
+          for (int c = 0; c < QB; ++c) s_nxt[mb][c] = mfma16<DT>(ka, qf[c][kk], s_nxt[mb][c]);
         }
       }
-      pair_max<16>(t);
-      pair_max<32>(t);
-      mnew[c] = fmaxf(m[c], t);
-      grow_any |= mnew[c] > m[c] + kRescaleThreshold;
     }
-    if (__builtin_amdgcn_ballot_w64(grow_any)) {
+    if constexpr (PV) {
+      // O^T += V^T P^T: A = V^T rows d0 + n, tokens 4 g4 + k and 16 + 4 g4 + k
+      const char* V = lv[(j - 1) & 1];
 #pragma unroll
-      for (int c = 0; c < QB; ++c) {
-        const bool grow = mnew[c] > m[c] + kRescaleThreshold;
-        const float alpha = grow ? fast_exp2(m[c] - mnew[c]) : 1.f;
+      for (int d = 0; d < NDB; ++d) {
+        const char* vp = V + (4 * g4 + (n >> 2)) * VP + (16 * d + 4 * (n & 3)) * ES;
+        const uint2 lo = lds_read_tr16(vp);
+        const uint2 hi = lds_read_tr16(vp + 16 * VP);
+        const u32x4_t va = u32x4_t{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-        for (int d = 0; d < NDB; ++d) o[d][c] *= alpha;
-        lsum[c] *= alpha;
-        m[c] = grow ? mnew[c] : m[c];
+        for (int c = 0; c < QB; ++c) {
+          o[d][c] = mfma16<DT>(va, pph[c], o[d][c]);
+          if constexpr (PSPLIT) o[d][c] = mfma16<DT>(va, ppl[c], o[d][c]);
+        }
       }
     }
+    if constexpr (SM) {
+      const int kv0 = j * kTileKV;
+      float alpha[QB];
+      bool grow_any = false;
+#pragma unroll
+      for (int c = 0; c < QB; ++c) {
+        float r[8];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = s_cur[mb][c][i];
+            if constexpr (MASK) v = kv0 + 16 * mb + 4 * g4 + i <= pos[c] ? v : -__builtin_inff();
+            r[4 * mb + i] = v;
+          }
+        const float t = group_max_raw(
+            max3_raw(max3_raw(r[0], r[1], r[2]), max3_raw(r[3], r[4], r[5]), max3_raw(r[6], r[7], r[7])));
+        const float mn = fmaxf(m[c], t * sl);
+        const bool grow = mn > m[c] + kRescaleThreshold;
+        alpha[c] = grow ? fast_exp2(m[c] - mn) : 1.f;
+        m[c] = grow ? mn : m[c];
+        grow_any |= grow;
+        const float mu = m[c] == -__builtin_inff() ? 0.f : m[c];
+        float rs = 0.f;
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) {
+          float p0 = fast_exp2(__builtin_fmaf(r[k], sl, -mu));
+          float p1 = fast_exp2(__builtin_fmaf(r[k + 1], sl, -mu));
+          if constexpr (MASK) {
+            const int kv = kv0 + 16 * (k >> 2) + 4 * g4 + (k & 3);
+            p0 = kv <= pos[c] ? p0 : 0.f;
+            p1 = kv + 1 <= pos[c] ? p1 : 0.f;
+          }
+          rs += p0 + p1;
+          const uint32_t h = pack2<DT>(p0, p1);
+          hw[k / 2] = h;
+          if constexpr (PSPLIT) lw[k / 2] = pack2<DT>(p0 - lo16<DT>(h), p1 - hi16<DT>(h));
+        }
+        nph[c] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+        if constexpr (PSPLIT) npl[c] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+        lsum[c] = lsum[c] * alpha[c] + rs;
+      }
+      // keep the weights' computation here, beside the matrix-core work it
+      // overlaps (else it sinks past the rescale branch below)
+#pragma unroll
+      for (int c = 0; c < QB; ++c) {
+        asm volatile("" ::"v"(nph[c]), "v"(lsum[c]));
+        if constexpr (PSPLIT) asm volatile("" ::"v"(npl[c]));
+      }
+      // O now includes P(j-1) V(j-1): bring it to the new max
+      if (__builtin_amdgcn_ballot_w64(grow_any)) {
+#pragma unroll
+        for (int d = 0; d < NDB; ++d)
+#pragma unroll
+          for (int c = 0; c < QB; ++c) o[d][c] *= alpha[c];
+      }
+    }
+    if constexpr (LD) lds_barrier();
+  };
+  using T = BoolTag<true>;
+  using F = BoolTag<false>;
+  auto copy_back = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < QB; ++c) {
-      const float mu = m[c] == -__builtin_inff() ? 0.f : m[c];
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int k = 0; k < 8; k += 2) {
-        const float p0 = fast_exp2(sc[c][k] - mu);
-        const float p1 = fast_exp2(sc[c][k + 1] - mu);
-        lsum[c] += p0 + p1;
-        const uint32_t h = pack2<DT>(p0, p1);
-        hw[k / 2] = h;
-        if constexpr (PSPLIT) lw[k / 2] = pack2<DT>(p0 - lo16<DT>(h), p1 - hi16<DT>(h));
-      }
-      ph[c] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-      if constexpr (PSPLIT) pl[c] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+      SA[0][c] = SB[0][c];
+      SA[1][c] = SB[1][c];
+      PAh[c] = PBh[c];
+      if constexpr (PSPLIT) PAl[c] = PBl[c];
     }
-    // O^T += V^T P^T: A = V^T rows d0 + n, tokens 4 g4 + k and 16 + 4 g4 + k
-#pragma unroll
-    for (int d = 0; d < NDB; ++d) {
-      const char* vp = V + (4 * g4 + (n >> 2)) * VP + (16 * d + 4 * (n & 3)) * ES;
-      const uint2 lo = lds_read_tr16(vp);
-      const uint2 hi = lds_read_tr16(vp + 16 * VP);
-      const u32x4_t va = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-      for (int c = 0; c < QB; ++c) {
-        o[d][c] = mfma16<DT>(va, ph[c], o[d][c]);
-        if constexpr (PSPLIT) o[d][c] = mfma16<DT>(va, pl[c], o[d][c]);
-      }
-    }
-    if (j + 1 < ntiles) {
-      lstore(buf ^ 1);
-      if (j + 2 < ntiles) {
-        gload(j + 2);
-        if (j + 3 < ntiles) ent_issue(j + 3);
-      }
-    }
-    lds_barrier();
   };
-  // tiles wholly at or before every row's position need no causal mask (a
-  // wave without valid rows has pos_min = INT_MAX: no tile needs it)
-  const int nfree = pos_min == 0x7fffffff ? ntiles : min(ntiles, (pos_min + 1) / kTileKV);
-  for (int j = 0; j < nfree; ++j) tile(j, BoolTag<false>{});
-  for (int j = nfree; j < ntiles; ++j) tile(j, BoolTag<true>{});
+
+  // step -1: S(0) into SB; step 0: softmax(0), S(1) into SA, P(0) into PA
+  step(-1, T{}, F{}, T{}, F{}, F{}, SA, SB, PAh, PAl, PBh, PBl);
+  step(0, T{}, F{}, T{}, T{}, T{}, SB, SA, PBh, PBl, PAh, PAl);
+  if (ntiles >= 2) {
+    // steady state, unrolled by two so S and P alternate between the A and B
+    // registers; tiles wholly at or before every row's position skip the mask
+    const int nfree = pos_min == 0x7fffffff ? tl : max(1, min(tl, (pos_min + 1) / kTileKV));
+    int j = 1;
+    for (; j + 1 < nfree; j += 2) {
+      step(j, T{}, T{}, T{}, T{}, F{}, SA, SB, PAh, PAl, PBh, PBl);
+      step(j + 1, T{}, T{}, T{}, T{}, F{}, SB, SA, PBh, PBl, PAh, PAl);
+    }
+    if (j < nfree) {
+      step(j, T{}, T{}, T{}, T{}, F{}, SA, SB, PAh, PAl, PBh, PBl);
+      copy_back();
+      ++j;
+    }
+    for (; j < tl; ++j) {
+      step(j, T{}, T{}, T{}, T{}, T{}, SA, SB, PAh, PAl, PBh, PBl);
+      copy_back();
+    }
+    // last tile: no next S; P(tl) into PB, then its product
+    step(tl, T{}, T{}, F{}, T{}, T{}, SA, SB, PAh, PAl, PBh, PBl);
+    step(tl + 1, F{}, T{}, F{}, F{}, F{}, SA, SB, PBh, PBl, PAh, PAl);
+  } else {
+    step(1, F{}, T{}, F{}, F{}, F{}, SA, SB, PAh, PAl, PBh, PBl);
+  }
 
   // total weight of each row (the four lane groups hold different tokens)
 #pragma unroll
@@ -749,8 +873,6 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillArgs a) {
   }
 }
 
-constexpr int kTileQB = 2;  // q blocks of 16 rows per wave in the tile kernel
-
 template <int DT, int D>
 pkv_status launch_tile(const PrefillArgs& a, hipStream_t stream) {
   constexpr int RW = kWaves * 16 * kTileQB;
@@ -760,7 +882,7 @@ pkv_status launch_tile(const PrefillArgs& a, hipStream_t stream) {
   const int64_t grid = nqt * a.S * a.Hkv;
   if (grid == 0) return PKV_OK;
   if (grid > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "prefill grid too large");
-  hipLaunchKernelGGL((prefill_tile_kernel<DT, D, kTileQB>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((prefill_tile_kernel<DT, D>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, a);
   return check_launch("paged_attention_prefill");
 }

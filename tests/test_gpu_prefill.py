@@ -97,3 +97,24 @@ def test_prefill_full_size_sampled(gpu_lib):
     rng = np.random.default_rng(1)
     rows = sorted(set([0, 511, 4095, 2048] + rng.choice(b.q.shape[0], 12, replace=False).tolist()))
     check(gpu_lib, b, rows=rows)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D,B", [(128, 16), (64, 32), (128, 32)])
+def test_pipeline_depths(gpu_lib, dtype, D, B):
+    """Contexts from one KV tile to nine (odd and even step counts of the
+    tile pipeline), chunks that start on, before and after a tile boundary,
+    and a last tile that is full, nearly empty or one token."""
+    prior = [0, 0, 16, 33, 64, 95, 130, 200, 31, 255]
+    chunks = [1, 32, 16, 31, 33, 64, 62, 88, 2, 33]
+    check(gpu_lib, W.varlen_prefill(D + B + 3, prior, chunks, 32, 8, D, B, dtype))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.35])
+def test_scale_sign_and_zero(gpu_lib, dtype, scale):
+    """A negative softmax scale (the kernel flips q's sign and uses |scale|),
+    a zero scale (uniform weights over the visible tokens) and a large one."""
+    b = W.varlen_prefill(77, [0, 40, 300], [20, 70, 45], 16, 4, 128, 16, dtype)
+    b.scale = scale
+    check(gpu_lib, b)
