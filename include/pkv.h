@@ -9,9 +9,8 @@
  *  - Ownership: every pointer is owned by the caller.  Tensor pointers are
  *    DEVICE pointers (hipMalloc'd or torch CUDA tensors on the current device);
  *    the library allocates no device memory and keeps no state beyond a
- *    thread-local error string, the host block managers the caller creates,
- *    and one auxiliary stream with two events per device that the mixed-batch
- *    call creates on first use.
+ *    thread-local error string, the host block managers the caller creates
+ *    and a per-device cache of the CU count.
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  *    stream).  Kernel calls are asynchronous on that stream.
  *  - Errors: scalar arguments are validated on the host before any launch; a
@@ -226,11 +225,23 @@ pkv_status pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype, const 
  *   max_query_len  : host bound >= every chunk length
  *   context_lens   : device int32 [S]; prior context + chunk, the chunk's K/V
  *                    already written to the cache (pkv_reshape_and_cache)
+ *   workspace      : device scratch of pkv_prefill_workspace_size() bytes
+ *                    (may be NULL when that size is 0)
  * Row i of sequence s sits at position context_lens[s] - Q_s + i and attends
  * to positions 0 .. context_lens[s] - Q_s + i.  kv_dtype f16/bf16 use the
- * matrix cores (16-bit operands, fp32 accumulation; the softmax weights are
- * rounded to kv_dtype before the PV product); f32 uses fp32 vector math.
+ * matrix cores (16-bit operands, fp32 accumulation; the softmax weights enter
+ * the PV product as kv_dtype values, split into two parts for bf16); f32 uses
+ * fp32 vector math.  A call with too few (sequence, KV head, query tile)
+ * units to fill the GPU -- few sequences with long contexts -- splits each
+ * unit's KV range and merges the partial softmax results (log-sum-exp); the
+ * split is a function of the arguments and the device's CU count only, so
+ * equal calls give equal bits.  A workspace smaller than the size query's
+ * answer fails with PKV_ERR_WORKSPACE and launches nothing.
  * ------------------------------------------------------------------------ */
+pkv_status pkv_prefill_workspace_size(int32_t S, int32_t Tq, int32_t max_query_len, int32_t Hq,
+                                      int32_t Hkv, int32_t D, int32_t B, pkv_dtype kv_dtype,
+                                      int32_t max_context_len, size_t* bytes);
+
 pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* q,
                                        const int32_t* cu_seqlens_q, int32_t Tq,
                                        int32_t max_query_len, const void* k_cache,
@@ -238,7 +249,8 @@ pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const voi
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                                        const int32_t* context_lens, int32_t max_context_len,
                                        int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
-                                       float scale, void* stream);
+                                       float scale, void* workspace, size_t workspace_bytes,
+                                       void* stream);
 
 /* ------------------------------------------------------------------------
  * paged_attention_mixed -- one call for a batch mixing decode requests and
@@ -257,14 +269,13 @@ pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const voi
  *                prefill chunks
  *   workspace  : device scratch of pkv_mixed_workspace_size() bytes
  * Every output row equals what pkv_paged_attention_decode (decode rows) or
- * pkv_paged_attention_prefill (chunk rows) give for it, bit for bit.  The two
- * parts run concurrently: the decodes on `stream`, the chunks on a stream the
- * library creates once per device (default priority) and keeps until the
- * process ends, forked from and joined back into `stream` with events, so the
- * call is ordered on `stream` like any other.
+ * pkv_paged_attention_prefill (chunk rows) give for it, bit for bit: the
+ * decode part and then the chunks, on `stream`; chunks too few to fill the
+ * GPU have their KV ranges split as in pkv_paged_attention_prefill.
  * ------------------------------------------------------------------------ */
-pkv_status pkv_mixed_workspace_size(int32_t S, int32_t num_decode, int32_t Hq, int32_t Hkv,
-                                    int32_t D, int32_t B, int32_t max_context_len,
+pkv_status pkv_mixed_workspace_size(int32_t S, int32_t num_decode, int32_t Tq,
+                                    int32_t max_query_len, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t B, pkv_dtype kv_dtype, int32_t max_context_len,
                                     size_t* bytes);
 
 pkv_status pkv_paged_attention_mixed(void* out, pkv_dtype out_dtype, const void* q,

@@ -58,8 +58,9 @@ def load_library(path: str | None = None):
         "pkv_decode_workspace_size": (st, [i32, i32, i32, i32, i32, i32, SZP]),
         "pkv_paged_attention_decode": (st, [P, st, P, P, P, st, P, i32, P, i32, i32, i32, i32, i32,
                                             i32, f32, P, sz, P]),
+        "pkv_prefill_workspace_size": (st, [i32, i32, i32, i32, i32, i32, i32, st, i32, SZP]),
         "pkv_paged_attention_prefill": (st, [P, st, P, P, i32, i32, P, P, st, P, i32, P, i32, i32,
-                                             i32, i32, i32, i32, f32, P]),
+                                             i32, i32, i32, i32, f32, P, sz, P]),
         "pkv_copy_blocks": (st, [P, P, i32, P, i32, i32, i32, i32, st, P]),
         "pkv_swap_blocks": (st, [P, P, i32, P, i32, i32, i32, i32, st, P]),
         "pkv_bm_set_cpu_blocks": (st, [P, i32]),
@@ -67,7 +68,7 @@ def load_library(path: str | None = None):
         "pkv_bm_swap_out": (st, [P, i32, P, i32, I32P]),
         "pkv_bm_swap_in": (st, [P, i32, P, i32, I32P]),
         "pkv_reshape_and_cache_fp8": (st, [P, P, st, P, P, P, i32, i32, i32, i32, i64, P, P, P]),
-        "pkv_mixed_workspace_size": (st, [i32, i32, i32, i32, i32, i32, i32, SZP]),
+        "pkv_mixed_workspace_size": (st, [i32, i32, i32, i32, i32, i32, i32, i32, st, i32, SZP]),
         "pkv_paged_attention_mixed": (st, [P, st, P, P, i32, i32, i32, P, P, st, P, i32, P, i32, i32,
                                            i32, i32, i32, i32, f32, P, sz, P]),
         "pkv_decode_cascade_workspace_size": (st, [i32, i32, i32, i32, i32, i32, i32, i32, i32, st,
@@ -205,10 +206,21 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     return out
 
 
+def prefill_workspace_size(S: int, Tq: int, max_query_len: int, Hq: int, Hkv: int, D: int, B: int,
+                           dtype: str, max_context_len: int) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    _check(lib.pkv_prefill_workspace_size(S, Tq, max_query_len, Hq, Hkv, D, B, DTYPE_CODE[dtype],
+                                          max_context_len, ctypes.byref(out)), "prefill_workspace_size")
+    return out.value
+
+
 def paged_attention_prefill(out, q, cu_seqlens_q, max_query_len: int, k_cache, v_cache,
                             block_tables, context_lens, max_context_len: int, scale: float,
-                            stream=None):
-    """Causal attention of each sequence's query chunk over its paged context."""
+                            workspace=None, stream=None):
+    """Causal attention of each sequence's query chunk over its paged context.
+    ``workspace`` (uint8 device tensor) is allocated here if the call needs one
+    and none is given."""
     torch = _torch()
     lib = load_library()
     Tq, Hq, D = q.shape
@@ -220,22 +232,31 @@ def paged_attention_prefill(out, q, cu_seqlens_q, max_query_len: int, k_cache, v
         raise TypeError("paged_attention_prefill: q/k/v dtype mismatch")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("paged_attention_prefill: block_tables [S, max_nb] / context_lens [S]")
+    kv_code = dtype_code(k_cache)
+    need = ctypes.c_size_t(0)
+    _check(lib.pkv_prefill_workspace_size(S, Tq, int(max_query_len), Hq, Hkv, D, B, kv_code,
+                                          int(max_context_len), ctypes.byref(need)), "prefill_workspace_size")
+    if workspace is None and need.value:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.pkv_paged_attention_prefill(
         _dev(out, "out"), dtype_code(out), _dev(q, "q"),
         _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), Tq, int(max_query_len),
-        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), dtype_code(k_cache),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), kv_code,
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B,
-        float(scale), _stream(stream)), "paged_attention_prefill")
+        float(scale), ws_ptr, ws_bytes, _stream(stream)), "paged_attention_prefill")
     return out
 
 
-def mixed_workspace_size(S: int, num_decode: int, Hq: int, Hkv: int, D: int, B: int,
-                         max_context_len: int) -> int:
+def mixed_workspace_size(S: int, num_decode: int, Tq: int, max_query_len: int, Hq: int, Hkv: int,
+                         D: int, B: int, dtype: str, max_context_len: int) -> int:
     lib = load_library()
     out = ctypes.c_size_t(0)
-    _check(lib.pkv_mixed_workspace_size(S, num_decode, Hq, Hkv, D, B, max_context_len,
-                                        ctypes.byref(out)), "mixed_workspace_size")
+    _check(lib.pkv_mixed_workspace_size(S, num_decode, Tq, max_query_len, Hq, Hkv, D, B,
+                                        DTYPE_CODE[dtype], max_context_len, ctypes.byref(out)),
+           "mixed_workspace_size")
     return out.value
 
 
@@ -243,8 +264,8 @@ def paged_attention_mixed(out, q, cu_seqlens_q, num_decode: int, max_query_len: 
                           v_cache, block_tables, context_lens, max_context_len: int, scale: float,
                           workspace=None, stream=None):
     """One call for a batch whose first ``num_decode`` sequences are decodes
-    (one query row each) and the rest prefill chunks; decodes and chunks run
-    concurrently.  Same rows as paged_attention_decode / _prefill, bit for bit."""
+    (one query row each) and the rest prefill chunks.  Same rows as
+    paged_attention_decode / _prefill, bit for bit."""
     torch = _torch()
     lib = load_library()
     Tq, Hq, D = q.shape
@@ -256,7 +277,11 @@ def paged_attention_mixed(out, q, cu_seqlens_q, num_decode: int, max_query_len: 
         raise TypeError("paged_attention_mixed: q/k/v dtype mismatch")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("paged_attention_mixed: block_tables [S, max_nb] / context_lens [S]")
-    need = mixed_workspace_size(S, num_decode, Hq, Hkv, D, B, max_context_len)
+    need = ctypes.c_size_t(0)
+    _check(lib.pkv_mixed_workspace_size(S, int(num_decode), Tq, int(max_query_len), Hq, Hkv, D, B,
+                                        dtype_code(k_cache), int(max_context_len), ctypes.byref(need)),
+           "mixed_workspace_size")
+    need = need.value
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib.pkv_paged_attention_mixed(

@@ -338,10 +338,36 @@ static pkv_status prefill_args(void* out, pkv_dtype out_dtype, const void* q,
   a->max_ctx = max_context_len;
   a->out_dt = out_dtype;
   a->scale_log2 = scale * 1.4426950408889634f;
+  a->n_split = 1;
+  a->tiles_per_split = 0;
+  a->ws_o = nullptr;
+  a->ws_ml = nullptr;
   return PKV_OK;
 }
 
+// Points a at its split plan and workspace (ws: plan.workspace_bytes bytes).
+static void attach_prefill_plan(const PrefillPlan& plan, void* ws, PrefillArgs* a) {
+  a->n_split = plan.n_split;
+  a->tiles_per_split = plan.tiles_per_split;
+  if (plan.n_split > 1) {
+    a->ws_o = static_cast<float*>(ws);
+    a->ws_ml = a->ws_o + (size_t)plan.n_split * a->Tq * a->Hq * a->D;
+  }
+}
+
 extern "C" {
+
+pkv_status pkv_prefill_workspace_size(int32_t S, int32_t Tq, int32_t max_query_len, int32_t Hq,
+                                      int32_t Hkv, int32_t D, int32_t B, pkv_dtype kv_dtype,
+                                      int32_t max_context_len, size_t* bytes) {
+  g_last_error[0] = 0;
+  PKV_REQUIRE(bytes, PKV_ERR_INVALID_ARG, "prefill_workspace_size: null output");
+  PKV_REQUIRE(S >= 0 && Tq >= 0 && max_query_len >= 0 && Hq > 0 && Hkv > 0 && D > 0 && B > 0 &&
+                  max_context_len >= 0 && Hq % Hkv == 0,
+              PKV_ERR_INVALID_ARG, "prefill_workspace_size: bad sizes");
+  *bytes = plan_prefill(kv_dtype, S, Tq, max_query_len, Hq, Hkv, D, B, max_context_len).workspace_bytes;
+  return PKV_OK;
+}
 
 pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* q,
                                        const int32_t* cu_seqlens_q, int32_t Tq,
@@ -350,7 +376,8 @@ pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const voi
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                                        const int32_t* context_lens, int32_t max_context_len,
                                        int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
-                                       float scale, void* stream) {
+                                       float scale, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
   g_last_error[0] = 0;
   PrefillArgs a;
   bool empty = true;
@@ -359,23 +386,32 @@ pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const voi
                                      context_lens, max_context_len, S, Hq, Hkv, D, B, scale, &a,
                                      &empty);
   if (st != PKV_OK || empty) return st;
+  const PrefillPlan plan = plan_prefill(kv_dtype, S, Tq, max_query_len, Hq, Hkv, D, B, max_context_len);
+  PKV_REQUIRE(plan.workspace_bytes == 0 || (workspace && workspace_bytes >= plan.workspace_bytes),
+              PKV_ERR_WORKSPACE, "prefill: workspace of %zu bytes needed, %zu given",
+              plan.workspace_bytes, workspace ? workspace_bytes : (size_t)0);
+  attach_prefill_plan(plan, workspace, &a);
   return launch_prefill(kv_dtype, a, static_cast<hipStream_t>(stream));
 }
 
-pkv_status pkv_mixed_workspace_size(int32_t S, int32_t num_decode, int32_t Hq, int32_t Hkv,
-                                    int32_t D, int32_t B, int32_t max_context_len,
+pkv_status pkv_mixed_workspace_size(int32_t S, int32_t num_decode, int32_t Tq,
+                                    int32_t max_query_len, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t B, pkv_dtype kv_dtype, int32_t max_context_len,
                                     size_t* bytes) {
   g_last_error[0] = 0;
   PKV_REQUIRE(bytes, PKV_ERR_INVALID_ARG, "mixed_workspace_size: null output");
-  PKV_REQUIRE(S >= 0 && num_decode >= 0 && num_decode <= S && Hq > 0 && Hkv > 0 && D > 0 &&
-                  B > 0 && max_context_len >= 0 && Hq % Hkv == 0,
+  PKV_REQUIRE(S >= 0 && num_decode >= 0 && num_decode <= S && Tq >= num_decode &&
+                  max_query_len >= 0 && Hq > 0 && Hkv > 0 && D > 0 && B > 0 &&
+                  max_context_len >= 0 && Hq % Hkv == 0,
               PKV_ERR_INVALID_ARG, "mixed_workspace_size: bad sizes");
   DecodePlan plan{};
   if (num_decode > 0) {
     const pkv_status st = plan_decode(num_decode, Hq, Hkv, D, B, max_context_len, &plan);
     if (st != PKV_OK) return st;
   }
-  *bytes = mixed_workspace_size(plan, S - num_decode);
+  const PrefillPlan pplan = plan_prefill(kv_dtype, S - num_decode, Tq - num_decode, max_query_len,
+                                         Hq, Hkv, D, B, max_context_len);
+  *bytes = mixed_workspace_size(plan, pplan, S - num_decode);
   return PKV_OK;
 }
 
@@ -404,7 +440,9 @@ pkv_status pkv_paged_attention_mixed(void* out, pkv_dtype out_dtype, const void*
     st = plan_decode(num_decode, Hq, Hkv, D, B, max_context_len, &plan);
     if (st != PKV_OK) return st;
   }
-  const size_t need = mixed_workspace_size(plan, S - num_decode);
+  const PrefillPlan pplan = plan_prefill(kv_dtype, S - num_decode, Tq - num_decode, max_query_len,
+                                         Hq, Hkv, D, B, max_context_len);
+  const size_t need = mixed_workspace_size(plan, pplan, S - num_decode);
   PKV_REQUIRE(workspace && workspace_bytes >= need, PKV_ERR_WORKSPACE,
               "mixed: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   DecodeArgs da{};
@@ -429,7 +467,7 @@ pkv_status pkv_paged_attention_mixed(void* out, pkv_dtype out_dtype, const void*
   da.out_dt = out_dtype;
   da.scale_log2 = scale * 1.4426950408889634f;
   pa.S = S - num_decode;
-  return launch_mixed(kv_dtype, plan, da, pa, num_decode, workspace,
+  return launch_mixed(kv_dtype, plan, pplan, da, pa, num_decode, workspace,
                       static_cast<hipStream_t>(stream));
 }
 

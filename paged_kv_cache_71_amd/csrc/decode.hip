@@ -1071,17 +1071,6 @@ int occupancy_of() {
   return occ;
 }
 
-int device_cu_count() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  static int cache[64] = {0};
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-  if (dev >= 0 && dev < 64 && n > 0) cache[dev] = n;
-  return n;
-}
-
 // Split launch (one resident wave set: CUs x occupancy, capped by grid_cap)
 // followed by the merge launch.
 template <int DT, int D, int GC, bool UNI, bool MF, bool F8>
@@ -1149,6 +1138,17 @@ void tile_geometry(int kv_dt, int D, int* tile, int* rpw) {
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static int cache[64] = {0};
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+  if (dev >= 0 && dev < 64 && n > 0) cache[dev] = n;
+  return n;
+}
 
 pkv_status plan_decode(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t /*B*/,
                        int32_t max_context_len, DecodePlan* plan) {

@@ -9,42 +9,20 @@
 // each, rows 0 .. num_decode - 1); the rest are prefill chunks.  Every output
 // row is what paged_attention_decode / paged_attention_prefill give for it.
 //
-// Design: the two parts run concurrently.  The decode part (split + merge
-// kernels, about one workgroup per CU on the matrix-core path, bound by HBM)
-// goes on the caller's stream; the prefill part (tile kernel, bound by the
-// matrix cores) on a library-owned stream of default priority, forked from
-// and joined back into the caller's stream with events.  A CU holds a decode
-// workgroup and a prefill workgroup at once, so the two share every CU.
-#include <mutex>
-
+// Design: the two parts run one after the other on the caller's stream, the
+// decode part (split + merge kernels, bound by HBM) and then the chunks
+// (tile kernel on the matrix cores).  A chunk too small to fill the GPU by
+// itself -- one long prompt's 512 tokens are 128 workgroups -- has its KV
+// range split across the whole GPU (prefill's split plan), so neither part
+// leaves CUs idle.  Running the two concurrently on two streams was measured
+// slower (444 us against 425 us on 256 Llama-3-8B decodes + one 512-token
+// chunk after 8192 tokens): the decode kernels need the same SIMD issue
+// slots as the chunk's matrix-core work, and their fixed per-workgroup
+// shares stretch when workgroups of the other kernel share their CUs.
 #include "pkv_internal.h"
 
 namespace pkv {
 namespace {
-
-constexpr int kMaxDevices = 64;
-
-struct AuxStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-AuxStream g_aux[kMaxDevices];
-std::mutex g_aux_mutex;  // also orders the fork / launch / join of concurrent calls
-
-pkv_status aux_for_current_device(AuxStream** out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-    return fail(PKV_ERR_HIP, "mixed: cannot query the current device");
-  AuxStream& a = g_aux[dev];
-  if (!a.s) {
-    if (hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&a.join, hipEventDisableTiming) != hipSuccess)
-      return fail(PKV_ERR_HIP, "mixed: cannot create the auxiliary stream");
-  }
-  *out = &a;
-  return PKV_OK;
-}
 
 // cu_out[i] = cu[num_decode + i] - num_decode, i <= S_p (the prefill chunks'
 // boundaries counted from their first row)
@@ -57,16 +35,20 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-size_t mixed_workspace_size(const DecodePlan& plan, int32_t S_prefill) {
-  return align_up(plan.workspace_bytes) + ((size_t)S_prefill + 1) * sizeof(int32_t);
+// Workspace: the decode part's, the chunks' rebased cu_seqlens, the chunks'
+// split partial results (when their plan splits).
+size_t mixed_workspace_size(const DecodePlan& plan, const PrefillPlan& pplan, int32_t S_prefill) {
+  return align_up(plan.workspace_bytes) + align_up(((size_t)S_prefill + 1) * sizeof(int32_t)) +
+         pplan.workspace_bytes;
 }
 
-pkv_status launch_mixed(int kv_dt, const DecodePlan& plan, const DecodeArgs& dec,
-                        const PrefillArgs& pre, int32_t num_decode, void* workspace,
-                        hipStream_t stream) {
+pkv_status launch_mixed(int kv_dt, const DecodePlan& plan, const PrefillPlan& pplan,
+                        const DecodeArgs& dec, const PrefillArgs& pre, int32_t num_decode,
+                        void* workspace, hipStream_t stream) {
   const int32_t S_p = pre.S;
   char* ws = static_cast<char*>(workspace);
   int32_t* cu_p = reinterpret_cast<int32_t*>(ws + align_up(plan.workspace_bytes));
+  char* ws_split = reinterpret_cast<char*>(cu_p) + align_up(((size_t)S_p + 1) * sizeof(int32_t));
   if (S_p == 0) return dec.S ? launch_decode(kv_dt, false, plan, dec, stream) : PKV_OK;
 
   PrefillArgs p = pre;
@@ -77,33 +59,21 @@ pkv_status launch_mixed(int kv_dt, const DecodePlan& plan, const DecodeArgs& dec
   p.Tq = pre.Tq - num_decode;
   p.block_tables = pre.block_tables + (int64_t)num_decode * pre.max_nb;
   p.context_lens = pre.context_lens + num_decode;
-
-  if (dec.S == 0) {
-    hipLaunchKernelGGL(rebase_cu_kernel, dim3(1), dim3(256), 0, stream, pre.cu_seqlens_q, num_decode,
-                       S_p, cu_p);
-    const pkv_status st = check_launch("mixed (rebase)");
-    return st != PKV_OK ? st : launch_prefill(kv_dt, p, stream);
+  p.n_split = pplan.n_split;
+  p.tiles_per_split = pplan.tiles_per_split;
+  if (pplan.n_split > 1) {
+    p.ws_o = reinterpret_cast<float*>(ws_split);
+    p.ws_ml = p.ws_o + (size_t)pplan.n_split * p.Tq * p.Hq * p.D;
   }
 
-  std::lock_guard<std::mutex> lock(g_aux_mutex);
-  AuxStream* aux = nullptr;
-  pkv_status st = aux_for_current_device(&aux);
-  if (st != PKV_OK) return st;
-  // fork: the prefill part waits for everything queued on the caller's stream
-  if (hipEventRecord(aux->fork, stream) != hipSuccess ||
-      hipStreamWaitEvent(aux->s, aux->fork, 0) != hipSuccess)
-    return fail(PKV_ERR_HIP, "mixed: fork failed");
-  hipLaunchKernelGGL(rebase_cu_kernel, dim3(1), dim3(256), 0, aux->s, pre.cu_seqlens_q, num_decode,
+  if (dec.S > 0) {
+    const pkv_status sd = launch_decode(kv_dt, false, plan, dec, stream);
+    if (sd != PKV_OK) return sd;
+  }
+  hipLaunchKernelGGL(rebase_cu_kernel, dim3(1), dim3(256), 0, stream, pre.cu_seqlens_q, num_decode,
                      S_p, cu_p);
-  st = check_launch("mixed (rebase)");
-  if (st == PKV_OK) st = launch_prefill(kv_dt, p, aux->s);
-  const pkv_status sd = launch_decode(kv_dt, false, plan, dec, stream);
-  // join: the caller's stream waits for the prefill part (also after a failed
-  // launch, so nothing is left behind on the auxiliary stream unordered)
-  if (hipEventRecord(aux->join, aux->s) != hipSuccess ||
-      hipStreamWaitEvent(stream, aux->join, 0) != hipSuccess)
-    return fail(PKV_ERR_HIP, "mixed: join failed");
-  return st != PKV_OK ? st : sd;
+  const pkv_status st = check_launch("mixed (rebase)");
+  return st != PKV_OK ? st : launch_prefill(kv_dt, p, stream);
 }
 
 }  // namespace pkv

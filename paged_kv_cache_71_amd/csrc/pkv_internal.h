@@ -153,15 +153,32 @@ struct PrefillArgs {
   int32_t max_ctx;   // context lengths are clamped to this (<= max_nb * B)
   int32_t out_dt;
   float scale_log2;
+  // split of each workgroup's KV range (plan_prefill): n_split > 1 writes
+  // partial results of rows whose range spans several splits to ws_o / ws_ml
+  // and a merge kernel combines them
+  int32_t n_split, tiles_per_split;
+  float* ws_o;   // [n_split][Tq * Hq][D] unnormalised outputs
+  float* ws_ml;  // [n_split][Tq * Hq][2] running max (log2 units) and weight sum
 };
+// Split plan of a prefill launch: a deterministic function of the arguments
+// (and of the device's CU count), so equal calls give equal bits.
+struct PrefillPlan {
+  int n_split;          // 1: no split
+  int tiles_per_split;  // KV tiles (32 tokens) per split
+  size_t workspace_bytes;
+};
+PrefillPlan plan_prefill(int kv_dt, int32_t S, int32_t Tq, int32_t max_query_len, int32_t Hq,
+                         int32_t Hkv, int32_t D, int32_t B, int32_t max_ctx);
 pkv_status launch_prefill(int kv_dt, const PrefillArgs& a, hipStream_t stream);
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cu_count();
 
 // Mixed decode + prefill batch (mixed.hip): the decode part (dec.S sequences,
 // plan for them) and the prefill part (pre: the whole batch's pointers, pre.S =
 // number of prefill sequences after the num_decode decodes).
-size_t mixed_workspace_size(const DecodePlan& plan, int32_t S_prefill);
-pkv_status launch_mixed(int kv_dt, const DecodePlan& plan, const DecodeArgs& dec,
-                        const PrefillArgs& pre, int32_t num_decode, void* workspace,
-                        hipStream_t stream);
+size_t mixed_workspace_size(const DecodePlan& plan, const PrefillPlan& pplan, int32_t S_prefill);
+pkv_status launch_mixed(int kv_dt, const DecodePlan& plan, const PrefillPlan& pplan,
+                        const DecodeArgs& dec, const PrefillArgs& pre, int32_t num_decode,
+                        void* workspace, hipStream_t stream);
 
 }  // namespace pkv

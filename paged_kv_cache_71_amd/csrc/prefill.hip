@@ -34,6 +34,8 @@
 //    past the context is never dereferenced.
 //
 // fp32 KV: a plain vector-ALU kernel (one wave per query token and KV head).
+#include <algorithm>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -454,17 +456,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int G = a.Hq / a.Hkv;
   const int TQ = RW / G;  // query tokens per workgroup
   const int nqt = (a.max_query_len + TQ - 1) / TQ;
+  const int ns = a.n_split;
+  const int units = nqt * ns;  // workgroups per (sequence, KV head): query tiles x splits
   const int n_pairs = a.S * a.Hkv;
   const int b = blockIdx.x;
-  int pair, qt;
+  int pair, u;
   if ((n_pairs & 7) == 0) {  // all workgroups of a (sequence, KV head) on one XCD
     const int r = b >> 3;
-    pair = (r / nqt) * 8 + (b & 7);
-    qt = nqt - 1 - r % nqt;
+    pair = (r / units) * 8 + (b & 7);
+    u = r % units;
   } else {
-    pair = b / nqt;
-    qt = nqt - 1 - b % nqt;
+    pair = b / units;
+    u = b % units;
   }
+  const int qt = nqt - 1 - u / ns;  // longest query tiles first
+  const int sp = u % ns;
   const int s = pair / a.Hkv;
   const int kvh = pair % a.Hkv;
   const int q0 = a.cu_seqlens_q[s];
@@ -493,6 +499,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const int kv_end = L - Qs + min(tq0 + TQ, Qs);  // tokens any row of the workgroup sees
   const int ntiles = (kv_end + kTileKV - 1) / kTileKV;  // >= 1 here
+  // this workgroup's tiles t0 .. tl (split sp of the rows' range)
+  const int tps = ns > 1 ? a.tiles_per_split : ntiles;
+  const int t0 = sp * tps;
+  if (t0 >= ntiles) return;  // past the rows' last tile; uniform, before any barrier
+  const int tl = min(ntiles, t0 + tps) - 1;
+  const bool partial = ntiles > tps;  // the rows' range spans several splits
 
   // Scores are kept as raw q.k; the softmax scale enters the exponent through
   // one fma.  A negative scale flips the sign of q instead (exact for 16-bit
@@ -608,19 +620,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int i = 0; i < NCH; ++i) sv[i] = make_uint4(0, 0, 0, 0);
   int ea0, ea1, eb0, eb1, ent;  // entries of tiles j+1 and j+2; vector of tile j+3
-  const int tl = ntiles - 1;
   {
-    const int en0 = ent_load(0);
-    const int en1 = ent_load(min(1, tl));
-    ent = ent_load(min(2, tl));
+    const int en0 = ent_load(t0);
+    const int en1 = ent_load(min(t0 + 1, tl));
+    ent = ent_load(min(t0 + 2, tl));
     ea0 = __builtin_amdgcn_readlane(en0, 0);
     ea1 = __builtin_amdgcn_readlane(en0, 1);
     eb0 = __builtin_amdgcn_readlane(en1, 0);
     eb1 = __builtin_amdgcn_readlane(en1, 1);
   }
-  gload(sk, kpool, 0, ea0, ea1);
-  lstore(lk[0], KP, sk);
-  gload(sk, kpool, min(1, tl), eb0, eb1);
+  gload(sk, kpool, t0, ea0, ea1);
+  lstore(lk[t0 & 1], KP, sk);
+  gload(sk, kpool, min(t0 + 1, tl), eb0, eb1);
   lds_barrier();
 
   f32x4_t SA[2][QB], SB[2][QB];   // S of the tile being softmaxed / of the next one
@@ -751,14 +762,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  // step -1: S(0) into SB; step 0: softmax(0), S(1) into SA, P(0) into PA
-  step(-1, T{}, F{}, T{}, F{}, F{}, SA, SB, PAh, PAl, PBh, PBl);
-  step(0, T{}, F{}, T{}, T{}, T{}, SB, SA, PBh, PBl, PAh, PAl);
-  if (ntiles >= 2) {
+  // step t0-1: S(t0) into SB; step t0: softmax(t0), S(t0+1) into SA, P(t0) into PA
+  step(t0 - 1, T{}, F{}, T{}, F{}, F{}, SA, SB, PAh, PAl, PBh, PBl);
+  step(t0, T{}, F{}, T{}, T{}, T{}, SB, SA, PBh, PBl, PAh, PAl);
+  if (tl > t0) {
     // steady state, unrolled by two so S and P alternate between the A and B
     // registers; tiles wholly at or before every row's position skip the mask
-    const int nfree = pos_min == 0x7fffffff ? tl : max(1, min(tl, (pos_min + 1) / kTileKV));
-    int j = 1;
+    const int nfree = pos_min == 0x7fffffff ? tl : max(t0 + 1, min(tl, (pos_min + 1) / kTileKV));
+    int j = t0 + 1;
     for (; j + 1 < nfree; j += 2) {
       step(j, T{}, T{}, T{}, T{}, F{}, SA, SB, PAh, PAl, PBh, PBl);
       step(j + 1, T{}, T{}, T{}, T{}, F{}, SB, SA, PBh, PBl, PAh, PAl);
@@ -776,7 +787,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     step(tl, T{}, T{}, F{}, T{}, T{}, SA, SB, PAh, PAl, PBh, PBl);
     step(tl + 1, F{}, T{}, F{}, F{}, F{}, SA, SB, PBh, PBl, PAh, PAl);
   } else {
-    step(1, F{}, T{}, F{}, F{}, F{}, SA, SB, PAh, PAl, PBh, PBl);
+    step(t0 + 1, F{}, T{}, F{}, F{}, F{}, SA, SB, PAh, PAl, PBh, PBl);
   }
 
   // total weight of each row (the four lane groups hold different tokens)
@@ -784,6 +795,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int c = 0; c < QB; ++c) {
     pair_sum<16>(lsum[c]);
     pair_sum<32>(lsum[c]);
+  }
+  if (partial) {
+    // unnormalised output, running max and weight sum of this split
+    const int64_t rec = (int64_t)sp * a.Tq * a.Hq;
+#pragma unroll
+    for (int c = 0; c < QB; ++c) {
+      if (!valid[c]) continue;
+      float* po = a.ws_o + (rec + orow[c]) * D;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+        *reinterpret_cast<float4*>(po + 16 * d + 4 * g4) =
+            make_float4(o[d][c][0], o[d][c][1], o[d][c][2], o[d][c][3]);
+      if (g4 == 0) *reinterpret_cast<float2*>(a.ws_ml + (rec + orow[c]) * 2) = make_float2(m[c], lsum[c]);
+    }
+    return;
   }
 #pragma unroll
   for (int c = 0; c < QB; ++c) {
@@ -806,6 +832,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
   }
+}
+
+// Merge of split prefill results ("Flash-Decoding" style log-sum-exp merge of
+// partial softmax results over disjoint KV ranges): one wave per output row
+// (token, query head); rows whose range was not split were written by the
+// tile kernel and are skipped.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a) {
+  constexpr int EPL = D / 64;
+  constexpr int RW = kWaves * 16 * kTileQB;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nrows = (int64_t)a.Tq * a.Hq;
+  if (row >= nrows) return;
+  const int t = (int)(row / a.Hq);
+  int lo = 0, hi = a.S;  // sequence of token t: last s with cu[s] <= t
+  if (t >= a.cu_seqlens_q[a.S]) return;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_seqlens_q[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int q0 = a.cu_seqlens_q[lo];
+  const int Qs = a.cu_seqlens_q[lo + 1] - q0;
+  const int L = min(a.context_lens[lo], a.max_ctx);
+  if (Qs > L) return;  // skipped by the tile kernel as well
+  const int TQ = RW / (a.Hq / a.Hkv);
+  const int qt = (t - q0) / TQ;
+  const int kv_end = L - Qs + min(qt * TQ + TQ, Qs);
+  const int ntiles = (kv_end + kTileKV - 1) / kTileKV;
+  const int nu = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
+  if (nu <= 1) return;
+  const int64_t stride = nrows;
+  float M = -__builtin_inff();
+  for (int i = 0; i < nu; ++i) M = fmaxf(M, a.ws_ml[(i * stride + row) * 2]);
+  float den = 0.f, acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int i = 0; i < nu; ++i) {
+    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + (i * stride + row) * 2);
+    const float w = fast_exp2(ml.x - M);  // a split no row position reaches: m = -inf, w = 0
+    den += w * ml.y;
+    const float* po = a.ws_o + (i * stride + row) * D + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += w * po[e];
+  }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) store_out(a.out, a.out_dt, row * D + lane * EPL + e, acc[e] * inv);
 }
 
 // fp32 KV: one wave per (query token, KV head); each lane owns D/64 elements
@@ -879,12 +953,17 @@ pkv_status launch_tile(const PrefillArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const int TQ = RW / G;
   const int64_t nqt = (a.max_query_len + TQ - 1) / TQ;
-  const int64_t grid = nqt * a.S * a.Hkv;
+  const int64_t grid = nqt * a.S * a.Hkv * a.n_split;
   if (grid == 0) return PKV_OK;
   if (grid > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "prefill grid too large");
   hipLaunchKernelGGL((prefill_tile_kernel<DT, D>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, a);
-  return check_launch("paged_attention_prefill");
+  pkv_status st = check_launch("paged_attention_prefill");
+  if (st != PKV_OK || a.n_split <= 1) return st;
+  const int64_t mgrid = ((int64_t)a.Tq * a.Hq + 3) / 4;
+  if (mgrid > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "prefill merge grid too large");
+  hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3((unsigned)mgrid), dim3(256), 0, stream, a);
+  return check_launch("paged_attention_prefill (merge)");
 }
 
 template <int DT, int D>
@@ -914,6 +993,35 @@ pkv_status launch_f32(const PrefillArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Split plan.  A launch whose workgroups ((sequence, KV head) pairs x query
+// tiles) would not fill the GPU twice over with two per CU -- few sequences,
+// e.g. one long prompt's chunk -- cuts every workgroup's KV range into splits
+// of tiles_per_split tiles (at least kMinSplitTiles), up to four workgroups
+// per CU in total.  Workgroups whose range fits one split write their rows
+// directly; the others leave partial results for the merge kernel.
+PrefillPlan plan_prefill(int kv_dt, int32_t S, int32_t Tq, int32_t max_query_len, int32_t Hq,
+                         int32_t Hkv, int32_t D, int32_t B, int32_t max_ctx) {
+  constexpr int kMinSplitTiles = 8;
+  PrefillPlan p{1, 0, 0};
+  const int G = Hkv > 0 ? Hq / Hkv : 0;
+  const bool tile = kv_dt != DT_F32 && B >= 16 && G >= 1 && G <= kWaves * 16 * kTileQB;
+  if (!tile || S <= 0 || Tq <= 0 || max_query_len <= 0 || max_ctx <= 0) return p;
+  const int TQ = kWaves * 16 * kTileQB / G;
+  const int64_t grid0 = (int64_t)((max_query_len + TQ - 1) / TQ) * S * Hkv;
+  const int max_tiles = (max_ctx + kTileKV - 1) / kTileKV;
+  const int64_t target = 4 * (int64_t)std::max(device_cu_count(), 1);
+  if (grid0 >= target) return p;
+  int ns = (int)std::min<int64_t>((target + grid0 - 1) / grid0, std::max(1, max_tiles / kMinSplitTiles));
+  if (ns <= 1) return p;
+  const int tps = (max_tiles + ns - 1) / ns;
+  ns = (max_tiles + tps - 1) / tps;
+  if (ns <= 1) return p;
+  p.n_split = ns;
+  p.tiles_per_split = tps;
+  p.workspace_bytes = (size_t)ns * Tq * Hq * (D + 2) * sizeof(float);
+  return p;
+}
 
 pkv_status launch_prefill(int kv_dt, const PrefillArgs& a, hipStream_t stream) {
   if (kv_dt == DT_F32) {

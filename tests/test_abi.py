@@ -61,11 +61,36 @@ def test_decode_rejects_bad_arguments(lib, kw, status):
 
 def test_prefill_rejects_bad_arguments(lib):
     rc = lib.pkv_paged_attention_prefill(FAKE, 0, FAKE, FAKE, 10, 20, FAKE, FAKE, 2, FAKE, 4, FAKE,
-                                         16, 2, 8, 4, 128, 16, 0.1, None)   # max_query_len > max ctx
+                                         16, 2, 8, 4, 128, 16, 0.1, None, 0, None)  # max_query_len > max ctx
     assert rc == 1
     rc = lib.pkv_paged_attention_prefill(FAKE, 0, FAKE, FAKE, 10, 8, FAKE, FAKE, 2, FAKE, 4, FAKE,
-                                         16, 2, 8, 3, 128, 16, 0.1, None)   # Hq % Hkv
+                                         16, 2, 8, 3, 128, 16, 0.1, None, 0, None)  # Hq % Hkv
     assert rc == 1
+
+
+def prefill_ws(lib, S, Tq, maxq, Hq, Hkv, D, B, kv, maxL):
+    n = ctypes.c_size_t(123)
+    assert lib.pkv_prefill_workspace_size(S, Tq, maxq, Hq, Hkv, D, B, kv, maxL, ctypes.byref(n)) == 0
+    return n.value
+
+
+def test_prefill_split_plan_and_workspace_check(lib):
+    """One long sequence cannot fill the GPU with (KV head, query tile) units:
+    its KV range is split, which needs a workspace of partial results; the call
+    without one fails before launching anything.  f32 pools, blocks under 16
+    tokens and many-sequence batches need none."""
+    need = prefill_ws(lib, 1, 32, 32, 4, 1, 128, 16, 2, 8192)         # one unit, 256 tiles
+    assert need > 0 and need % (32 * 4 * 130 * 4) == 0
+    assert prefill_ws(lib, 1, 32, 32, 4, 1, 128, 16, 0, 8192) == 0     # f32
+    assert prefill_ws(lib, 1, 32, 32, 4, 1, 128, 8, 2, 8192) == 0      # block 8
+    assert prefill_ws(lib, 1, 32, 32, 4, 1, 128, 16, 2, 200) == 0      # under two splits of tiles
+    assert prefill_ws(lib, 4096, 4096, 1, 32, 8, 128, 16, 2, 8192) == 0  # enough units
+    rc = lib.pkv_paged_attention_prefill(FAKE, 0, FAKE, FAKE, 32, 32, FAKE, FAKE, 2, FAKE, 512, FAKE,
+                                         8192, 1, 4, 1, 128, 16, 0.1, None, 0, None)
+    assert rc == 3 and b"workspace" in lib.pkv_last_error()
+    rc = lib.pkv_paged_attention_prefill(FAKE, 0, FAKE, FAKE, 32, 32, FAKE, FAKE, 2, FAKE, 512, FAKE,
+                                         8192, 1, 4, 1, 128, 16, 0.1, FAKE, need - 1, None)
+    assert rc == 3
 
 
 def test_cache_ops_reject_bad_arguments(lib):

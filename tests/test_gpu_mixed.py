@@ -1,7 +1,7 @@
-"""Mixed decode + prefill batches on the GPU: one call whose decode rows and
-chunk rows run concurrently.  Every row must equal the standalone decode /
-prefill result bit for bit, and the fp64 oracle (a decode row is a chunk of
-one token) within tolerance."""
+"""Mixed decode + prefill batches on the GPU: one call for decode rows and
+chunk rows.  Every row must equal the standalone decode / prefill result bit
+for bit, and the fp64 oracle (a decode row is a chunk of one token) within
+tolerance."""
 import numpy as np
 import pytest
 import torch

@@ -118,3 +118,34 @@ def test_scale_sign_and_zero(gpu_lib, dtype, scale):
     b = W.varlen_prefill(77, [0, 40, 300], [20, 70, 45], 16, 4, 128, 16, dtype)
     b.scale = scale
     check(gpu_lib, b)
+
+
+@pytest.mark.parametrize("dtype,D,B", [("bf16", 128, 16), ("f16", 128, 16), ("bf16", 64, 32)])
+def test_split_long_contexts(gpu_lib, dtype, D, B):
+    """Few sequences with long contexts: each workgroup's KV range is split
+    and the partial softmax results merged.  The short sequence's rows fit one
+    split (written directly) and leave most of their splits empty."""
+    b = W.varlen_prefill(11 + D, [5000, 300, 2100], [100, 37, 64], 32, 8, D, B, dtype)
+    assert gpu_lib.prefill_workspace_size(b.S, b.q.shape[0], 100, 32, 8, D, B, dtype,
+                                          b.max_context_len) > 0, "expected a split launch"
+    check(gpu_lib, b)
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+def test_split_merge_low_precision_output(gpu_lib, out_dtype):
+    """The merge kernel's 16-bit output is the round-to-nearest-even of its
+    fp32 output, bit for bit."""
+    b = W.varlen_prefill(5, [3000], [70], 32, 8, 128, 16, "bf16")
+    db = DevBatch(b)
+    full = gpu_prefill(gpu_lib, db, "f32")
+    low = gpu_prefill(gpu_lib, db, out_dtype, write_chunk=False)
+    assert torch.equal(low, full.to(low.dtype))
+
+
+def test_split_one_long_prompt_full_size_sampled(gpu_lib):
+    """One 512-token chunk after 8192 cached tokens (the chunk of the mixed
+    batch), alone: split into partial ranges; sampled rows against the oracle."""
+    b = W.varlen_prefill(2, [8192], [512], 32, 8, 128, 16, "bf16")
+    assert gpu_lib.prefill_workspace_size(1, 512, 512, 32, 8, 128, 16, "bf16", b.max_context_len) > 0
+    rows = [0, 1, 31, 32, 200, 480, 511]
+    check(gpu_lib, b, rows=rows)
