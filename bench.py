@@ -291,18 +291,19 @@ def main():
     torch.cuda.synchronize()
     dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    start.record(stream)
+    step_ev[0].record(stream)
     for i in range(args.steps):
         d.reshape()
         dec_ev[i][0].record(stream)
         d.decode()
         dec_ev[i][1].record(stream)
-    stop.record(stream)
+        step_ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
+    total_ms = step_ev[0].elapsed_time(step_ev[-1])
     ms_per_step = total_ms / args.steps
+    step_ms = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)])
     dec_ms = float(np.mean([a.elapsed_time(z) for a, z in dec_ev]))
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (dec_ms * 1e-3) / 1e9
@@ -330,6 +331,7 @@ def main():
             "context_tokens": int(b.context_lens.sum()),
             "kv_bytes_per_step": kv_bytes,
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+            "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
         },
         "roofline": {
             "bound": "hbm",

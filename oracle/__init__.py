@@ -81,6 +81,9 @@ def _load(path: str | None = None):
         lib.pkvo_decode_fp8.restype = ci
         lib.pkvo_decode_fp8.argtypes = [P, P, ci, P, P, P, P, P, i32, P, i64, i32, i32, i32, i32,
                                         i32, dbl]
+        lib.pkvo_prefill_fp8_rows.restype = ci
+        lib.pkvo_prefill_fp8_rows.argtypes = [P, P, ci, P, i32, P, P, P, P, P, i32, P, i64, i32, i32,
+                                              i32, i32, i32, dbl, P, i32]
         if path is not None:
             return lib
         _lib = lib
@@ -204,6 +207,35 @@ def prefill(q, cu_seqlens_q, k_cache, v_cache, dtype: str, block_tables, context
     _check(lib.pkvo_prefill_rows(_ptr(out), _ptr(q), _ptr(cu), Tq, _ptr(k_cache), _ptr(v_cache),
                                  DTYPE_CODE[dtype], _ptr(block_tables), max_nb, _ptr(context_lens),
                                  NB, S, Hq, Hkv, D, B, scale, rp, nr), "prefill")
+    return out
+
+
+def prefill_fp8(q, q_dtype: str, cu_seqlens_q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                context_lens, scale: float, rows=None) -> np.ndarray:
+    """fp64 causal prefill output [Tq, Hq, D] over FP8 pools read as code * scale;
+    with ``rows`` only those query tokens are computed (the rest stay NaN)."""
+    lib = _load()
+    q, k_cache, v_cache = _c(q), _c(k_cache, np.uint8), _c(v_cache, np.uint8)
+    k_scale, v_scale = _c(k_scale, np.float32), _c(v_scale, np.float32)
+    cu = _c(cu_seqlens_q, np.int32)
+    block_tables = _c(block_tables, np.int32)
+    context_lens = _c(context_lens, np.int32)
+    Tq, Hq, D = q.shape
+    S = cu.shape[0] - 1
+    NB, B, Hkv, Dk = k_cache.shape
+    assert Dk == D and v_cache.shape == k_cache.shape
+    assert k_scale.shape == (Hkv,) and v_scale.shape == (Hkv,)
+    max_nb = block_tables.shape[1]
+    out = np.full((Tq, Hq, D), np.nan, np.float64)
+    if rows is None:
+        rp, nr = None, 0
+    else:
+        rows = _c(rows, np.int32)
+        rp, nr = _ptr(rows), rows.shape[0]
+    _check(lib.pkvo_prefill_fp8_rows(_ptr(out), _ptr(q), DTYPE_CODE[q_dtype], _ptr(cu), Tq,
+                                     _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                     _ptr(block_tables), max_nb, _ptr(context_lens), NB, S, Hq, Hkv,
+                                     D, B, scale, rp, nr), "prefill_fp8")
     return out
 
 

@@ -296,13 +296,17 @@ int pkvo_decode(double* out, const void* q, const void* k_cache, const void* v_c
  * i of sequence s is at absolute position L_s - Q_s + i and sees positions
  * 0..L_s - Q_s + i.
  */
-int pkvo_prefill_rows(double* out, const void* q, const int32_t* cu_seqlens_q, int32_t Tq,
-                      const void* k_cache, const void* v_cache, int dtype,
-                      const int32_t* block_tables, int32_t max_nb, const int32_t* context_lens,
-                      int64_t NB, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
-                      double scale, const int32_t* rows, int32_t n_rows) {
-  int rc = check_shapes(dtype, S, Hq, Hkv, D, B, max_nb);
+static int prefill_rows_impl(double* out, const void* q, int q_dtype,
+                             const int32_t* cu_seqlens_q, int32_t Tq, const void* k_cache,
+                             const void* v_cache, int kv_dtype, const float* k_scale,
+                             const float* v_scale, const int32_t* block_tables, int32_t max_nb,
+                             const int32_t* context_lens, int64_t NB, int32_t S, int32_t Hq,
+                             int32_t Hkv, int32_t D, int32_t B, double scale, const int32_t* rows,
+                             int32_t n_rows) {
+  if (q_dtype == PKVO_FP8) return PKVO_EINVAL;
+  int rc = check_shapes(q_dtype, S, Hq, Hkv, D, B, max_nb);
   if (rc) return rc;
+  if (!elem_bytes(kv_dtype)) return PKVO_EINVAL;
   if (cu_seqlens_q[0] != 0 || cu_seqlens_q[S] != Tq) return PKVO_EINVAL;
   const int32_t G = Hq / Hkv;
   int32_t maxL = 0;
@@ -337,15 +341,21 @@ int pkvo_prefill_rows(double* out, const void* q, const int32_t* cu_seqlens_q, i
     if (!any) continue;
     const int32_t* table = block_tables + (int64_t)s * max_nb;
     for (int32_t g = 0; g < Hkv && rc == PKVO_OK; ++g) {
-      rc = pkvo_gather(K, k_cache, dtype, table, L, NB, Hkv, D, B, g);
-      if (rc == PKVO_OK) rc = pkvo_gather(V, v_cache, dtype, table, L, NB, Hkv, D, B, g);
+      rc = pkvo_gather(K, k_cache, kv_dtype, table, L, NB, Hkv, D, B, g);
+      if (rc == PKVO_OK) rc = pkvo_gather(V, v_cache, kv_dtype, table, L, NB, Hkv, D, B, g);
+      if (k_scale && v_scale) {
+        for (int64_t e = 0; e < (int64_t)L * D; ++e) {
+          K[e] *= (double)k_scale[g];
+          V[e] *= (double)v_scale[g];
+        }
+      }
       for (int32_t i = 0; i < Qs && rc == PKVO_OK; ++i) {
         if (!want[r0 + i]) continue;
         const int32_t visible = L - Qs + i + 1; /* positions 0 .. L-Qs+i */
         for (int32_t j = 0; j < G && rc == PKVO_OK; ++j) {
           const int32_t h = g * G + j;
           const int64_t base = ((int64_t)(r0 + i) * Hq + h) * D;
-          for (int32_t d = 0; d < D; ++d) qd[d] = pkvo_load_elem(q, dtype, base + d);
+          for (int32_t d = 0; d < D; ++d) qd[d] = pkvo_load_elem(q, q_dtype, base + d);
           rc = pkvo_attend(out + base, qd, K, V, visible, D, scale);
         }
       }
@@ -353,6 +363,33 @@ int pkvo_prefill_rows(double* out, const void* q, const int32_t* cu_seqlens_q, i
   }
   free(want); free(K); free(V); free(qd);
   return rc;
+}
+
+int pkvo_prefill_rows(double* out, const void* q, const int32_t* cu_seqlens_q, int32_t Tq,
+                      const void* k_cache, const void* v_cache, int dtype,
+                      const int32_t* block_tables, int32_t max_nb, const int32_t* context_lens,
+                      int64_t NB, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                      double scale, const int32_t* rows, int32_t n_rows) {
+  return prefill_rows_impl(out, q, dtype, cu_seqlens_q, Tq, k_cache, v_cache, dtype, NULL, NULL,
+                           block_tables, max_nb, context_lens, NB, S, Hq, Hkv, D, B, scale, rows,
+                           n_rows);
+}
+
+/*
+ * Prefill over FP8 pools: as pkvo_prefill_rows, with q in q_dtype and every
+ * cached element read as code * scale of its KV head (the same reading of an
+ * FP8 pool as pkvo_decode_fp8).
+ */
+int pkvo_prefill_fp8_rows(double* out, const void* q, int q_dtype, const int32_t* cu_seqlens_q,
+                          int32_t Tq, const uint8_t* k_cache, const uint8_t* v_cache,
+                          const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                          int32_t max_nb, const int32_t* context_lens, int64_t NB, int32_t S,
+                          int32_t Hq, int32_t Hkv, int32_t D, int32_t B, double scale,
+                          const int32_t* rows, int32_t n_rows) {
+  if (!k_scale || !v_scale) return PKVO_EINVAL;
+  return prefill_rows_impl(out, q, q_dtype, cu_seqlens_q, Tq, k_cache, v_cache, PKVO_FP8, k_scale,
+                           v_scale, block_tables, max_nb, context_lens, NB, S, Hq, Hkv, D, B,
+                           scale, rows, n_rows);
 }
 
 int pkvo_prefill(double* out, const void* q, const int32_t* cu_seqlens_q, int32_t Tq,

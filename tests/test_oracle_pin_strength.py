@@ -56,6 +56,8 @@ MUTATIONS = [
      "const float vq = load_f32(value, in_dtype, src) / k_scale[h];"),
     ("fp8_decode_drops_k_scale", "        K[i] *= (double)k_scale[g];\n", ""),
     ("fp8_decode_v_scale_of_k", "V[i] *= (double)v_scale[g];", "V[i] *= (double)k_scale[g];"),
+    ("fp8_prefill_v_scale_of_k", "V[e] *= (double)v_scale[g];", "V[e] *= (double)k_scale[g];"),
+    ("fp8_prefill_drops_k_scale", "          K[e] *= (double)k_scale[g];\n", ""),
 ]
 
 # the pins, called directly (parametrised ones with representative arguments)
@@ -81,6 +83,7 @@ CASES = [
     (pins.test_reshape_and_cache_fp8_matches_torch_quantization, {"in_dtype": "bf16"}),
     (pins.test_decode_fp8_matches_sdpa_on_dequantized_values, {"q_dtype": "bf16"}),
     (pins.test_decode_fp8_single_token_returns_code_times_scale, {}),
+    (pins.test_prefill_fp8_matches_causal_sdpa_on_dequantized_values, {"q_dtype": "bf16"}),
 ]
 
 

@@ -456,6 +456,50 @@ def test_decode_fp8_single_token_returns_code_times_scale():
             assert np.array_equal(out[s, h], want)
 
 
+@pytest.mark.parametrize("q_dtype", ["bf16", "f16"])
+def test_prefill_fp8_matches_causal_sdpa_on_dequantized_values(q_dtype):
+    """A 9-token chunk after 14 cached tokens, blocks scattered by the table:
+    causal attention (bottom-right aligned mask) over code * head scale."""
+    rng = np.random.default_rng(21)
+    Hq, Hkv, B, D, L, Q = 6, 2, 4, 16, 23, 9
+    nb = -(-L // B)
+    k, v = _fp8_pool(rng, nb + 3, B, Hkv, D)
+    table = rng.permutation(nb + 3)[:nb].astype(np.int32)
+    ks, vs = np.float32([0.05, 0.8]), np.float32([0.3, 0.0125])
+    q = W.to_storage(rng.standard_normal((Q, Hq, D), dtype=np.float32), q_dtype)
+    out = oracle.prefill_fp8(q, q_dtype, np.array([0, Q], np.int32), k, v, ks, vs, table[None],
+                             np.array([L]), 0.3)
+    pos = np.arange(nb * B)
+    Kc = (_torch_e4m3_to_f64(k[table]).reshape(nb * B, Hkv, D)[:L] * ks.astype(np.float64)[None, :, None])
+    Vc = (_torch_e4m3_to_f64(v[table]).reshape(nb * B, Hkv, D)[:L] * vs.astype(np.float64)[None, :, None])
+    qc = W.storage_to_f32(q, q_dtype).astype(np.float64).transpose(1, 0, 2)      # [Hq, Q, D]
+    mask = torch.from_numpy(pos[None, :L] <= (L - Q + np.arange(Q))[:, None])
+    qt, Kt, Vt = (torch.from_numpy(np.ascontiguousarray(x)) for x in
+                  (qc, Kc.transpose(1, 0, 2), Vc.transpose(1, 0, 2)))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qt[None], Kt[None], Vt[None], attn_mask=mask, scale=0.3, enable_gqa=True)[0].numpy()
+    np.testing.assert_allclose(out, ref.transpose(1, 0, 2), rtol=1e-12, atol=1e-15)
+
+
+def test_prefill_fp8_unit_scales_equal_the_16_bit_prefill():
+    """Every E4M3 value is a bf16 value: with unit scales the FP8 prefill of the
+    codes equals the bf16 prefill of their values, bit for bit."""
+    rng = np.random.default_rng(22)
+    Hq, Hkv, B, D = 4, 2, 8, 8
+    lens, chunks = np.array([13, 30], np.int32), np.array([5, 30], np.int32)
+    k, v = _fp8_pool(rng, 8, B, Hkv, D)
+    tables = np.array([[5, 1, 0, 0], [2, 7, 3, 6]], np.int32)
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = W.to_storage(rng.standard_normal((int(cu[-1]), Hq, D), dtype=np.float32), "bf16")
+    one = np.ones(Hkv, np.float32)
+    got = oracle.prefill_fp8(q, "bf16", cu, k, v, one, one, tables, lens, 0.5)
+    kb = W.to_storage(_torch_e4m3_to_f64(k).astype(np.float32), "bf16")
+    vb = W.to_storage(_torch_e4m3_to_f64(v).astype(np.float32), "bf16")
+    assert np.array_equal(W.storage_to_f32(kb, "bf16"), _torch_e4m3_to_f64(k).astype(np.float32))
+    want = oracle.prefill(q, cu, kb, vb, "bf16", tables, lens, 0.5)
+    assert np.array_equal(got, want)
+
+
 # ---------------------------------------------------------------- swap_blocks
 def test_swap_blocks_matches_numpy_indexing():
     """Device-side pools of 12 blocks, host-side pools of 7; out and back."""
