@@ -210,6 +210,46 @@ def main():
         return {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 1),
                 "frac_of_bf16_peak": round(flops / ms / 1e9 / BF16_DENSE_TFLOPS, 4)}
 
+    def prefill_fp8_row(bf16_ms):
+        """The same 8 x 512 chunks over FP8 (E4M3) pools with per-KV-head scales
+        (q bf16); the codes are widened to bf16 on their way into LDS."""
+        pb = W.prefill_bf16(args.seed)
+        f8 = W.fp8_pools(pb, args.seed + 2)
+        shape = (pb.NB, pb.B, pb.Hkv, pb.D)
+        idx = torch.from_numpy(pb.block_ids).to(dev)
+        k8 = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
+        v8 = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
+        k8.index_copy_(0, idx, torch.from_numpy(f8.k_blocks).to(dev))
+        v8.index_copy_(0, idx, torch.from_numpy(f8.v_blocks).to(dev))
+        ks8 = torch.from_numpy(f8.k_scale).to(dev)
+        vs8 = torch.from_numpy(f8.v_scale).to(dev)
+        del f8
+        q = up(pb.q, "bf16")
+        cu = torch.from_numpy(pb.cu_seqlens_q).to(dev)
+        tables = torch.from_numpy(pb.block_tables).to(dev)
+        lens = torch.from_numpy(pb.context_lens).to(dev)
+        out = torch.empty(tuple(q.shape), dtype=torch.float32, device=dev)
+        maxq = int(np.max(np.diff(pb.cu_seqlens_q)))
+        ws = torch.empty(max(pkv.prefill_workspace_size(pb.S, q.shape[0], maxq, pb.Hq, pb.Hkv, pb.D,
+                                                        pb.B, "fp8", pb.max_context_len), 1),
+                         dtype=torch.uint8, device=dev)
+
+        def run():
+            pkv.paged_attention_prefill_fp8(out, q, cu, maxq, k8, v8, ks8, vs8, tables, lens,
+                                            pb.max_context_len, pb.scale, workspace=ws)
+
+        ms, _ = time_fn(run, 10)
+        flops = 0
+        for s in range(pb.S):
+            Q = int(pb.cu_seqlens_q[s + 1] - pb.cu_seqlens_q[s])
+            L = int(pb.context_lens[s])
+            flops += 4 * pb.Hq * pb.D * sum(L - Q + i + 1 for i in range(Q))
+        log(f"[bench] prefill fp8: {ms:.3f} ms, {flops / ms / 1e9:.0f} TFLOP/s")
+        del k8, v8, q, out, ws
+        torch.cuda.empty_cache()
+        return {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 1),
+                "speedup_vs_bf16": round(bf16_ms / ms, 3)}
+
     if args.prefill_only:
         print(json.dumps({"prefill_bf16_8x512": prefill_row()}), flush=True)
         return
@@ -432,6 +472,7 @@ def main():
         torch.cuda.empty_cache()
 
         rows["prefill_bf16_8x512"] = prefill_row()
+        rows["prefill_fp8_8x512"] = prefill_fp8_row(rows["prefill_bf16_8x512"]["ms"])
         rows["mixed_llama3_8b_256_decodes_512_chunk"] = mixed_row()
         result["rows"] = rows
 

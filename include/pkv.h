@@ -253,6 +253,32 @@ pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const voi
                                        void* stream);
 
 /* ------------------------------------------------------------------------
+ * paged_attention_prefill_fp8 -- pkv_paged_attention_prefill over pools of
+ * OCP FP8 E4M3 codes, one fp32 scale per KV head for K and one for V (the
+ * pools of pkv_reshape_and_cache_fp8; "LLM inference, part 3" ch. 10: KV
+ * cache quantization), so chunked prefill can run over a quantized cache.
+ *
+ *   q, out             : as for pkv_paged_attention_prefill, q in q_dtype
+ *                        (f16 or bf16)
+ *   k_cache, v_cache   : device uint8 [NB, B, Hkv, D]
+ *   k_scale, v_scale   : device float [Hkv]
+ *   workspace          : pkv_prefill_workspace_size(..., PKV_FP8_E4M3, ...)
+ * Every cached element is read as code * scale of its KV head (exact in
+ * fp32); the codes are widened to q_dtype exactly and the products run on the
+ * matrix cores as in the 16-bit prefill.  Needs block_size >= 16 and at most
+ * 128 query heads per KV head (PKV_ERR_UNSUPPORTED otherwise).
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_paged_attention_prefill_fp8(void* out, pkv_dtype out_dtype, const void* q,
+                                           pkv_dtype q_dtype, const int32_t* cu_seqlens_q,
+                                           int32_t Tq, int32_t max_query_len, const void* k_cache,
+                                           const void* v_cache, const float* k_scale,
+                                           const float* v_scale, const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                           int32_t max_context_len, int32_t S, int32_t Hq,
+                                           int32_t Hkv, int32_t D, int32_t B, float scale,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * paged_attention_mixed -- one call for a batch mixing decode requests and
  * prefill chunks.
  *

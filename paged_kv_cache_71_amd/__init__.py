@@ -10,7 +10,8 @@ from ._binding import (BlockManager, PkvError, PkvOOM, copy_blocks, declared_sym
                        decode_cascade_workspace_size, decode_workspace_size, load_library,
                        mixed_workspace_size, paged_attention_decode,
                        paged_attention_decode_cascade, paged_attention_decode_fp8,
-                       paged_attention_mixed, paged_attention_prefill, prefill_workspace_size,
+                       paged_attention_mixed, paged_attention_prefill,
+                       paged_attention_prefill_fp8, prefill_workspace_size,
                        reshape_and_cache, reshape_and_cache_fp8, swap_blocks)
 
 __all__ = [
@@ -18,5 +19,6 @@ __all__ = [
     "decode_cascade_workspace_size", "decode_workspace_size", "load_library",
     "mixed_workspace_size", "paged_attention_decode", "paged_attention_decode_cascade",
     "paged_attention_decode_fp8", "paged_attention_mixed", "paged_attention_prefill",
+    "paged_attention_prefill_fp8",
     "prefill_workspace_size", "reshape_and_cache", "reshape_and_cache_fp8", "swap_blocks",
 ]

@@ -78,6 +78,8 @@ def load_library(path: str | None = None):
                                                     P]),
         "pkv_paged_attention_decode_fp8": (st, [P, st, P, st, P, P, P, P, P, i32, P, i32, i32, i32,
                                                 i32, i32, i32, f32, P, sz, P]),
+        "pkv_paged_attention_prefill_fp8": (st, [P, st, P, st, P, i32, i32, P, P, P, P, P, i32, P,
+                                                 i32, i32, i32, i32, i32, i32, f32, P, sz, P]),
         "pkv_bm_create": (st, [i32, i32, P, ctypes.POINTER(P)]),
         "pkv_bm_destroy": (None, [P]),
         "pkv_bm_add_seq": (st, [P, i32, I32P]),
@@ -423,6 +425,38 @@ def paged_attention_decode_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B,
         float(scale), ws_ptr, ws_bytes, _stream(stream)), "paged_attention_decode_fp8")
+    return out
+
+
+def paged_attention_prefill_fp8(out, q, cu_seqlens_q, max_query_len: int, k_cache, v_cache, k_scale,
+                                v_scale, block_tables, context_lens, max_context_len: int,
+                                scale: float, workspace=None, stream=None):
+    """Causal chunk attention over FP8 pools read as code * scale of the KV
+    head; q is f16 or bf16.  ``workspace`` as for paged_attention_prefill."""
+    torch = _torch()
+    lib = load_library()
+    Tq, Hq, D = q.shape
+    NB, B, Hkv, D2 = k_cache.shape
+    S = cu_seqlens_q.shape[0] - 1
+    if D2 != D or v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("paged_attention_prefill_fp8: shape mismatch")
+    if k_scale.shape != (Hkv,) or v_scale.shape != (Hkv,):
+        raise ValueError("paged_attention_prefill_fp8: scales must be [Hkv]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("paged_attention_prefill_fp8: block_tables [S, max_nb] / context_lens [S]")
+    need = prefill_workspace_size(S, Tq, int(max_query_len), Hq, Hkv, D, B, "fp8", int(max_context_len))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pkv_paged_attention_prefill_fp8(
+        _dev(out, "out"), dtype_code(out), _dev(q, "q"), dtype_code(q),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), Tq, int(max_query_len),
+        _fp8_pool(k_cache, "k_cache"), _fp8_pool(v_cache, "v_cache"),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B,
+        float(scale), ws_ptr, ws_bytes, _stream(stream)), "paged_attention_prefill_fp8")
     return out
 
 

@@ -292,9 +292,11 @@ pkv_status pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype, const 
 }  // extern "C"
 
 // Validates the prefill arguments and fills *a; *empty: nothing to compute.
+// kv_dtype is q's dtype; fp8: the pools hold E4M3 codes with per-head scales.
 static pkv_status prefill_args(void* out, pkv_dtype out_dtype, const void* q,
                                const int32_t* cu_seqlens_q, int32_t Tq, int32_t max_query_len,
                                const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                               bool fp8, const float* k_scale, const float* v_scale,
                                const int32_t* block_tables, int32_t max_blocks_per_seq,
                                const int32_t* context_lens, int32_t max_context_len, int32_t S,
                                int32_t Hq, int32_t Hkv, int32_t D, int32_t B, float scale,
@@ -315,10 +317,17 @@ static pkv_status prefill_args(void* out, pkv_dtype out_dtype, const void* q,
               "prefill: max_context_len %d exceeds table capacity %d x %d", max_context_len,
               max_blocks_per_seq, B);
   PKV_REQUIRE(scale == scale, PKV_ERR_INVALID_ARG, "prefill: scale is NaN");
+  PKV_REQUIRE(!fp8 || kv_dtype != PKV_F32, PKV_ERR_UNSUPPORTED, "prefill_fp8: q must be f16 or bf16");
+  PKV_REQUIRE((int64_t)B * Hkv * D * (fp8 ? 1 : dt_bytes(kv_dtype)) < ((int64_t)1 << 31),
+              PKV_ERR_UNSUPPORTED, "prefill: one block of one pool must be smaller than 2 GiB");
+  PKV_REQUIRE(!fp8 || (B >= 16 && Hq / Hkv <= 128), PKV_ERR_UNSUPPORTED,
+              "prefill_fp8: needs block_size >= 16 and at most 128 query heads per KV head "
+              "(B=%d, G=%d)", B, Hq / Hkv);
   if (S == 0 || Tq == 0) return PKV_OK;
   *empty = false;
   PKV_REQUIRE(out && q && cu_seqlens_q && k_cache && v_cache && block_tables && context_lens,
               PKV_ERR_INVALID_ARG, "prefill: null pointer");
+  PKV_REQUIRE(!fp8 || (k_scale && v_scale), PKV_ERR_INVALID_ARG, "prefill_fp8: null scale array");
   a->out = out;
   a->q = q;
   a->cu_seqlens_q = cu_seqlens_q;
@@ -342,6 +351,9 @@ static pkv_status prefill_args(void* out, pkv_dtype out_dtype, const void* q,
   a->tiles_per_split = 0;
   a->ws_o = nullptr;
   a->ws_ml = nullptr;
+  a->q_dt = kv_dtype;
+  a->k_scale = fp8 ? k_scale : nullptr;
+  a->v_scale = fp8 ? v_scale : nullptr;
   return PKV_OK;
 }
 
@@ -382,9 +394,9 @@ pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const voi
   PrefillArgs a;
   bool empty = true;
   const pkv_status st = prefill_args(out, out_dtype, q, cu_seqlens_q, Tq, max_query_len, k_cache,
-                                     v_cache, kv_dtype, block_tables, max_blocks_per_seq,
-                                     context_lens, max_context_len, S, Hq, Hkv, D, B, scale, &a,
-                                     &empty);
+                                     v_cache, kv_dtype, false, nullptr, nullptr, block_tables,
+                                     max_blocks_per_seq, context_lens, max_context_len, S, Hq, Hkv,
+                                     D, B, scale, &a, &empty);
   if (st != PKV_OK || empty) return st;
   const PrefillPlan plan = plan_prefill(kv_dtype, S, Tq, max_query_len, Hq, Hkv, D, B, max_context_len);
   PKV_REQUIRE(plan.workspace_bytes == 0 || (workspace && workspace_bytes >= plan.workspace_bytes),
@@ -392,6 +404,31 @@ pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const voi
               plan.workspace_bytes, workspace ? workspace_bytes : (size_t)0);
   attach_prefill_plan(plan, workspace, &a);
   return launch_prefill(kv_dtype, a, static_cast<hipStream_t>(stream));
+}
+
+pkv_status pkv_paged_attention_prefill_fp8(void* out, pkv_dtype out_dtype, const void* q,
+                                           pkv_dtype q_dtype, const int32_t* cu_seqlens_q,
+                                           int32_t Tq, int32_t max_query_len, const void* k_cache,
+                                           const void* v_cache, const float* k_scale,
+                                           const float* v_scale, const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                           int32_t max_context_len, int32_t S, int32_t Hq,
+                                           int32_t Hkv, int32_t D, int32_t B, float scale,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  PrefillArgs a;
+  bool empty = true;
+  const pkv_status st = prefill_args(out, out_dtype, q, cu_seqlens_q, Tq, max_query_len, k_cache,
+                                     v_cache, q_dtype, true, k_scale, v_scale, block_tables,
+                                     max_blocks_per_seq, context_lens, max_context_len, S, Hq, Hkv,
+                                     D, B, scale, &a, &empty);
+  if (st != PKV_OK || empty) return st;
+  const PrefillPlan plan = plan_prefill(DT_FP8, S, Tq, max_query_len, Hq, Hkv, D, B, max_context_len);
+  PKV_REQUIRE(plan.workspace_bytes == 0 || (workspace && workspace_bytes >= plan.workspace_bytes),
+              PKV_ERR_WORKSPACE, "prefill_fp8: workspace of %zu bytes needed, %zu given",
+              plan.workspace_bytes, workspace ? workspace_bytes : (size_t)0);
+  attach_prefill_plan(plan, workspace, &a);
+  return launch_prefill(DT_FP8, a, static_cast<hipStream_t>(stream));
 }
 
 pkv_status pkv_mixed_workspace_size(int32_t S, int32_t num_decode, int32_t Tq,
@@ -430,8 +467,9 @@ pkv_status pkv_paged_attention_mixed(void* out, pkv_dtype out_dtype, const void*
   PrefillArgs pa;
   bool empty = true;
   pkv_status st = prefill_args(out, out_dtype, q, cu_seqlens_q, Tq, max_query_len, k_cache,
-                               v_cache, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
-                               max_context_len, S, Hq, Hkv, D, B, scale, &pa, &empty);
+                               v_cache, kv_dtype, false, nullptr, nullptr, block_tables,
+                               max_blocks_per_seq, context_lens, max_context_len, S, Hq, Hkv, D, B,
+                               scale, &pa, &empty);
   if (st != PKV_OK || empty) return st;
   PKV_REQUIRE((int64_t)B * Hkv * D * dt_bytes(kv_dtype) < ((int64_t)1 << 31), PKV_ERR_UNSUPPORTED,
               "mixed: one block of one pool must be smaller than 2 GiB");

@@ -185,25 +185,6 @@ __device__ __forceinline__ uint2 ld8_stream(const char* p) {
   return make_uint2(v.x, v.y);
 }
 
-// 8 OCP E4M3 codes (one lane's K load) -> 8 elements of the 16-bit dtype DT,
-// in order; every E4M3 value is exact in bf16 and in fp16 (unit scale).
-template <int DT>
-__device__ __forceinline__ uint4 fp8x8_to16(const uint2 v) {
-  if constexpr (DT == DT_BF16) {
-    return make_uint4(
-        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, false)),
-        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, true)),
-        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, false)),
-        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, true)));
-  } else {
-    return make_uint4(
-        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 1.f, false)),
-        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 1.f, true)),
-        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 1.f, false)),
-        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 1.f, true)));
-  }
-}
-
 // 8 OCP E4M3 codes (one lane's V load) -> 8 fp32 values, exact.
 __device__ __forceinline__ void fp8x8_to_f32(const uint2 v, float* f) {
   const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(v.x, false);

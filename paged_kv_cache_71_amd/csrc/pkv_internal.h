@@ -39,6 +39,25 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// 8 OCP E4M3 codes -> 8 elements of the 16-bit dtype DT, in order; every
+// E4M3 value is exact in bf16 and in fp16 (unit scale).
+template <int DT>
+__device__ __forceinline__ uint4 fp8x8_to16(const uint2 v) {
+  if constexpr (DT == DT_BF16) {
+    return make_uint4(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, true)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, true)));
+  } else {
+    return make_uint4(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 1.f, true)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 1.f, true)));
+  }
+}
+
 // Store one fp32 result into an output tensor of dtype out_dt.
 __device__ __forceinline__ void store_out(void* out, int out_dt, int64_t idx, float v) {
   if (out_dt == DT_F32) {
@@ -159,6 +178,11 @@ struct PrefillArgs {
   int32_t n_split, tiles_per_split;
   float* ws_o;   // [n_split][Tq * Hq][D] unnormalised outputs
   float* ws_ml;  // [n_split][Tq * Hq][2] running max (log2 units) and weight sum
+  // FP8 pools (launch_prefill with DT_FP8): q's 16-bit dtype and the per-KV-head
+  // scales the codes are multiplied by
+  int32_t q_dt;
+  const float* k_scale;
+  const float* v_scale;
 };
 // Split plan of a prefill launch: a deterministic function of the arguments
 // (and of the device's CU count), so equal calls give equal bits.

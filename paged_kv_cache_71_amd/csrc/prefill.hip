@@ -35,6 +35,7 @@
 //
 // fp32 KV: a plain vector-ALU kernel (one wave per query token and KV head).
 #include <algorithm>
+#include <type_traits>
 
 #include "pkv_internal.h"
 
@@ -425,11 +426,15 @@ __device__ __forceinline__ float group_max_raw(float x) {
   return max3_raw(__uint_as_float(r32[0]), __uint_as_float(r32[1]), __uint_as_float(r32[0]));
 }
 
-template <int DT, int D>
+// F8: the pools hold OCP E4M3 codes (one scale per KV head); they are widened
+// to DT (q's dtype, exact) as they go into LDS, so everything after the
+// staging is the 16-bit kernel.
+template <int DT, int D, bool F8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_tile_kernel(
     const PrefillArgs a) {
   constexpr int QB = kTileQB;
-  constexpr int ES = 2;
+  constexpr int ES = 2;            // q and LDS element bytes
+  constexpr int ESK = F8 ? 1 : 2;  // pool element bytes
   constexpr int NKK = D / 32;                 // k-steps of S^T = K Q^T
   constexpr int NDB = D / 16;                 // 16-wide d blocks of O^T
   // LDS row pitches: 32 bytes of skew per row make both the 16-byte K reads
@@ -437,8 +442,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // costs the K reads 1.6x)
   constexpr int KP = D * ES + 32;
   constexpr int VP = D * ES + 32;
-  constexpr int CPR = D * ES / 16;            // 16-byte chunks per row
+  constexpr int CPR = F8 ? 8 : D * ES / 16;      // staging chunks per row
+  constexpr int CBP = D * ESK / CPR;             // pool bytes per chunk (16, or 8 for FP8 D = 64)
+  constexpr int CBL = D * ES / CPR;              // LDS bytes per chunk (16 or 32)
   constexpr int NCH = kTileKV * CPR / kThreads;  // chunks per thread per tile, K and V each
+  using Chunk = std::conditional_t<CBP == 16, uint4, uint2>;
+  static_assert(CBP == 16 || CBP == 8, "staging chunk");
   constexpr int RW = kWaves * 16 * QB;        // query rows per workgroup
   constexpr bool PSPLIT = DT == DT_BF16;
   static_assert(NCH >= 1 && kTileKV * CPR % kThreads == 0, "staging split");
@@ -509,8 +518,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Scores are kept as raw q.k; the softmax scale enters the exponent through
   // one fma.  A negative scale flips the sign of q instead (exact for 16-bit
   // values), so the factor used is |scale| and the running max stays a max.
-  const float sl = fabsf(a.scale_log2);
-  const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  // FP8 pools: the K scale joins the softmax scale, the V scale the output.
+  const float kscale = F8 ? a.k_scale[kvh] : 1.f;
+  const float oscale = F8 ? a.v_scale[kvh] : 1.f;
+  const float sl = fabsf(a.scale_log2 * kscale);
+  const uint32_t qflip = a.scale_log2 * kscale < 0.f ? 0x80008000u : 0u;
 
   // Q^T fragments: lane holds Q[row][32 kk + 8 g4 .. + 7]
   u32x4_t qf[QB][NKK];
@@ -528,17 +540,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) asm volatile("" ::"v"(qf[c][kk]));
 
-  const int64_t row_stride = (int64_t)a.Hkv * D * ES;
+  const int64_t row_stride = (int64_t)a.Hkv * D * ESK;
   const int64_t blk_stride = row_stride * a.B;
   const int rs32 = (int)row_stride;
   const int log2B = a.log2B;
   const int bmask = a.B - 1;
-  const char* kpool = static_cast<const char*>(a.k_cache) + (int64_t)kvh * D * ES;
-  const char* vpool = static_cast<const char*>(a.v_cache) + (int64_t)kvh * D * ES;
+  const char* kpool = static_cast<const char*>(a.k_cache) + (int64_t)kvh * D * ESK;
+  const char* vpool = static_cast<const char*>(a.v_cache) + (int64_t)kvh * D * ESK;
   const int32_t* tbv = a.block_tables + (int64_t)s * a.max_nb;
 
-  // Staging: chunk i of a thread is 16 bytes at column ch % CPR of tile row
-  // ch / CPR (ch = tid + 256 i).  The rows a wave stages for one chunk lie in
+  // Staging: chunk i of a thread is column ch % CPR of tile row ch / CPR
+  // (ch = tid + 256 i): CBP pool bytes, CBL bytes in LDS.  The rows a wave stages for one chunk lie in
   // one 16-token half of the tile, and a half lies in one block (B >= 16), so
   // a chunk's pool address is a per-wave base plus a per-lane offset.
   int crow[NCH], ccol[NCH], chalf[NCH];
@@ -549,7 +561,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     crow[i] = ch / CPR;
     ccol[i] = ch - crow[i] * CPR;
     chalf[i] = __builtin_amdgcn_readfirstlane(crow[i] >> 4);
-    loff[i] = (uint32_t)((crow[i] & 15) * rs32 + ccol[i] * 16);
+    loff[i] = (uint32_t)((crow[i] & 15) * rs32 + ccol[i] * CBP);
   }
   // Block table entries of tile t: lane 0 the block of its first 16 tokens,
   // lane 1 of the next 16 (clamped to the last visible token, so the table is
@@ -560,7 +572,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
   // global -> registers: the chunks of tile t (entries e0, e1 of its halves).
   // Rows past the visible range (last tile only) repeat its last row.
-  auto gload = [&](uint4 (&dst)[NCH], const char* pool, int t, int e0, int e1)
+  auto ldc = [](const char* p) __attribute__((always_inline)) -> Chunk {
+    return *reinterpret_cast<const Chunk*>(p);
+  };
+  auto gload = [&](Chunk (&dst)[NCH], const char* pool, int t, int e0, int e1)
       __attribute__((always_inline)) {
     const int kv0 = t * kTileKV;
     if (kv0 + kTileKV <= kv_end) {
@@ -569,7 +584,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int h = chalf[i];
         const char* base = pool + (int64_t)(h ? e1 : e0) * blk_stride +
                            (int64_t)(((kv0 + 16 * h) & bmask) * rs32);
-        dst[i] = ld16(base + loff[i]);
+        dst[i] = ldc(base + loff[i]);
       }
     } else {
 #pragma unroll
@@ -577,13 +592,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int h = chalf[i];
         const int kvc = min(kv0 + crow[i], kv_end - 1);
         const char* base = pool + (int64_t)(h ? e1 : e0) * blk_stride;
-        dst[i] = ld16(base + (uint32_t)((kvc & bmask) * rs32 + ccol[i] * 16));
+        dst[i] = ldc(base + (uint32_t)((kvc & bmask) * rs32 + ccol[i] * CBP));
       }
     }
   };
-  auto lstore = [&](char* buf, int pitch, const uint4 (&src)[NCH]) __attribute__((always_inline)) {
+  auto lstore = [&](char* buf, int pitch, const Chunk (&src)[NCH]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) *reinterpret_cast<uint4*>(buf + crow[i] * pitch + ccol[i] * 16) = src[i];
+    for (int i = 0; i < NCH; ++i) {
+      char* dst = buf + crow[i] * pitch + ccol[i] * CBL;
+      if constexpr (!F8) {
+        *reinterpret_cast<uint4*>(dst) = src[i];
+      } else if constexpr (CBP == 16) {
+        *reinterpret_cast<uint4*>(dst) = fp8x8_to16<DT>(make_uint2(src[i].x, src[i].y));
+        *reinterpret_cast<uint4*>(dst + 16) = fp8x8_to16<DT>(make_uint2(src[i].z, src[i].w));
+      } else {
+        *reinterpret_cast<uint4*>(dst) = fp8x8_to16<DT>(src[i]);
+      }
+    }
   };
   // LDS writes of this thread are complete and every wave has arrived; global
   // loads already issued stay in flight (no memory fence on the barrier)
@@ -616,9 +641,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // on either side of it.  K(t) sits in LDS buffer t % 2 during steps t-2 ..
   // t-1, V(t) in buffer t % 2 during steps t .. t+1.  Tile indices past the
   // last tile are clamped to it (their loads repeat it and are never used).
-  uint4 sk[NCH], sv[NCH];
+  Chunk sk[NCH], sv[NCH];
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) sv[i] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < NCH; ++i) sv[i] = Chunk{};
   int ea0, ea1, eb0, eb1, ent;  // entries of tiles j+1 and j+2; vector of tile j+3
   {
     const int en0 = ent_load(t0);
@@ -806,7 +831,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int d = 0; d < NDB; ++d)
         *reinterpret_cast<float4*>(po + 16 * d + 4 * g4) =
-            make_float4(o[d][c][0], o[d][c][1], o[d][c][2], o[d][c][3]);
+            make_float4(o[d][c][0] * oscale, o[d][c][1] * oscale, o[d][c][2] * oscale,
+                        o[d][c][3] * oscale);
       if (g4 == 0) *reinterpret_cast<float2*>(a.ws_ml + (rec + orow[c]) * 2) = make_float2(m[c], lsum[c]);
     }
     return;
@@ -814,7 +840,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int c = 0; c < QB; ++c) {
     if (!valid[c]) continue;
-    const float inv = 1.f / lsum[c];
+    const float inv = F8 ? oscale / lsum[c] : 1.f / lsum[c];
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
       const int64_t off = (int64_t)orow[c] * D + 16 * d + 4 * g4;
@@ -947,7 +973,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillArgs a) {
   }
 }
 
-template <int DT, int D>
+template <int DT, int D, bool F8>
 pkv_status launch_tile(const PrefillArgs& a, hipStream_t stream) {
   constexpr int RW = kWaves * 16 * kTileQB;
   const int G = a.Hq / a.Hkv;
@@ -956,7 +982,7 @@ pkv_status launch_tile(const PrefillArgs& a, hipStream_t stream) {
   const int64_t grid = nqt * a.S * a.Hkv * a.n_split;
   if (grid == 0) return PKV_OK;
   if (grid > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "prefill grid too large");
-  hipLaunchKernelGGL((prefill_tile_kernel<DT, D>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((prefill_tile_kernel<DT, D, F8>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, a);
   pkv_status st = check_launch("paged_attention_prefill");
   if (st != PKV_OK || a.n_split <= 1) return st;
@@ -969,7 +995,7 @@ pkv_status launch_tile(const PrefillArgs& a, hipStream_t stream) {
 template <int DT, int D>
 pkv_status launch_mfma(const PrefillArgs& a, hipStream_t stream) {
   // blocks of at least 16 tokens and groups that fit a workgroup: tile kernel
-  if (a.B >= 16 && a.Hq / a.Hkv <= kWaves * 16 * kTileQB) return launch_tile<DT, D>(a, stream);
+  if (a.B >= 16 && a.Hq / a.Hkv <= kWaves * 16 * kTileQB) return launch_tile<DT, D, false>(a, stream);
   const int G = a.Hq / a.Hkv;
   if (G > kRowsPerWG) return fail(PKV_ERR_UNSUPPORTED, "prefill: group size %d > %d", G, kRowsPerWG);
   const int TQ = kRowsPerWG / G;
@@ -1024,6 +1050,17 @@ PrefillPlan plan_prefill(int kv_dt, int32_t S, int32_t Tq, int32_t max_query_len
 }
 
 pkv_status launch_prefill(int kv_dt, const PrefillArgs& a, hipStream_t stream) {
+  if (kv_dt == DT_FP8) {
+    // FP8 pools: the tile kernel only (blocks of >= 16 tokens, groups that fit
+    // a workgroup), q in f16 or bf16
+    if (a.B < 16 || a.Hq / a.Hkv > kWaves * 16 * kTileQB)
+      return fail(PKV_ERR_UNSUPPORTED, "prefill_fp8: block_size %d / group %d", a.B, a.Hq / a.Hkv);
+    if (a.q_dt == DT_BF16 && a.D == 128) return launch_tile<DT_BF16, 128, true>(a, stream);
+    if (a.q_dt == DT_BF16 && a.D == 64) return launch_tile<DT_BF16, 64, true>(a, stream);
+    if (a.q_dt == DT_F16 && a.D == 128) return launch_tile<DT_F16, 128, true>(a, stream);
+    if (a.q_dt == DT_F16 && a.D == 64) return launch_tile<DT_F16, 64, true>(a, stream);
+    return fail(PKV_ERR_UNSUPPORTED, "prefill_fp8: q dtype %d, head_dim %d", a.q_dt, a.D);
+  }
   if (kv_dt == DT_F32) {
     switch (a.D) {
       case 64: return launch_f32<64>(a, stream);

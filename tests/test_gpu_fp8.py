@@ -238,3 +238,77 @@ def test_decode_fp8_llama3_8b_full_size_sampled(gpu_lib):
     seqs = sorted(set([int(order[0]), int(order[-1])] +
                       np.random.default_rng(1).choice(b.S, 10, replace=False).tolist()))
     check(gpu_lib, b, seed=1, seqs=seqs)
+
+
+# ---------------------------------------------------------------- prefill over FP8 pools
+def gpu_prefill_fp8(pkv, d: Fp8Dev, out_dtype="f32"):
+    b = d.b
+    out = torch.full(tuple(d.q.shape), float("nan"), dtype=TORCH_DT[out_dtype], device="cuda")
+    maxq = int(np.max(np.diff(b.cu_seqlens_q)))
+    pkv.paged_attention_prefill_fp8(out, d.q, torch.from_numpy(b.cu_seqlens_q).cuda(), maxq,
+                                    d.k_cache, d.v_cache, d.k_scale, d.v_scale, d.block_tables,
+                                    d.context_lens, b.max_context_len, b.scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_prefill(pkv, b, seed=0, rows=None):
+    print(f"[fp8 prefill] {b.name} S={b.S} Hq={b.Hq} Hkv={b.Hkv} D={b.D} B={b.B} q={b.dtype} "
+          f"Tq={b.q.shape[0]} maxL={b.max_context_len}", flush=True)
+    f = W.fp8_pools(b, seed)
+    out = gpu_prefill_fp8(pkv, Fp8Dev(b, f))
+    _, _, tables = b.compact_pool(extra_poison_blocks=0)
+    ref = oracle.prefill_fp8(b.q, b.dtype, b.cu_seqlens_q, f.k_blocks, f.v_blocks, f.k_scale,
+                             f.v_scale, tables, b.context_lens, b.scale, rows=rows)
+    if rows is not None:
+        ref = ref[rows]
+        out = out[torch.as_tensor(np.asarray(rows)).cuda()]
+    err = max_abs(out, ref)
+    assert err <= TOL[b.dtype], f"max abs err {err}"
+    return err
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("Hq,Hkv,D,B", [(8, 8, 128, 16), (32, 8, 128, 16), (4, 1, 64, 32),
+                                        (16, 2, 128, 32), (24, 8, 64, 16)])
+def test_prefill_fp8_small_varlen(gpu_lib, dtype, Hq, Hkv, D, B):
+    prior, chunks = [0, 7, 30, 100, 0, 64], [5, 9, 16, 77, 1, 40]
+    check_prefill(gpu_lib, W.varlen_prefill(Hq + D + B + 1, prior, chunks, Hq, Hkv, D, B, dtype),
+                  seed=Hq + B)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prefill_fp8_split_long_contexts(gpu_lib, dtype):
+    """Few sequences with long contexts: the KV ranges are split and merged,
+    the V scale applied to every partial result."""
+    b = W.varlen_prefill(31, [5000, 300, 2100], [100, 37, 64], 32, 8, 128, 16, dtype)
+    assert gpu_lib.prefill_workspace_size(b.S, b.q.shape[0], 100, 32, 8, 128, 16, "fp8",
+                                          b.max_context_len) > 0
+    check_prefill(gpu_lib, b, seed=4)
+
+
+def test_prefill_fp8_one_token_chunks_match_fp8_decode(gpu_lib):
+    """A chunk of one token is a decode: the FP8 prefill and the FP8 decode of
+    the same pools agree within tolerance (two different kernels)."""
+    b = W.varlen_prefill(12, [0, 15, 300, 1000], [1, 1, 1, 1], 32, 8, 128, 16, "bf16")
+    f = W.fp8_pools(b, 2)
+    d = Fp8Dev(b, f)
+    pre = gpu_prefill_fp8(gpu_lib, d)
+    dec = gpu_decode(gpu_lib, d)
+    assert float((pre - dec).abs().max()) <= 2 * TOL["bf16"]
+
+
+def test_prefill_fp8_rejects_small_blocks(gpu_lib):
+    b = W.varlen_prefill(13, [20], [8], 8, 2, 128, 8, "bf16")
+    d = Fp8Dev(b, W.fp8_pools(b, 0))
+    with pytest.raises(gpu_lib.PkvError, match="block_size"):
+        gpu_prefill_fp8(gpu_lib, d)
+
+
+def test_prefill_fp8_full_size_sampled(gpu_lib):
+    """The benchmarked prefill workload (8 x 512-token chunks after 4k-33k
+    tokens) over FP8 pools, sampled rows against the oracle."""
+    b = W.prefill_bf16(0)
+    rng = np.random.default_rng(5)
+    rows = sorted(set([0, 511, 4095, 2048] + rng.choice(b.q.shape[0], 10, replace=False).tolist()))
+    check_prefill(gpu_lib, b, seed=7, rows=rows)
