@@ -82,6 +82,14 @@ def test_long_rows_span_many_waves(gpu_lib, dtype):
     check(gpu_lib, W.decode_batch(5, [8192], 32, 8, 128, 16, dtype))
 
 
+def test_context_of_131072_tokens(gpu_lib):
+    """A 131,072-token sequence (8,192 blocks, 512 MiB of bf16 K+V) beside a
+    short and a 70,000-token one: rows cut across the whole wave set, block
+    offsets past 2^31 bytes in the pool."""
+    b = W.decode_batch(7, [131072, 5, 70000], 32, 8, 128, 16, "bf16", NB=70000)
+    check(gpu_lib, b)
+
+
 def test_more_sequences_than_one_launch(gpu_lib):
     """4100 short sequences (some empty): more than one split + merge launch pair."""
     lengths = np.random.default_rng(3).integers(0, 40, 4100)

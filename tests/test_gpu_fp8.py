@@ -312,3 +312,9 @@ def test_prefill_fp8_full_size_sampled(gpu_lib):
     rng = np.random.default_rng(5)
     rows = sorted(set([0, 511, 4095, 2048] + rng.choice(b.q.shape[0], 10, replace=False).tolist()))
     check_prefill(gpu_lib, b, seed=7, rows=rows)
+
+
+def test_prefill_fp8_context_of_131072_tokens(gpu_lib):
+    """FP8 pools, a 256-token chunk at the end of a 131,072-token context."""
+    b = W.varlen_prefill(9, [130816], [256], 32, 8, 128, 16, "bf16")
+    check_prefill(gpu_lib, b, seed=3, rows=[0, 100, 255])

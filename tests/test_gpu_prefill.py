@@ -149,3 +149,10 @@ def test_split_one_long_prompt_full_size_sampled(gpu_lib):
     assert gpu_lib.prefill_workspace_size(1, 512, 512, 32, 8, 128, 16, "bf16", b.max_context_len) > 0
     rows = [0, 1, 31, 32, 200, 480, 511]
     check(gpu_lib, b, rows=rows)
+
+
+def test_prefill_context_of_131072_tokens(gpu_lib):
+    """A 256-token chunk at the end of a 131,072-token context: the KV range
+    is split into long splits; sampled rows against the oracle."""
+    b = W.varlen_prefill(8, [130816], [256], 32, 8, 128, 16, "bf16")
+    check(gpu_lib, b, rows=[0, 1, 127, 128, 255])
