@@ -316,8 +316,12 @@ struct Cursor {
 // the matrix cores; everything else as in the vector path (see below).
 // F8: the pools hold E4M3 codes (DT is then the dtype of q and of the widened
 // elements); the lane layout is DT's, with 8-byte instead of 16-byte loads.
+// The two-waves-per-SIMD bound keeps the matrix-core results in ordinary
+// VGPRs (no accumulation registers, hence no copies out of them before the
+// softmax): FP8 decode 176 -> 173 us on the Llama-3-8B batch, bf16 unchanged.
 template <int DT, int D, int GC, bool UNI, bool MF, bool F8>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(
+    const DecodeArgs a) {
   using Gm = Geo<DT, D>;
   constexpr int ES = Gm::ES, EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
   constexpr int NLD = Gm::NLD, TILE = Gm::TILE;
