@@ -167,6 +167,20 @@ pkv_status pkv_paged_attention_decode_cascade(
     const int32_t* group_prefix_lens, int32_t n_groups, int32_t max_group_size,
     int32_t max_prefix_len, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Cascade decode over FP8 (E4M3) pools with per-KV-head scales: the
+ * arguments of pkv_paged_attention_decode_cascade with q in q_dtype (f16 or
+ * bf16) and k_scale / v_scale as for pkv_paged_attention_decode_fp8; the
+ * workspace is pkv_decode_cascade_workspace_size(..., q_dtype, ...).  Same
+ * result, within the FP8 decode's tolerance, as pkv_paged_attention_decode_fp8
+ * on the same pools ("LLM inference, part 3" ch. 10 for the cache format). */
+pkv_status pkv_paged_attention_decode_cascade_fp8(
+    void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* k_cache,
+    const void* v_cache, const float* k_scale, const float* v_scale, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len, int32_t S,
+    int32_t Hq, int32_t Hkv, int32_t D, int32_t B, float scale, const int32_t* cu_group_seqs,
+    const int32_t* group_prefix_lens, int32_t n_groups, int32_t max_group_size,
+    int32_t max_prefix_len, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * FP8 KV cache -- the pools hold OCP E4M3 codes, one byte per element, with
  * one fp32 scale per KV head for K and one for V.
@@ -313,6 +327,23 @@ pkv_status pkv_paged_attention_mixed(void* out, pkv_dtype out_dtype, const void*
                                      int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
                                      float scale, void* workspace, size_t workspace_bytes,
                                      void* stream);
+
+/* Mixed batch over FP8 (E4M3) pools with per-KV-head scales: the arguments of
+ * pkv_paged_attention_mixed with q in q_dtype (f16 or bf16) and k_scale /
+ * v_scale as for pkv_paged_attention_decode_fp8; the workspace is
+ * pkv_mixed_workspace_size(..., PKV_FP8_E4M3, ...).  Every row equals what
+ * pkv_paged_attention_decode_fp8 / pkv_paged_attention_prefill_fp8 give for
+ * it, bit for bit; the chunks need block_size >= 16. */
+pkv_status pkv_paged_attention_mixed_fp8(void* out, pkv_dtype out_dtype, const void* q,
+                                         pkv_dtype q_dtype, const int32_t* cu_seqlens_q,
+                                         int32_t Tq, int32_t num_decode, int32_t max_query_len,
+                                         const void* k_cache, const void* v_cache,
+                                         const float* k_scale, const float* v_scale,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t max_context_len,
+                                         int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                         float scale, void* workspace, size_t workspace_bytes,
+                                         void* stream);
 
 /* ------------------------------------------------------------------------
  * copy_blocks -- batched whole-block copies for copy-on-write.

@@ -76,6 +76,11 @@ def load_library(path: str | None = None):
         "pkv_paged_attention_decode_cascade": (st, [P, st, P, P, P, st, P, i32, P, i32, i32, i32,
                                                     i32, i32, i32, f32, P, P, i32, i32, i32, P, sz,
                                                     P]),
+        "pkv_paged_attention_decode_cascade_fp8": (st, [P, st, P, st, P, P, P, P, P, i32, P, i32,
+                                                        i32, i32, i32, i32, i32, f32, P, P, i32,
+                                                        i32, i32, P, sz, P]),
+        "pkv_paged_attention_mixed_fp8": (st, [P, st, P, st, P, i32, i32, i32, P, P, P, P, P, i32,
+                                               P, i32, i32, i32, i32, i32, i32, f32, P, sz, P]),
         "pkv_paged_attention_decode_fp8": (st, [P, st, P, st, P, P, P, P, P, i32, P, i32, i32, i32,
                                                 i32, i32, i32, f32, P, sz, P]),
         "pkv_paged_attention_prefill_fp8": (st, [P, st, P, st, P, i32, i32, P, P, P, P, P, i32, P,
@@ -368,6 +373,79 @@ def paged_attention_decode_cascade(out, q, k_cache, v_cache, block_tables, conte
         float(scale), _dev(cu_group_seqs, "cu_group_seqs", torch.int32),
         _dev(group_prefix_lens, "group_prefix_lens", torch.int32), n_groups, int(max_group_size),
         int(max_prefix_len), ws_ptr, ws_bytes, _stream(stream)), "paged_attention_decode_cascade")
+    return out
+
+
+def paged_attention_decode_cascade_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                       context_lens, max_context_len: int, scale: float,
+                                       cu_group_seqs, group_prefix_lens, max_group_size: int,
+                                       max_prefix_len: int, workspace=None, stream=None):
+    """paged_attention_decode_cascade over FP8 pools read as code * scale of
+    the KV head; q is f16 or bf16."""
+    torch = _torch()
+    lib = load_library()
+    S, Hq, D = q.shape
+    NB, B, Hkv, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("paged_attention_decode_cascade_fp8: shape mismatch")
+    if k_scale.shape != (Hkv,) or v_scale.shape != (Hkv,):
+        raise ValueError("paged_attention_decode_cascade_fp8: scales must be [Hkv]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("paged_attention_decode_cascade_fp8: block_tables [S, max_nb] / context_lens [S]")
+    n_groups = cu_group_seqs.shape[0] - 1
+    if group_prefix_lens.shape != (n_groups,):
+        raise ValueError("paged_attention_decode_cascade_fp8: group_prefix_lens must be [n_groups]")
+    qdt = {1: "f16", 2: "bf16"}.get(dtype_code(q))
+    if qdt is None:
+        raise TypeError("paged_attention_decode_cascade_fp8: q must be f16 or bf16")
+    need = decode_cascade_workspace_size(S, Hq, Hkv, D, B, max_context_len, n_groups,
+                                         max_group_size, max_prefix_len, qdt)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pkv_paged_attention_decode_cascade_fp8(
+        _dev(out, "out"), dtype_code(out), _dev(q, "q"), dtype_code(q),
+        _fp8_pool(k_cache, "k_cache"), _fp8_pool(v_cache, "v_cache"),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B,
+        float(scale), _dev(cu_group_seqs, "cu_group_seqs", torch.int32),
+        _dev(group_prefix_lens, "group_prefix_lens", torch.int32), n_groups, int(max_group_size),
+        int(max_prefix_len), ws_ptr, ws_bytes, _stream(stream)), "paged_attention_decode_cascade_fp8")
+    return out
+
+
+def paged_attention_mixed_fp8(out, q, cu_seqlens_q, num_decode: int, max_query_len: int, k_cache,
+                              v_cache, k_scale, v_scale, block_tables, context_lens,
+                              max_context_len: int, scale: float, workspace=None, stream=None):
+    """paged_attention_mixed over FP8 pools read as code * scale of the KV
+    head; q is f16 or bf16.  Same rows as paged_attention_decode_fp8 /
+    paged_attention_prefill_fp8, bit for bit."""
+    torch = _torch()
+    lib = load_library()
+    Tq, Hq, D = q.shape
+    NB, B, Hkv, D2 = k_cache.shape
+    S = cu_seqlens_q.shape[0] - 1
+    if D2 != D or v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("paged_attention_mixed_fp8: shape mismatch")
+    if k_scale.shape != (Hkv,) or v_scale.shape != (Hkv,):
+        raise ValueError("paged_attention_mixed_fp8: scales must be [Hkv]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("paged_attention_mixed_fp8: block_tables [S, max_nb] / context_lens [S]")
+    need = mixed_workspace_size(S, int(num_decode), Tq, int(max_query_len), Hq, Hkv, D, B, "fp8",
+                                int(max_context_len))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.pkv_paged_attention_mixed_fp8(
+        _dev(out, "out"), dtype_code(out), _dev(q, "q"), dtype_code(q),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), Tq, int(num_decode), int(max_query_len),
+        _fp8_pool(k_cache, "k_cache"), _fp8_pool(v_cache, "v_cache"),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B,
+        float(scale), _dev(workspace, "workspace"), workspace.numel(), _stream(stream)),
+        "paged_attention_mixed_fp8")
     return out
 
 

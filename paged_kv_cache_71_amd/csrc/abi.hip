@@ -168,7 +168,6 @@ static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv
               PKV_ERR_UNSUPPORTED,
               "decode: one block of one pool must be smaller than 2 GiB");
   if (cascade) {
-    PKV_REQUIRE(!fp8, PKV_ERR_UNSUPPORTED, "decode_cascade: FP8 pools not supported");
     PKV_REQUIRE(cg.n_groups >= (S > 0 ? 1 : 0) && cg.n_groups <= S && cg.max_group_size >= 1 &&
                     cg.max_group_size <= S + (S == 0),
                 PKV_ERR_INVALID_ARG, "decode_cascade: n_groups=%d max_group_size=%d for S=%d",
@@ -217,7 +216,7 @@ static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv
   a.seq_start = nullptr;
   a.lse = nullptr;
   if (cascade)
-    return launch_decode_cascade(kv_dtype, a, cg.cu, cg.prefix_lens, cg.n_groups,
+    return launch_decode_cascade(kv_dtype, fp8, a, cg.cu, cg.prefix_lens, cg.n_groups,
                                  cg.max_group_size, cg.max_prefix_len, workspace, workspace_bytes,
                                  static_cast<hipStream_t>(stream));
   return launch_decode(kv_dtype, fp8, plan, a, static_cast<hipStream_t>(stream));
@@ -272,6 +271,25 @@ pkv_status pkv_paged_attention_decode_cascade(
   cg.max_group_size = max_group_size;
   cg.max_prefix_len = max_prefix_len;
   return decode_impl(out, out_dtype, q, kv_dtype, false, k_cache, v_cache, nullptr, nullptr,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, S, Hq, Hkv,
+                     D, B, scale, workspace, workspace_bytes, stream, cg);
+}
+
+pkv_status pkv_paged_attention_decode_cascade_fp8(
+    void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* k_cache,
+    const void* v_cache, const float* k_scale, const float* v_scale, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len, int32_t S,
+    int32_t Hq, int32_t Hkv, int32_t D, int32_t B, float scale, const int32_t* cu_group_seqs,
+    const int32_t* group_prefix_lens, int32_t n_groups, int32_t max_group_size,
+    int32_t max_prefix_len, void* workspace, size_t workspace_bytes, void* stream) {
+  CascadeGroups cg;
+  cg.on = true;
+  cg.cu = cu_group_seqs;
+  cg.prefix_lens = group_prefix_lens;
+  cg.n_groups = n_groups;
+  cg.max_group_size = max_group_size;
+  cg.max_prefix_len = max_prefix_len;
+  return decode_impl(out, out_dtype, q, q_dtype, true, k_cache, v_cache, k_scale, v_scale,
                      block_tables, max_blocks_per_seq, context_lens, max_context_len, S, Hq, Hkv,
                      D, B, scale, workspace, workspace_bytes, stream, cg);
 }
@@ -452,34 +470,36 @@ pkv_status pkv_mixed_workspace_size(int32_t S, int32_t num_decode, int32_t Tq,
   return PKV_OK;
 }
 
-pkv_status pkv_paged_attention_mixed(void* out, pkv_dtype out_dtype, const void* q,
-                                     const int32_t* cu_seqlens_q, int32_t Tq, int32_t num_decode,
-                                     int32_t max_query_len, const void* k_cache,
-                                     const void* v_cache, pkv_dtype kv_dtype,
-                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                     const int32_t* context_lens, int32_t max_context_len,
-                                     int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
-                                     float scale, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
+}  // extern "C"
+
+// Mixed batch; kv_dtype is q's dtype, fp8: E4M3 pools with per-head scales.
+static pkv_status mixed_impl(void* out, pkv_dtype out_dtype, const void* q,
+                             const int32_t* cu_seqlens_q, int32_t Tq, int32_t num_decode,
+                             int32_t max_query_len, const void* k_cache, const void* v_cache,
+                             pkv_dtype kv_dtype, bool fp8, const float* k_scale,
+                             const float* v_scale, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t max_context_len, int32_t S, int32_t Hq, int32_t Hkv,
+                             int32_t D, int32_t B, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
   PKV_REQUIRE(num_decode >= 0 && num_decode <= S && num_decode <= Tq, PKV_ERR_INVALID_ARG,
               "mixed: num_decode %d outside [0, min(S=%d, Tq=%d)]", num_decode, S, Tq);
   PrefillArgs pa;
   bool empty = true;
   pkv_status st = prefill_args(out, out_dtype, q, cu_seqlens_q, Tq, max_query_len, k_cache,
-                               v_cache, kv_dtype, false, nullptr, nullptr, block_tables,
+                               v_cache, kv_dtype, fp8, k_scale, v_scale, block_tables,
                                max_blocks_per_seq, context_lens, max_context_len, S, Hq, Hkv, D, B,
                                scale, &pa, &empty);
   if (st != PKV_OK || empty) return st;
-  PKV_REQUIRE((int64_t)B * Hkv * D * dt_bytes(kv_dtype) < ((int64_t)1 << 31), PKV_ERR_UNSUPPORTED,
-              "mixed: one block of one pool must be smaller than 2 GiB");
   DecodePlan plan{};
   if (num_decode > 0) {
     st = plan_decode(num_decode, Hq, Hkv, D, B, max_context_len, &plan);
     if (st != PKV_OK) return st;
   }
-  const PrefillPlan pplan = plan_prefill(kv_dtype, S - num_decode, Tq - num_decode, max_query_len,
-                                         Hq, Hkv, D, B, max_context_len);
+  const PrefillPlan pplan = plan_prefill(fp8 ? (int)DT_FP8 : (int)kv_dtype, S - num_decode,
+                                         Tq - num_decode, max_query_len, Hq, Hkv, D, B,
+                                         max_context_len);
   const size_t need = mixed_workspace_size(plan, pplan, S - num_decode);
   PKV_REQUIRE(workspace && workspace_bytes >= need, PKV_ERR_WORKSPACE,
               "mixed: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
@@ -504,9 +524,44 @@ pkv_status pkv_paged_attention_mixed(void* out, pkv_dtype out_dtype, const void*
   da.max_ctx = max_context_len;
   da.out_dt = out_dtype;
   da.scale_log2 = scale * 1.4426950408889634f;
+  da.k_scale = fp8 ? k_scale : nullptr;
+  da.v_scale = fp8 ? v_scale : nullptr;
   pa.S = S - num_decode;
-  return launch_mixed(kv_dtype, plan, pplan, da, pa, num_decode, workspace,
+  return launch_mixed(kv_dtype, fp8, plan, pplan, da, pa, num_decode, workspace,
                       static_cast<hipStream_t>(stream));
+}
+
+extern "C" {
+
+pkv_status pkv_paged_attention_mixed(void* out, pkv_dtype out_dtype, const void* q,
+                                     const int32_t* cu_seqlens_q, int32_t Tq, int32_t num_decode,
+                                     int32_t max_query_len, const void* k_cache,
+                                     const void* v_cache, pkv_dtype kv_dtype,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t max_context_len,
+                                     int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                     float scale, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  return mixed_impl(out, out_dtype, q, cu_seqlens_q, Tq, num_decode, max_query_len, k_cache,
+                    v_cache, kv_dtype, false, nullptr, nullptr, block_tables, max_blocks_per_seq,
+                    context_lens, max_context_len, S, Hq, Hkv, D, B, scale, workspace,
+                    workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_attention_mixed_fp8(void* out, pkv_dtype out_dtype, const void* q,
+                                         pkv_dtype q_dtype, const int32_t* cu_seqlens_q,
+                                         int32_t Tq, int32_t num_decode, int32_t max_query_len,
+                                         const void* k_cache, const void* v_cache,
+                                         const float* k_scale, const float* v_scale,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t max_context_len,
+                                         int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                         float scale, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  return mixed_impl(out, out_dtype, q, cu_seqlens_q, Tq, num_decode, max_query_len, k_cache,
+                    v_cache, q_dtype, true, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                    context_lens, max_context_len, S, Hq, Hkv, D, B, scale, workspace,
+                    workspace_bytes, stream);
 }
 
 

@@ -164,7 +164,7 @@ pkv_status cascade_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
   return PKV_OK;
 }
 
-pkv_status launch_decode_cascade(int kv_dt, const DecodeArgs& base, const int32_t* cu_group_seqs,
+pkv_status launch_decode_cascade(int kv_dt, bool fp8, const DecodeArgs& base, const int32_t* cu_group_seqs,
                                  const int32_t* group_prefix_lens, int32_t n_groups,
                                  int32_t max_group_size, int32_t max_prefix_len, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
@@ -212,7 +212,7 @@ pkv_status launch_decode_cascade(int kv_dt, const DecodeArgs& base, const int32_
   p.seq_start = nullptr;
   p.lse = lse_p;
   if (n_groups > 0) {
-    st = launch_decode(kv_dt, false, L.plan_p, p, stream);
+    st = launch_decode(kv_dt, fp8, L.plan_p, p, stream);
     if (st != PKV_OK) return st;
   }
 
@@ -225,7 +225,7 @@ pkv_status launch_decode_cascade(int kv_dt, const DecodeArgs& base, const int32_
   sf.ws_acc = reinterpret_cast<float*>(ws + L.ws_s + L.plan_s.ws_acc_off);
   sf.seq_start = seq_start;
   sf.lse = lse_s;
-  st = launch_decode(kv_dt, false, L.plan_s, sf, stream);
+  st = launch_decode(kv_dt, fp8, L.plan_s, sf, stream);
   if (st != PKV_OK) return st;
 
   const int64_t items = (int64_t)base.S * base.Hq * (base.D / 4);

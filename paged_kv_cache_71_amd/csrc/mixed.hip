@@ -42,14 +42,14 @@ size_t mixed_workspace_size(const DecodePlan& plan, const PrefillPlan& pplan, in
          pplan.workspace_bytes;
 }
 
-pkv_status launch_mixed(int kv_dt, const DecodePlan& plan, const PrefillPlan& pplan,
+pkv_status launch_mixed(int kv_dt, bool fp8, const DecodePlan& plan, const PrefillPlan& pplan,
                         const DecodeArgs& dec, const PrefillArgs& pre, int32_t num_decode,
                         void* workspace, hipStream_t stream) {
   const int32_t S_p = pre.S;
   char* ws = static_cast<char*>(workspace);
   int32_t* cu_p = reinterpret_cast<int32_t*>(ws + align_up(plan.workspace_bytes));
   char* ws_split = reinterpret_cast<char*>(cu_p) + align_up(((size_t)S_p + 1) * sizeof(int32_t));
-  if (S_p == 0) return dec.S ? launch_decode(kv_dt, false, plan, dec, stream) : PKV_OK;
+  if (S_p == 0) return dec.S ? launch_decode(kv_dt, fp8, plan, dec, stream) : PKV_OK;
 
   PrefillArgs p = pre;
   const int es = dt_bytes(kv_dt), oes = dt_bytes(pre.out_dt);
@@ -67,13 +67,13 @@ pkv_status launch_mixed(int kv_dt, const DecodePlan& plan, const PrefillPlan& pp
   }
 
   if (dec.S > 0) {
-    const pkv_status sd = launch_decode(kv_dt, false, plan, dec, stream);
+    const pkv_status sd = launch_decode(kv_dt, fp8, plan, dec, stream);
     if (sd != PKV_OK) return sd;
   }
   hipLaunchKernelGGL(rebase_cu_kernel, dim3(1), dim3(256), 0, stream, pre.cu_seqlens_q, num_decode,
                      S_p, cu_p);
   const pkv_status st = check_launch("mixed (rebase)");
-  return st != PKV_OK ? st : launch_prefill(kv_dt, p, stream);
+  return st != PKV_OK ? st : launch_prefill(fp8 ? (int)DT_FP8 : kv_dt, p, stream);
 }
 
 }  // namespace pkv

@@ -154,7 +154,7 @@ pkv_status launch_decode(int q_dt, bool fp8, const DecodePlan& plan, DecodeArgs 
 pkv_status cascade_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
                                   int32_t max_context_len, int32_t n_groups, int32_t max_group_size,
                                   int32_t max_prefix_len, int kv_dt, size_t* bytes);
-pkv_status launch_decode_cascade(int kv_dt, const DecodeArgs& base, const int32_t* cu_group_seqs,
+pkv_status launch_decode_cascade(int kv_dt, bool fp8, const DecodeArgs& base, const int32_t* cu_group_seqs,
                                  const int32_t* group_prefix_lens, int32_t n_groups,
                                  int32_t max_group_size, int32_t max_prefix_len, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
@@ -201,7 +201,7 @@ int device_cu_count();
 // plan for them) and the prefill part (pre: the whole batch's pointers, pre.S =
 // number of prefill sequences after the num_decode decodes).
 size_t mixed_workspace_size(const DecodePlan& plan, const PrefillPlan& pplan, int32_t S_prefill);
-pkv_status launch_mixed(int kv_dt, const DecodePlan& plan, const PrefillPlan& pplan,
+pkv_status launch_mixed(int kv_dt, bool fp8, const DecodePlan& plan, const PrefillPlan& pplan,
                         const DecodeArgs& dec, const PrefillArgs& pre, int32_t num_decode,
                         void* workspace, hipStream_t stream);
 

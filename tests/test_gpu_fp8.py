@@ -318,3 +318,72 @@ def test_prefill_fp8_context_of_131072_tokens(gpu_lib):
     """FP8 pools, a 256-token chunk at the end of a 131,072-token context."""
     b = W.varlen_prefill(9, [130816], [256], 32, 8, 128, 16, "bf16")
     check_prefill(gpu_lib, b, seed=3, rows=[0, 100, 255])
+
+
+# ---------------------------------------------------------------- cascade and mixed over FP8 pools
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D,B,Hq,Hkv", [(128, 16, 32, 8), (64, 32, 6, 2), (128, 8, 8, 8)])
+def test_cascade_fp8_matches_oracle(gpu_lib, dtype, D, B, Hq, Hkv):
+    """Shared-prefix groups over FP8 pools: prefixes read once per group and
+    merged with the suffixes; the FP8 decode oracle is the reference."""
+    rng = np.random.default_rng(D + B + Hq + 1)
+    sizes = [4, 1, 3, 2, 4]
+    pblocks = [int(x) for x in rng.integers(0, 600 // B + 1, len(sizes))]
+    pblocks[1] = 0
+    suffix = rng.integers(0, 300, sum(sizes))
+    suffix[0] = 0
+    b = W.grouped_batch(D * B + Hq + 1, sizes, pblocks, suffix, Hq, Hkv, D, B, dtype)
+    print(f"[fp8 cascade] S={b.S} Hq={Hq} Hkv={Hkv} D={D} B={B} q={dtype}", flush=True)
+    f = W.fp8_pools(b, 5)
+    d = Fp8Dev(b, f)
+    cu = np.asarray(b.meta["cu_group_seqs"], np.int32)
+    plens = np.asarray(b.meta["group_prefix_lens"], np.int32)
+    out = torch.full(tuple(d.q.shape), float("nan"), dtype=torch.float32, device="cuda")
+    gpu_lib.paged_attention_decode_cascade_fp8(out, d.q, d.k_cache, d.v_cache, d.k_scale, d.v_scale,
+                                               d.block_tables, d.context_lens, b.max_context_len,
+                                               b.scale, torch.from_numpy(cu).cuda(),
+                                               torch.from_numpy(plens).cuda(), int(np.diff(cu).max()),
+                                               int(plens.max()))
+    torch.cuda.synchronize()
+    err = max_abs(out, oracle_decode(b, f))
+    assert err <= TOL[dtype], f"max abs err {err}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("chunks", [[70, 33, 128], [512]])
+def test_mixed_fp8_matches_separate_calls_and_oracle(gpu_lib, dtype, chunks):
+    """Decodes and chunks over FP8 pools in one call: every row equals the
+    separate FP8 decode / FP8 prefill result bit for bit, and the oracle
+    within tolerance (a decode row is a chunk of one token)."""
+    rng = np.random.default_rng(len(chunks) + 2)
+    dl = rng.integers(1, 700, 9)
+    prior = [300, 0, 1000][:len(chunks)] if len(chunks) > 1 else [4000]
+    b = W.mixed_batch(40 + len(chunks), dl, prior, chunks, 32, 8, 128, 16, dtype)
+    nd = b.meta["num_decode"]
+    print(f"[fp8 mixed] decodes={nd} chunks={chunks} q={dtype}", flush=True)
+    f = W.fp8_pools(b, 6)
+    d = Fp8Dev(b, f)
+    cu = torch.from_numpy(b.cu_seqlens_q).cuda()
+    maxq = int(np.max(np.diff(b.cu_seqlens_q)))
+    mixed = torch.full(tuple(d.q.shape), float("nan"), dtype=torch.float32, device="cuda")
+    gpu_lib.paged_attention_mixed_fp8(mixed, d.q, cu, nd, maxq, d.k_cache, d.v_cache, d.k_scale,
+                                      d.v_scale, d.block_tables, d.context_lens, b.max_context_len,
+                                      b.scale)
+    sep = torch.full_like(mixed, float("nan"))
+    gpu_lib.paged_attention_decode_fp8(sep[:nd], d.q[:nd], d.k_cache, d.v_cache, d.k_scale,
+                                       d.v_scale, d.block_tables[:nd].contiguous(),
+                                       d.context_lens[:nd].contiguous(), b.max_context_len, b.scale)
+    cup = (cu[nd:] - nd).contiguous()
+    gpu_lib.paged_attention_prefill_fp8(sep[nd:], d.q[nd:].contiguous(), cup,
+                                        int(np.max(np.diff(b.cu_seqlens_q[nd:]))), d.k_cache,
+                                        d.v_cache, d.k_scale, d.v_scale,
+                                        d.block_tables[nd:].contiguous(),
+                                        d.context_lens[nd:].contiguous(), b.max_context_len, b.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(mixed, sep)
+    _, _, tables = b.compact_pool(extra_poison_blocks=0)
+    rows = sorted(set([0, nd - 1, nd, b.q.shape[0] - 1] + rng.choice(b.q.shape[0], 12, replace=False).tolist()))
+    ref = oracle.prefill_fp8(b.q, dtype, b.cu_seqlens_q, f.k_blocks, f.v_blocks, f.k_scale,
+                             f.v_scale, tables, b.context_lens, b.scale, rows=rows)
+    err = max_abs(mixed[torch.as_tensor(rows).cuda()], ref[rows])
+    assert err <= TOL[dtype], f"max abs err {err}"
