@@ -1,4 +1,4 @@
-// cache_ops.hip -- the two pure data-movement kernels of the paged KV cache.
+// cache_ops.hip -- the data-movement kernels of the paged KV cache.
 //
 //  * reshape_and_cache: every new token's K row and V row (Hkv*D contiguous
 //    elements each) is written to its absolute slot of the pool.  With the
@@ -19,8 +19,9 @@
 //    scaled by its KV head's scale and rounded into an OCP E4M3 code
 //    ("LLM inference, part 3", ch. 10: scale and clip into 8 bits on write).
 //
-// Both are HBM copies: 16-byte lanes, fully coalesced, one workgroup per row
-// (or per block and layer), no LDS.
+// All are copies (through HBM, or over the host link for swaps): 16-byte
+// lanes, fully coalesced, one workgroup per row (or per block and layer), no
+// LDS.
 #include "pkv_internal.h"
 
 namespace pkv {

@@ -34,20 +34,27 @@
 //    and masked by selection afterwards, so the compiler can wait for exactly
 //    one tile (vmcnt) instead of draining the queue.
 //  * Each K/V load serves all GC query heads of the group (GQA reuse in
-//    registers).  q . k uses the packed dot2 instructions for 16-bit KV
-//    (exact products, fp32 accumulation), then a DPP butterfly over the LPR
-//    lanes of the row.  Scores are kept in log2 units (scale * log2 e), and
-//    the accumulator is rescaled only when some lane's running max grows (a
-//    wave vote), which is bit-identical to rescaling by exp2(0) = 1 every tile.
+//    registers).  Matrix-core path (16-bit q, D = 128, groups of 4, 8 or 16
+//    query heads, B >= 16; the Llama-3-8B batch): q . k on
+//    v_mfma_f32_16x16x32 with the row's query heads as the 16 columns, P . V
+//    on v_mfma_f32_16x16x16 over V staged per wave in LDS and read transposed
+//    (ds_read_b64_tr_b16), three tiles in flight per wave.  Vector path (the
+//    rest): the packed dot2 instructions for 16-bit KV (exact products, fp32
+//    accumulation), then a DPP butterfly over the LPR lanes of the row.
+//    Scores are kept in log2 units (scale * log2 e), and the accumulator is
+//    rescaled only when some lane's running max grows (a wave vote), which is
+//    bit-identical to rescaling by exp2(0) = 1 every tile.
 //  * Rows past context_lens[s] and table entries past the last block are never
 //    used (clamped loads read valid rows only), so stale or poisoned memory
 //    there cannot reach the output.
 //  * FP8 pools ("LLM inference, part 3", ch. 10): the F8 instantiations keep
-//    every lane's element assignment of the 16-bit path but load 8 code bytes
-//    where that path loads 16 data bytes, so a tile costs half the HBM bytes;
-//    the codes are widened exactly in registers (gfx950 conversions) right
-//    before use, the K scale of the row's KV head is folded into the score
-//    scale and the V scale into the finished accumulator.
+//    every lane's element assignment of the 16-bit path with one code byte
+//    per element, so a tile costs half the HBM bytes (on the matrix-core path
+//    K codes come in 16-byte loads in a head-dimension order that q shares,
+//    V codes in 16-byte loads restaged through LDS); the codes are widened
+//    exactly in registers (gfx950 conversions) right before use, the K scale
+//    of the row's KV head is folded into the score scale and the V scale
+//    into the finished accumulator.
 #include <type_traits>
 
 #include "pkv_internal.h"

@@ -6,34 +6,18 @@
 // the sequence's tokens 0 .. that position (earlier prompt chunks plus the
 // chunk itself, already written by reshape_and_cache).
 //
-// 16-bit KV (bf16/f16): the only dense contraction of the path, so it runs on
-// the gfx950 matrix cores (v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation).
-//  * Workgroup = 4 waves = 128 query rows of one (sequence, KV head): the rows
-//    are (token, query head of the group) pairs, so the G heads that share a KV
-//    head share every K/V tile (GQA reuse).  Each wave owns 32 rows.
-//  * S^T = K Q^T per 32-token KV tile: K rows are the MFMA A operand and are
-//    loaded straight from the paged pool into registers (each lane reads one
-//    token row's contiguous half, 16 bytes at a time, its block found through
-//    the table); Q^T is the B operand, loaded once.  In the 32x32 result each
-//    lane holds 16 scores of ONE query row, so the softmax row max needs only
-//    one cross-lane exchange (lane ^ 32).
-//  * Online softmax in log2 units with a lazy rescale: the accumulator is only
-//    rescaled when the running max grows by more than 2^8, so weights stay
-//    <= 256 and most tiles skip the rescale.
-//  * O^T = V^T P^T: the contraction runs over KV tokens, so V is staged in LDS
-//    transposed ([d][token], double buffered, one barrier per tile) and read
-//    as the A operand; the weights P^T come straight out of the score
-//    registers as the B operand.  For bf16 the weights are split into
-//    hi + lo bf16 parts (two MFMAs), keeping ~16 significant bits so the
-//    result stays within fp32-accumulation accuracy even for peaked attention;
-//    for f16 one f16 operand (11 bits) suffices.
-//  * Workgroups of one (sequence, KV head) are mapped to the same XCD
-//    (blockIdx % 8), so their shared K/V tiles are served from that XCD's L2.
-//  * Positions past the row's causal limit, rows past the chunk and tokens
-//    past the context are masked by selection (never multiplied), and memory
-//    past the context is never dereferenced.
-//
-// fp32 KV: a plain vector-ALU kernel (one wave per query token and KV head).
+// Kernels:
+//  * prefill_tile_kernel -- 16-bit or FP8 pools with blocks of >= 16 tokens:
+//    the software-pipelined matrix-core kernel (both products on
+//    v_mfma_f32_16x16x32, K/V staged through LDS); described above it.
+//  * prefill_merge_kernel -- combines the partial results of launches whose
+//    KV ranges were split (plan_prefill: few sequences, long contexts).
+//  * prefill_mfma_kernel -- 16-bit pools with blocks of fewer than 16 tokens
+//    (32x32x16 matrix-core kernel, K read straight from the pool).
+//  * prefill_f32_kernel -- fp32 pools, a plain vector-ALU kernel.
+// Positions past a row's causal limit, rows past the chunk and tokens past
+// the context are masked by selection (never multiplied), and memory past the
+// context is never dereferenced.
 #include <algorithm>
 #include <type_traits>
 
@@ -100,6 +84,27 @@ struct BoolTag {
 
 __device__ __forceinline__ u32x4_t as_v(uint4 x) { return u32x4_t{x.x, x.y, x.z, x.w}; }
 
+// Blocks of fewer than 16 tokens (16-bit KV): v_mfma_f32_32x32x16_{bf16,f16},
+// fp32 accumulation.
+//  * Workgroup = 4 waves = 128 query rows of one (sequence, KV head): the rows
+//    are (token, query head of the group) pairs, so the G heads that share a KV
+//    head share every K/V tile (GQA reuse).  Each wave owns 32 rows.
+//  * S^T = K Q^T per 32-token KV tile: K rows are the MFMA A operand and are
+//    loaded straight from the paged pool into registers (each lane reads one
+//    token row's contiguous half, 16 bytes at a time, its block found through
+//    the table); Q^T is the B operand, loaded once.  In the 32x32 result each
+//    lane holds 16 scores of ONE query row, so the softmax row max needs only
+//    one cross-lane exchange (lane ^ 32).
+//  * Online softmax in log2 units with a lazy rescale: the accumulator is only
+//    rescaled when the running max grows by more than 2^8, so weights stay
+//    <= 256 and most tiles skip the rescale.
+//  * O^T = V^T P^T: V is staged in LDS transposed ([d][token], double
+//    buffered, one barrier per tile) and read as the A operand; the weights
+//    P^T come straight out of the score registers as the B operand.  For bf16
+//    the weights are split into hi + lo bf16 parts (two MFMAs), keeping ~16
+//    significant bits; for f16 one f16 operand (11 bits) suffices.
+//  * Workgroups of one (sequence, KV head) are mapped to the same XCD
+//    (blockIdx % 8), so their shared K/V tiles are served from that XCD's L2.
 template <int DT, int D, bool PSPLIT>
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArgs a) {
   constexpr int ES = 2;
