@@ -1026,10 +1026,12 @@ pkv_status launch_f32(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 // Split plan.  A launch whose workgroups ((sequence, KV head) pairs x query
-// tiles) would not fill the GPU twice over with two per CU -- few sequences,
-// e.g. one long prompt's chunk -- cuts every workgroup's KV range into splits
-// of tiles_per_split tiles (at least kMinSplitTiles), up to four workgroups
-// per CU in total.  Workgroups whose range fits one split write their rows
+// tiles) would not fill the GPU with two per CU -- few sequences, e.g. one
+// long prompt's chunk -- cuts every workgroup's KV range into splits of
+// tiles_per_split tiles (at least kMinSplitTiles), up to two workgroups per
+// CU in total: one round of resident workgroups.  (Four per CU, two rounds,
+// measured 7-9% slower on single 256- to 1024-token chunks: twice the partial
+// results to merge.)  Workgroups whose range fits one split write their rows
 // directly; the others leave partial results for the merge kernel.
 PrefillPlan plan_prefill(int kv_dt, int32_t S, int32_t Tq, int32_t max_query_len, int32_t Hq,
                          int32_t Hkv, int32_t D, int32_t B, int32_t max_ctx) {
@@ -1041,7 +1043,7 @@ PrefillPlan plan_prefill(int kv_dt, int32_t S, int32_t Tq, int32_t max_query_len
   const int TQ = kWaves * 16 * kTileQB / G;
   const int64_t grid0 = (int64_t)((max_query_len + TQ - 1) / TQ) * S * Hkv;
   const int max_tiles = (max_ctx + kTileKV - 1) / kTileKV;
-  const int64_t target = 4 * (int64_t)std::max(device_cu_count(), 1);
+  const int64_t target = 2 * (int64_t)std::max(device_cu_count(), 1);
   if (grid0 >= target) return p;
   int ns = (int)std::min<int64_t>((target + grid0 - 1) / grid0, std::max(1, max_tiles / kMinSplitTiles));
   if (ns <= 1) return p;
