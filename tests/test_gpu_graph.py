@@ -1,0 +1,114 @@
+"""The library's calls inside a captured HIP graph.  No call allocates,
+synchronises or records memset nodes, so a captured step replays the same
+kernels: every replay (with the program's own eager work and synchronisations
+between replays) must equal the eager result bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DevBatch
+from paged_kv_cache_71_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def replay_matches_eager(fn, out, replays=4):
+    """Run fn eagerly, capture it, then replay it several times with eager
+    work in between; each replay's output must equal the eager one."""
+    fn()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    out.fill_(float("nan"))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    for r in range(replays):
+        out.fill_(float("nan"))        # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r} differs from the eager result"
+        fn()                            # and the eager call still agrees afterwards
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+
+
+def test_decode_step_in_a_graph(gpu_lib):
+    """reshape_and_cache of the new tokens + decode, workspace given."""
+    b = W.llama3_8b_bf16(0, S=64, NB=20000)
+    print(f"[graph] decode step S={b.S}", flush=True)
+    db = DevBatch(b)
+    out = db.out()
+    ws = torch.empty(max(gpu_lib.decode_workspace_size(b.S, b.Hq, b.Hkv, b.D, b.B, b.max_context_len), 1),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        gpu_lib.reshape_and_cache(db.new_k, db.new_v, db.k_cache, db.v_cache, db.new_slots)
+        gpu_lib.paged_attention_decode(out, db.q, db.k_cache, db.v_cache, db.block_tables,
+                                       db.context_lens, b.max_context_len, b.scale, workspace=ws)
+
+    replay_matches_eager(step, out)
+
+
+def test_split_prefill_in_a_graph(gpu_lib):
+    """A prefill whose KV ranges are split (partials + merge kernel)."""
+    b = W.varlen_prefill(3, [3000, 500], [100, 40], 32, 8, 128, 16, "bf16")
+    print("[graph] split prefill", flush=True)
+    db = DevBatch(b)
+    out = db.out()
+    maxq = int(np.max(np.diff(b.cu_seqlens_q)))
+    need = gpu_lib.prefill_workspace_size(b.S, b.q.shape[0], maxq, b.Hq, b.Hkv, b.D, b.B, "bf16",
+                                          b.max_context_len)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def run():
+        gpu_lib.paged_attention_prefill(out, db.q, db.cu_seqlens_q, maxq, db.k_cache, db.v_cache,
+                                        db.block_tables, db.context_lens, b.max_context_len,
+                                        b.scale, workspace=ws)
+
+    replay_matches_eager(run, out)
+
+
+def test_mixed_batch_in_a_graph(gpu_lib):
+    b = W.mixed_batch(4, [100, 900, 33], [2000], [128], 32, 8, 128, 16, "bf16")
+    print("[graph] mixed", flush=True)
+    db = DevBatch(b)
+    out = db.out()
+    nd = b.meta["num_decode"]
+    maxq = int(np.max(np.diff(b.cu_seqlens_q)))
+    ws = torch.empty(max(gpu_lib.mixed_workspace_size(b.S, nd, b.q.shape[0], maxq, b.Hq, b.Hkv, b.D,
+                                                      b.B, "bf16", b.max_context_len), 1),
+                     dtype=torch.uint8, device="cuda")
+
+    def run():
+        gpu_lib.paged_attention_mixed(out, db.q, db.cu_seqlens_q, nd, maxq, db.k_cache, db.v_cache,
+                                      db.block_tables, db.context_lens, b.max_context_len, b.scale,
+                                      workspace=ws)
+
+    replay_matches_eager(run, out)
+
+
+def test_cascade_in_a_graph(gpu_lib):
+    b = W.grouped_batch(5, [4, 2, 3], [20, 7, 0], [10, 0, 50, 3, 200, 1, 1, 77, 9], 32, 8, 128, 16,
+                        "bf16")
+    print("[graph] cascade", flush=True)
+    db = DevBatch(b)
+    out = db.out()
+    cu = np.asarray(b.meta["cu_group_seqs"], np.int32)
+    plens = np.asarray(b.meta["group_prefix_lens"], np.int32)
+    mgs, mpl = int(np.diff(cu).max()), int(plens.max())
+    ws = torch.empty(max(gpu_lib.decode_cascade_workspace_size(b.S, b.Hq, b.Hkv, b.D, b.B,
+                                                               b.max_context_len, len(plens), mgs,
+                                                               mpl, "bf16"), 1),
+                     dtype=torch.uint8, device="cuda")
+    cu_d, pl_d = torch.from_numpy(cu).cuda(), torch.from_numpy(plens).cuda()
+
+    def run():
+        gpu_lib.paged_attention_decode_cascade(out, db.q, db.k_cache, db.v_cache, db.block_tables,
+                                               db.context_lens, b.max_context_len, b.scale, cu_d,
+                                               pl_d, mgs, mpl, workspace=ws)
+
+    replay_matches_eager(run, out)
