@@ -569,7 +569,8 @@ def cpu_baseline(b, sample_tokens):
         n = min(b.S, int(np.searchsorted(np.cumsum(b.context_lens), sample_tokens) + 1))
     sel = np.arange(n)
     runs, t0 = 0, time.perf_counter()
-    while runs < 3 and (runs == 0 or time.perf_counter() - t0 < 10.0):
+    # about 10-20 s of CPU work: whole passes until 10 s have gone by (at most 10)
+    while runs < 10 and (runs == 0 or time.perf_counter() - t0 < 10.0):
         oracle.decode(b.q[sel], k, v, b.dtype, tables[sel], b.context_lens[sel], b.scale)
         runs += 1
     dt = (time.perf_counter() - t0) / runs
