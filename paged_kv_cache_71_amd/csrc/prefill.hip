@@ -576,7 +576,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     return tbv[kv >> log2B];
   };
   // global -> registers: the chunks of tile t (entries e0, e1 of its halves).
-  // Rows past the visible range (last tile only) repeat its last row.
+  // Rows past the visible range (last tile only) repeat its last row.  The
+  // block base is an unsigned 32 x 32 -> 64-bit product: entries reached here
+  // are physical block ids (>= 0) and a block is under 2 GiB (checked on the
+  // host), which spares the signed 64-bit multiply's scalar instructions.
   auto ldc = [](const char* p) __attribute__((always_inline)) -> Chunk {
     return *reinterpret_cast<const Chunk*>(p);
   };
@@ -587,8 +590,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
         const int h = chalf[i];
-        const char* base = pool + (int64_t)(h ? e1 : e0) * blk_stride +
-                           (int64_t)(((kv0 + 16 * h) & bmask) * rs32);
+        const char* base = pool + (uint64_t)(uint32_t)(h ? e1 : e0) * (uint32_t)blk_stride +
+                           (uint32_t)(((kv0 + 16 * h) & bmask) * rs32);
         dst[i] = ldc(base + loff[i]);
       }
     } else {
@@ -596,7 +599,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int i = 0; i < NCH; ++i) {
         const int h = chalf[i];
         const int kvc = min(kv0 + crow[i], kv_end - 1);
-        const char* base = pool + (int64_t)(h ? e1 : e0) * blk_stride;
+        const char* base = pool + (uint64_t)(uint32_t)(h ? e1 : e0) * (uint32_t)blk_stride;
         dst[i] = ldc(base + (uint32_t)((kvc & bmask) * rs32 + ccol[i] * CBP));
       }
     }
