@@ -498,7 +498,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       // holds token l % 16, elements 32 kk + 8 (l / 16) .. + 7.  V rows as in
       // the vector path but with token 4 * row + i in load i, which is where
       // the MFMA result leaves that token's scores.
-      const int64_t base = (int64_t)en.e[0] * blk_stride;  // wave-uniform
+      // wave-uniform; unsigned 32 x 32 -> 64 bits: block ids are >= 0 and a
+      // block is under 2 GiB (checked on the host)
+      const uint64_t base = (uint64_t)(uint32_t)en.e[0] * (uint32_t)blk_stride;
       const int kvoff = c.kvh * D * KS;
       const int tk = min(ts + col, c.L - 1);
       if constexpr (F8) {
@@ -543,7 +545,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const int tok = min(ts + i * RPW + row, c.L - 1);
-        const int64_t base = (int64_t)en.e[i] * blk_stride;  // wave-uniform
+        const uint64_t base = (uint64_t)(uint32_t)en.e[i] * (uint32_t)blk_stride;  // as above
         const unsigned off = (unsigned)((tok & bmask) * row_stride32 + head_off);
         kb[i] = ldkv(kpool + base + off);
         vb[i] = ldkv(vpool + base + off);
