@@ -105,7 +105,8 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
  *   workspace      : device scratch of at least pkv_decode_workspace_size()
  *                    bytes (a size that depends on the arguments only, not on
  *                    the device); contents on entry are ignored.  It holds the
- *                    partial softmax states of rows split between waves.
+ *                    partial softmax states of rows split between waves and
+ *                    the list of those rows.
  * out[s, h, :] = sum_t softmax_t(scale * q[s,h,:] . K[s,t,:]) V[s,t,:],
  * computed in fp32.  The summation order depends only on logical positions,
  * so the result is bit-identical under any permutation of physical blocks and

@@ -195,10 +195,7 @@ static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  char* ws = static_cast<char*>(workspace);
-  a.ws_ps = reinterpret_cast<int32_t*>(ws + plan.ws_ps_off);
-  a.ws_ml = reinterpret_cast<float*>(ws + plan.ws_ml_off);
-  a.ws_acc = reinterpret_cast<float*>(ws + plan.ws_acc_off);
+  attach_decode_workspace(&a, plan, workspace);
   a.max_nb = max_blocks_per_seq;
   a.S = S;
   a.Hq = Hq;
@@ -510,10 +507,7 @@ static pkv_status mixed_impl(void* out, pkv_dtype out_dtype, const void* q,
   da.v_cache = v_cache;
   da.block_tables = block_tables;
   da.context_lens = context_lens;
-  char* ws = static_cast<char*>(workspace);
-  da.ws_ps = reinterpret_cast<int32_t*>(ws + plan.ws_ps_off);
-  da.ws_ml = reinterpret_cast<float*>(ws + plan.ws_ml_off);
-  da.ws_acc = reinterpret_cast<float*>(ws + plan.ws_acc_off);
+  attach_decode_workspace(&da, plan, workspace);
   da.max_nb = max_blocks_per_seq;
   da.S = num_decode;
   da.Hq = Hq;

@@ -206,9 +206,7 @@ pkv_status launch_decode_cascade(int kv_dt, bool fp8, const DecodeArgs& base, co
   p.S = n_groups;
   p.Hq = NM * base.Hq;
   p.max_ctx = L.max_prefix_len;
-  p.ws_ps = reinterpret_cast<int32_t*>(ws + L.ws_p + L.plan_p.ws_ps_off);
-  p.ws_ml = reinterpret_cast<float*>(ws + L.ws_p + L.plan_p.ws_ml_off);
-  p.ws_acc = reinterpret_cast<float*>(ws + L.ws_p + L.plan_p.ws_acc_off);
+  attach_decode_workspace(&p, L.plan_p, ws + L.ws_p);
   p.seq_start = nullptr;
   p.lse = lse_p;
   if (n_groups > 0) {
@@ -220,9 +218,7 @@ pkv_status launch_decode_cascade(int kv_dt, bool fp8, const DecodeArgs& base, co
   DecodeArgs sf = base;
   sf.out = o_s;
   sf.out_dt = DT_F32;
-  sf.ws_ps = reinterpret_cast<int32_t*>(ws + L.ws_s + L.plan_s.ws_ps_off);
-  sf.ws_ml = reinterpret_cast<float*>(ws + L.ws_s + L.plan_s.ws_ml_off);
-  sf.ws_acc = reinterpret_cast<float*>(ws + L.ws_s + L.plan_s.ws_acc_off);
+  attach_decode_workspace(&sf, L.plan_s, ws + L.ws_s);
   sf.seq_start = seq_start;
   sf.lse = lse_s;
   st = launch_decode(kv_dt, fp8, L.plan_s, sf, stream);

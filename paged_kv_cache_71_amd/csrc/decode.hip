@@ -19,11 +19,14 @@
 //  * Each workgroup first turns context_lens into a prefix sum of tile counts
 //    in LDS; a wave finds its first tile by binary search, then walks rows.
 //  * A row that lies entirely inside one wave's range is finished by that wave
-//    (output written directly).  A row cut by range boundaries leaves partial
-//    (max, sum, acc) states -- at most two per wave, in fixed slots -- merged by
-//    a second small kernel in a fixed order.  The cut points depend only on the
-//    context lengths, so results are bit-identical under any physical placement
-//    or aliasing of blocks.
+//    (output written directly, in any output dtype).  A row cut by range
+//    boundaries leaves partial (max, sum, acc) states -- at most two per wave,
+//    in fixed slots -- merged by a second small kernel in a fixed order.  Each
+//    wave also records the row that its start cuts first, so the merge kernel
+//    runs one wave per range boundary and finds its row with one load; rows
+//    with nothing to attend get their zero output from the split kernel.  The
+//    cut points depend only on the context lengths, so results are
+//    bit-identical under any physical placement or aliasing of blocks.
 //  * A token row of one KV head is D * elem bytes contiguous (256 B for bf16
 //    D = 128); LPR lanes cover it with 16-byte loads, so one wave-load reads RPW
 //    complete rows.  A tile is 4 such loads of K and 4 of V (8 KiB for bf16).
@@ -390,6 +393,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int i = tid; i <= S; i += kThreads) a.ws_ps[i] = sm_ps[i];
   }
 
+  // sequences with nothing to attend: all-zero output, -inf log-sum-exp
+  for (int i = blockIdx.x; i < S; i += gridDim.x) {
+    if (rfl(sm_len[i]) != 0) continue;
+    const int64_t ob = (int64_t)i * a.Hq * D;
+    for (int j = tid; j < a.Hq * D; j += kThreads) store_out(a.out, a.out_dt, ob + j, 0.f);
+    if (a.lse)
+      for (int h = tid; h < a.Hq; h += kThreads) a.lse[(int64_t)i * a.Hq + h] = -__builtin_inff();
+  }
+
   const int N = rfl(sm_ps[S]);
   const int NW = gridDim.x * kWaves;
   const int C = (N + NW - 1) / NW;
@@ -403,7 +415,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int w = wg_rank * kWaves + wave;
   const int x0 = w * C;
   const int x1 = min(x0 + C, N);
-  if (x0 >= x1) return;
+  if (x0 >= x1) {
+    if (lane == 0) a.ws_rec[w] = make_int4(-1, 0, 0, 0);  // nothing cut here
+    return;
+  }
 
   const int G = a.Hq / a.Hkv;
   const int nhc = a.n_hchunks;
@@ -461,6 +476,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     c0.j = u - c0.rho * c0.nt;
     set_row(c0);
   }
+  // the merge kernel's work list: x0 cuts the row holding it when the row
+  // starts earlier (j > 0); the row is listed at its first cut only, the one
+  // whose previous boundary x0 - C lies at or before the row's start
+  if (lane == 0)
+    a.ws_rec[w] = c0.j > 0 && c0.j <= C ? make_int4(c0.s * R + c0.rho, x0 - c0.j, c0.nt, C)
+                                        : make_int4(-1, 0, 0, 0);
 
   // table entries of a tile: one per wave-load (UNI) -- scalar loads
   struct Ent {
@@ -784,16 +805,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int db = 0; db < D / 16; ++db) oacc[db] *= c.vs;
       }
       if (col < GC) {  // one of the identical copies of each query column
-        if (complete && a.out_dt == DT_F32) {
+        if (complete) {
           const int64_t o = ((int64_t)c.s * a.Hq + c.h0 + col) * D + 4 * row;
           if (a.lse && row == 0) a.lse[(int64_t)c.s * a.Hq + c.h0 + col] = m[0] + __log2f(l[0]);
 #pragma unroll
-          for (int db = 0; db < D / 16; ++db)
-            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o + 16 * db) =
-                make_float4(oacc[db][0] / l[0], oacc[db][1] / l[0], oacc[db][2] / l[0],
-                            oacc[db][3] / l[0]);
+          for (int db = 0; db < D / 16; ++db) {
+            const float r4[4] = {oacc[db][0] / l[0], oacc[db][1] / l[0], oacc[db][2] / l[0],
+                                 oacc[db][3] / l[0]};
+            store_out_vec<4>(a.out, a.out_dt, o + 16 * db, r4);
+          }
         } else {
-          const int slot = complete ? 2 * NW + c.s * R + c.rho : (row_xb <= x0 ? 2 * w : 2 * w + 1);
+          const int slot = row_xb <= x0 ? 2 * w : 2 * w + 1;
           const int64_t o = ((int64_t)slot * GC + col) * D + 4 * row;
 #pragma unroll
           for (int db = 0; db < D / 16; ++db)
@@ -838,10 +860,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         merge_pair(c0v, l0, a0, c1v, l1, a1, m[g], l[g], acc[g]);
       }
     }
-    // A row lying inside this wave's range is final here: with fp32 output it
-    // is written directly, otherwise its state goes to the row's own slot.  A
-    // row cut by the range leaves its state in slot 2w (the row holding x0) or
-    // 2w + 1 (the row holding x1 - 1) for the merge kernel.
+    // A row lying inside this wave's range is final here and written
+    // directly.  A row cut by the range leaves its state in slot 2w (the row
+    // holding x0) or 2w + 1 (the row holding x1 - 1) for the merge kernel.
     if constexpr (F8) {  // V scale of the row's KV head (common to all its partial states)
 #pragma unroll
       for (int g = 0; g < GC; ++g)
@@ -849,7 +870,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int e = 0; e < EPL; ++e) acc[g][e] *= c.vs;
     }
     const bool complete = row_xb >= x0 && row_xb + c.nt <= x1;
-    if (complete && a.out_dt == DT_F32) {
+    if (complete) {
       if (a.lse && row == 0 && col == 0) {  // log2-sum-exp of the scaled scores, per head
 #pragma unroll
         for (int g = 0; g < GC; ++g) a.lse[(int64_t)c.s * a.Hq + c.h0 + g] = m[g] + __log2f(l[g]);
@@ -858,16 +879,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int g = 0; g < GC; ++g) {
           const float lg = l[g];
-          float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.out) +
-                                                  ((int64_t)c.s * a.Hq + c.h0 + g) * D + col * EPL);
+          const int64_t o = ((int64_t)c.s * a.Hq + c.h0 + g) * D + col * EPL;
 #pragma unroll
-          for (int e = 0; e < EPL / 4; ++e)
-            dst[e] = make_float4(acc[g][4 * e] / lg, acc[g][4 * e + 1] / lg, acc[g][4 * e + 2] / lg,
-                                 acc[g][4 * e + 3] / lg);
+          for (int e = 0; e < EPL / 4; ++e) {
+            const float r4[4] = {acc[g][4 * e] / lg, acc[g][4 * e + 1] / lg, acc[g][4 * e + 2] / lg,
+                                 acc[g][4 * e + 3] / lg};
+            store_out_vec<4>(a.out, a.out_dt, o + 4 * e, r4);
+          }
         }
       }
     } else {
-      const int slot = complete ? 2 * NW + c.s * R + c.rho : (row_xb <= x0 ? 2 * w : 2 * w + 1);
+      const int slot = row_xb <= x0 ? 2 * w : 2 * w + 1;
       if (row == 0) {
 #pragma unroll
         for (int g = 0; g < GC; ++g) {
@@ -956,96 +978,99 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   });
 }
 
-// Second pass: one workgroup per row (sequence, KV head, head chunk) turns the
-// fp32 softmax states of the split kernel into the output.  A row finished
-// inside one wave has one state (its own slot; with fp32 output the split
-// kernel has already written it and the row is skipped); a row cut by
-// wave-range boundaries has one state per wave it spans, merged in wave order:
-//   out = sum_w e^(m_w - M) acc_w / sum_w e^(m_w - M) l_w   (log2 units)
-// Every thread handles its outputs alone (no barriers): the states' (m, l) and
-// accumulator loads of up to 8 waves are issued together, so a row costs about
-// three dependent memory round trips.  Empty contexts give a zero output row.
+// Merge: one wave per range boundary b = 1 .. n_waves - 1.  The split kernel's
+// wave b recorded the row that its start cuts first (or nothing); that row's
+// states lie in slot 2(b-1)+1 (or 2(b-1) when the row starts exactly at wave
+// b-1's start) and then in slot 2w of each following wave w up to the one
+// holding the row's last tile.  They are combined in wave order,
+//   out = sum_w e^(m_w - M) acc_w / sum_w e^(m_w - M) l_w   (log2 units),
+// in batches of CH states whose loads are issued together: one running max
+// per batch, then each state's weight.  Lane l owns the NPL consecutive
+// outputs from l * NPL on (all of one query head of the row).
 template <int D, int GC>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const DecodeArgs a) {
-  constexpr int NPT = (GC * D + kMergeThreads - 1) / kMergeThreads;  // outputs per thread
-  constexpr int CH = 8;                                               // states per batch
+  constexpr int NPL = GC * D / 64;      // outputs per lane
+  constexpr int CH = NPL <= 8 ? 8 : 2;  // states per batch (register budget)
+  static_assert(NPL >= 1 && D % NPL == 0, "a lane's outputs belong to one head");
+  const int b = blockIdx.x * (kMergeThreads / 64) + rfl(threadIdx.x >> 6) + 1;
+  if (b >= a.n_waves) return;
+  const int4 r = a.ws_rec[b];
+  if (r.x < 0) return;
+  const int lane = threadIdx.x & 63;
   const int R = a.rows_per_seq;
-  const int s = blockIdx.x / R;
-  const int rho = blockIdx.x % R;
+  const int s = r.x / R;
+  const int rho = r.x - s * R;
   const int kvh = rho / a.n_hchunks;
   const int h0 = kvh * (a.Hq / a.Hkv) + (rho - kvh * a.n_hchunks) * GC;
-  const int N = a.ws_ps[a.S];
-  const int p0 = a.ws_ps[s];
-  const int nt = (a.ws_ps[s + 1] - p0) / R;
-  const int64_t obase = ((int64_t)s * a.Hq + h0) * D;
-  if (nt == 0) {  // empty context: defined as an all-zero output row
-    for (int j = threadIdx.x; j < GC * D; j += kMergeThreads) store_out(a.out, a.out_dt, obase + j, 0.f);
-    if (a.lse)
-      for (int g = threadIdx.x; g < GC; g += kMergeThreads)
-        a.lse[(int64_t)s * a.Hq + h0 + g] = -__builtin_inff();
-    return;
-  }
-  const int NW = a.n_waves;
-  const int C = (N + NW - 1) / NW;
-  const int xb = p0 + rho * nt;
-  const int w0 = xb / C;
-  const int w1 = (xb + nt - 1) / C;
-  if (w0 == w1 && a.out_dt == DT_F32) return;  // written by the split kernel
-  const int ns = w0 == w1 ? 1 : w1 - w0 + 1;  // states of this row, in wave order
+  const int xb = r.y, nt = r.z, C = r.w;
+  const int w0 = b - 1;                     // the wave holding the row's first tile
+  const int ns = (xb + nt - 1) / C - w0 + 1;  // states of this row, in wave order
   auto slot_of = [&](int k) __attribute__((always_inline)) -> int {
-    if (ns == 1) return 2 * NW + s * R + rho;
-    const int w = w0 + k;
-    return (w == w0 && xb != w0 * C) ? 2 * w0 + 1 : 2 * w;
+    return k == 0 ? (xb != w0 * C ? 2 * w0 + 1 : 2 * w0) : 2 * (w0 + k);
   };
-  float M[NPT], den[NPT], num[NPT];
+  const int j0 = lane * NPL;
+  const int g = j0 / D;
+  float M = -__builtin_inff(), den = 0.f, num[NPL];
 #pragma unroll
-  for (int k = 0; k < NPT; ++k) {
-    M[k] = -__builtin_inff();
-    den[k] = 0.f;
-    num[k] = 0.f;
-  }
+  for (int e = 0; e < NPL; ++e) num[e] = 0.f;
   for (int b0 = 0; b0 < ns; b0 += CH) {
-    float2 ml[NPT][CH];
-    float av[NPT][CH];
+    float2 ml[CH];
+    float av[CH][NPL];
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
-      const int slot = slot_of(b0 + q < ns ? b0 + q : ns - 1);
+      if (b0 + q < ns) {
+        const int64_t st = (int64_t)slot_of(b0 + q) * GC + g;
+        ml[q] = *reinterpret_cast<const float2*>(a.ws_ml + st * 2);
+        const float* src = a.ws_acc + st * D + (j0 - g * D);
+        if constexpr (NPL % 4 == 0) {
 #pragma unroll
-      for (int k = 0; k < NPT; ++k) {
-        const int j = min(threadIdx.x + k * kMergeThreads, GC * D - 1);
-        const int g = j / D;
-        ml[k][q] = *reinterpret_cast<const float2*>(a.ws_ml + ((int64_t)slot * GC + g) * 2);
-        av[k][q] = a.ws_acc[((int64_t)slot * GC + g) * D + (j - g * D)];
-      }
-    }
+          for (int e = 0; e < NPL; e += 4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(src + e);
+            av[q][e] = v4.x;
+            av[q][e + 1] = v4.y;
+            av[q][e + 2] = v4.z;
+            av[q][e + 3] = v4.w;
+          }
+        } else {
 #pragma unroll
-    for (int k = 0; k < NPT; ++k) {
-      float Mn = M[k];
-#pragma unroll
-      for (int q = 0; q < CH; ++q)
-        if (b0 + q < ns) Mn = fmaxf(Mn, ml[k][q].x);
-      const float rescale = M[k] == -__builtin_inff() ? 0.f : fast_exp2(M[k] - Mn);
-      float d = den[k] * rescale, n = num[k] * rescale;
-#pragma unroll
-      for (int q = 0; q < CH; ++q) {
-        if (b0 + q < ns) {
-          const float wq = fast_exp2(ml[k][q].x - Mn);
-          d += ml[k][q].y * wq;
-          n += av[k][q] * wq;
+          for (int e = 0; e < NPL; ++e) av[q][e] = src[e];
         }
       }
-      M[k] = Mn;
-      den[k] = d;
-      num[k] = n;
     }
-  }
+    float Mn = M;
 #pragma unroll
-  for (int k = 0; k < NPT; ++k) {
-    const int j = threadIdx.x + k * kMergeThreads;
-    if (j < GC * D) store_out(a.out, a.out_dt, obase + j, num[k] / den[k]);
-    if (a.lse && j < GC * D && j % D == 0)
-      a.lse[(int64_t)s * a.Hq + h0 + j / D] = M[k] + __log2f(den[k]);
+    for (int q = 0; q < CH; ++q)
+      if (b0 + q < ns) Mn = fmaxf(Mn, ml[q].x);
+    const float rescale = M == -__builtin_inff() ? 0.f : fast_exp2(M - Mn);
+    float d = den * rescale;
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) num[e] *= rescale;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      if (b0 + q < ns) {
+        const float wq = fast_exp2(ml[q].x - Mn);
+        d += ml[q].y * wq;
+#pragma unroll
+        for (int e = 0; e < NPL; ++e) num[e] += av[q][e] * wq;
+      }
+    }
+    M = Mn;
+    den = d;
   }
+  const int64_t o = ((int64_t)s * a.Hq + h0) * D + j0;
+  float res[NPL];
+#pragma unroll
+  for (int e = 0; e < NPL; ++e) res[e] = num[e] / den;
+  if constexpr (NPL % 8 == 0) {
+#pragma unroll
+    for (int e = 0; e < NPL; e += 8) store_out_vec<8>(a.out, a.out_dt, o + e, res + e);
+  } else if constexpr (NPL == 4) {
+    store_out_vec<4>(a.out, a.out_dt, o, res);
+  } else {
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) store_out(a.out, a.out_dt, o + e, res[e]);
+  }
+  if (a.lse && j0 % D == 0) a.lse[(int64_t)s * a.Hq + h0 + g] = M + __log2f(den);
 }
 
 // ---- host side -----------------------------------------------------------------
@@ -1082,7 +1107,10 @@ pkv_status launch_split(DecodeArgs a, int grid_cap, int ncu, hipStream_t stream)
                      dim3(kThreads), 0, stream, a);
   pkv_status st = check_launch("paged_attention_decode (split)");
   if (st != PKV_OK) return st;
-  hipLaunchKernelGGL((decode_merge_kernel<D, GC>), dim3(a.S * a.rows_per_seq),
+  // one merge wave per range boundary (the first range has none)
+  constexpr int kMergeWaves = kMergeThreads / 64;
+  const int nb = a.n_waves - 1;
+  hipLaunchKernelGGL((decode_merge_kernel<D, GC>), dim3((unsigned)((nb + kMergeWaves - 1) / kMergeWaves)),
                      dim3(kMergeThreads), 0, stream, a);
   return check_launch("paged_attention_decode (merge)");
 }
@@ -1186,13 +1214,22 @@ pkv_status plan_decode(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t /*
   if (grid > kMaxGrid) grid = kMaxGrid;
   if (grid < 1) grid = 1;
   plan->max_waves = (int)grid * kWaves;
-  // states: two slots per wave and one per row, gc heads each (whichever path runs)
-  const size_t states = (size_t)plan->max_waves * 2 * gc_max + (size_t)sc * Hkv * G;
+  // states: two slots per wave, gc heads each (whichever path runs)
+  const size_t states = (size_t)plan->max_waves * 2 * gc_max;
   plan->ws_ps_off = 0;
-  plan->ws_ml_off = align_up(((size_t)sc + 1) * sizeof(int32_t));
+  plan->ws_rec_off = align_up(((size_t)sc + 1) * sizeof(int32_t));
+  plan->ws_ml_off = plan->ws_rec_off + align_up((size_t)plan->max_waves * sizeof(int4));
   plan->ws_acc_off = plan->ws_ml_off + align_up(states * 2 * sizeof(float));
   plan->workspace_bytes = plan->ws_acc_off + states * (size_t)D * sizeof(float);
   return PKV_OK;
+}
+
+void attach_decode_workspace(DecodeArgs* a, const DecodePlan& plan, void* workspace) {
+  char* ws = static_cast<char*>(workspace);
+  a->ws_ps = reinterpret_cast<int32_t*>(ws + plan.ws_ps_off);
+  a->ws_rec = reinterpret_cast<int4*>(ws + plan.ws_rec_off);
+  a->ws_ml = reinterpret_cast<float*>(ws + plan.ws_ml_off);
+  a->ws_acc = reinterpret_cast<float*>(ws + plan.ws_acc_off);
 }
 
 pkv_status launch_decode(int kv_dt, bool fp8, const DecodePlan& plan, DecodeArgs a,

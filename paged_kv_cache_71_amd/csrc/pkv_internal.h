@@ -116,11 +116,14 @@ struct DecodePlan {
   int gc_mf;            // ... on the matrix-core path (4, 8 or 16 dividing G; 0: none)
   int max_waves;        // waves of the largest split launch (sizes the workspace)
   int seqs_per_launch;  // sequences handled by one split + merge launch pair
-  size_t ws_ps_off, ws_ml_off, ws_acc_off;  // workspace layout (bytes)
+  size_t ws_ps_off, ws_rec_off, ws_ml_off, ws_acc_off;  // workspace layout (bytes)
   size_t workspace_bytes;
 };
 pkv_status plan_decode(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
                        int32_t max_context_len, DecodePlan* plan);
+struct DecodeArgs;
+// point the workspace fields of a at the plan's layout inside ws
+void attach_decode_workspace(DecodeArgs* a, const DecodePlan& plan, void* ws);
 
 struct DecodeArgs {
   void* out;
@@ -130,6 +133,7 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   int32_t* ws_ps;   // [S + 1] prefix of tile counts (written by the split kernel)
+  int4* ws_rec;     // [n_waves] rows cut at each wave's start: the merge's work list
   float* ws_ml;     // [2 * n_waves, gc, 2] partial (c * max, sum) in log2 units
   float* ws_acc;    // [2 * n_waves, gc, D] partial accumulators
   int32_t max_nb;

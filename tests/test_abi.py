@@ -28,12 +28,12 @@ def test_status_strings(lib):
 
 def test_workspace_size(lib):
     # Llama-3-8B decode batch: fp32 softmax states (4 heads x (2 + 128) floats)
-    # in 2 slots per wave (at most 2048 workgroups x 4 waves) plus one slot per
-    # row (256 sequences x 8 KV heads), and the 257-entry prefix array; each
-    # part 256-byte aligned:  1280 + 18432 * 4 * 2 * 4 + 18432 * 4 * 128 * 4
-    assert pkv.decode_workspace_size(256, 32, 8, 128, 16, 8192) == 1280 + 589824 + 37748736
-    # tiny batch: at most 4 rows x ceil(33 / 8) tiles -> 80 waves -> 160 + 16 slots
-    assert pkv.decode_workspace_size(4, 4, 4, 64, 4, 33) == 256 + 1536 + 176 * 64 * 4
+    # in 2 slots per wave (at most 2048 workgroups x 4 waves = 8192 waves), one
+    # 16-byte merge record per wave, and the 257-entry prefix array; each part
+    # 256-byte aligned:  1280 + 8192 * 16 + 8192 * 2 * 4 * 2 * 4 + 8192 * 2 * 4 * 128 * 4
+    assert pkv.decode_workspace_size(256, 32, 8, 128, 16, 8192) == 1280 + 131072 + 524288 + 33554432
+    # tiny batch: at most 4 rows x ceil(33 / 8) tiles -> 80 waves -> 80 records, 160 slots
+    assert pkv.decode_workspace_size(4, 4, 4, 64, 4, 33) == 256 + 1280 + 1280 + 160 * 64 * 4
     assert pkv.decode_workspace_size(0, 4, 4, 64, 4, 33) == 0
     with pytest.raises(pkv.PkvError):
         pkv.decode_workspace_size(4, 6, 4, 64, 4, 33)                   # Hq % Hkv != 0

@@ -126,6 +126,23 @@ def test_low_precision_output_within_one_ulp(gpu_lib, out_dtype):
     assert np.mean(np.abs(diff) <= 1) > 0.999
 
 
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype,D,B,Hq,Hkv", [("bf16", 128, 16, 32, 8), ("bf16", 128, 16, 64, 4),
+                                               ("f16", 64, 4, 8, 2), ("f32", 64, 8, 4, 4)])
+def test_low_precision_output_is_the_rounded_fp32_output(gpu_lib, out_dtype, dtype, D, B, Hq, Hkv):
+    """Rows finished inside one wave, rows merged across waves and empty
+    contexts: a 16-bit output holds exactly the fp32 output rounded to nearest
+    even (the same fp32 value is computed on either path), on the matrix-core
+    and the vector path."""
+    lengths = [0, 1, 17, 300, 4100, 0, 2000, 65]
+    b = W.decode_batch(D + B + Hq, lengths, Hq, Hkv, D, B, dtype)
+    out32, _ = check(gpu_lib, b)
+    out16 = gpu_decode(gpu_lib, DevBatch(b), out_dtype)
+    want = out32.to(TORCH_DT[out_dtype])
+    assert torch.equal(out16.view(torch.int16), want.view(torch.int16))
+    assert torch.all(out16[0] == 0) and torch.all(out16[5] == 0)
+
+
 def _relayout(b: W.PagedBatch, seed: int, alias_copies: bool = False) -> W.PagedBatch:
     """Same logical contents, different physical blocks (a fresh permutation of
     the pool); optionally give every aliased block a private copy."""
