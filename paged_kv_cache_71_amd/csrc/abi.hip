@@ -346,6 +346,7 @@ static pkv_status prefill_args(void* out, pkv_dtype out_dtype, const void* q,
   a->out = out;
   a->q = q;
   a->cu_seqlens_q = cu_seqlens_q;
+  a->cu_base = 0;
   a->k_cache = k_cache;
   a->v_cache = v_cache;
   a->block_tables = block_tables;

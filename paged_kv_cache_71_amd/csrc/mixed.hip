@@ -24,38 +24,31 @@
 namespace pkv {
 namespace {
 
-// cu_out[i] = cu[num_decode + i] - num_decode, i <= S_p (the prefill chunks'
-// boundaries counted from their first row)
-__global__ void rebase_cu_kernel(const int32_t* __restrict__ cu, int32_t num_decode, int32_t S_p,
-                                 int32_t* __restrict__ cu_out) {
-  for (int i = threadIdx.x; i <= S_p; i += blockDim.x) cu_out[i] = cu[num_decode + i] - num_decode;
-}
-
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-// Workspace: the decode part's, the chunks' rebased cu_seqlens, the chunks'
-// split partial results (when their plan splits).
+// Workspace: the decode part's, then the chunks' split partial results (when
+// their plan splits).
 size_t mixed_workspace_size(const DecodePlan& plan, const PrefillPlan& pplan, int32_t S_prefill) {
-  return align_up(plan.workspace_bytes) + align_up(((size_t)S_prefill + 1) * sizeof(int32_t)) +
-         pplan.workspace_bytes;
+  (void)S_prefill;
+  return align_up(plan.workspace_bytes) + pplan.workspace_bytes;
 }
 
 pkv_status launch_mixed(int kv_dt, bool fp8, const DecodePlan& plan, const PrefillPlan& pplan,
                         const DecodeArgs& dec, const PrefillArgs& pre, int32_t num_decode,
                         void* workspace, hipStream_t stream) {
   const int32_t S_p = pre.S;
-  char* ws = static_cast<char*>(workspace);
-  int32_t* cu_p = reinterpret_cast<int32_t*>(ws + align_up(plan.workspace_bytes));
-  char* ws_split = reinterpret_cast<char*>(cu_p) + align_up(((size_t)S_p + 1) * sizeof(int32_t));
+  char* ws_split = static_cast<char*>(workspace) + align_up(plan.workspace_bytes);
   if (S_p == 0) return dec.S ? launch_decode(kv_dt, fp8, plan, dec, stream) : PKV_OK;
 
   PrefillArgs p = pre;
   const int es = dt_bytes(kv_dt), oes = dt_bytes(pre.out_dt);
   p.q = static_cast<const char*>(pre.q) + (int64_t)num_decode * pre.Hq * pre.D * es;
   p.out = static_cast<char*>(pre.out) + (int64_t)num_decode * pre.Hq * pre.D * oes;
-  p.cu_seqlens_q = cu_p;
+  // the chunks' boundaries, counted from their first row (row num_decode)
+  p.cu_seqlens_q = pre.cu_seqlens_q + num_decode;
+  p.cu_base = num_decode;
   p.Tq = pre.Tq - num_decode;
   p.block_tables = pre.block_tables + (int64_t)num_decode * pre.max_nb;
   p.context_lens = pre.context_lens + num_decode;
@@ -70,10 +63,7 @@ pkv_status launch_mixed(int kv_dt, bool fp8, const DecodePlan& plan, const Prefi
     const pkv_status sd = launch_decode(kv_dt, fp8, plan, dec, stream);
     if (sd != PKV_OK) return sd;
   }
-  hipLaunchKernelGGL(rebase_cu_kernel, dim3(1), dim3(256), 0, stream, pre.cu_seqlens_q, num_decode,
-                     S_p, cu_p);
-  const pkv_status st = check_launch("mixed (rebase)");
-  return st != PKV_OK ? st : launch_prefill(fp8 ? (int)DT_FP8 : kv_dt, p, stream);
+  return launch_prefill(fp8 ? (int)DT_FP8 : kv_dt, p, stream);
 }
 
 }  // namespace pkv

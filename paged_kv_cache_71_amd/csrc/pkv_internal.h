@@ -167,6 +167,8 @@ struct PrefillArgs {
   void* out;
   const void* q;
   const int32_t* cu_seqlens_q;
+  int32_t cu_base;   // subtracted from every cu_seqlens_q entry (mixed batches:
+                     // the decode rows that come before the chunks)
   const void* k_cache;
   const void* v_cache;
   const int32_t* block_tables;

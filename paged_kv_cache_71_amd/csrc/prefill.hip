@@ -24,6 +24,11 @@
 #include "pkv_internal.h"
 
 namespace pkv {
+
+// query-row boundary i of the launch's sequences (rows counted from q / out)
+__device__ __forceinline__ int cu_at(const PrefillArgs& a, int i) {
+  return a.cu_seqlens_q[i] - a.cu_base;
+}
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -138,8 +143,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
   }
   const int s = pair / a.Hkv;
   const int kvh = pair % a.Hkv;
-  const int q0 = a.cu_seqlens_q[s];
-  const int Qs = a.cu_seqlens_q[s + 1] - q0;
+  const int q0 = cu_at(a, s);
+  const int Qs = cu_at(a, s + 1) - q0;
   const int L = min(a.context_lens[s], a.max_ctx);  // a larger value would overrun the table
   const int tq0 = qt * TQ;
   if (tq0 >= Qs || Qs > L) return;
@@ -487,8 +492,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int sp = u % ns;
   const int s = pair / a.Hkv;
   const int kvh = pair % a.Hkv;
-  const int q0 = a.cu_seqlens_q[s];
-  const int Qs = a.cu_seqlens_q[s + 1] - q0;
+  const int q0 = cu_at(a, s);
+  const int Qs = cu_at(a, s + 1) - q0;
   const int L = min(a.context_lens[s], a.max_ctx);
   const int tq0 = qt * TQ;
   if (tq0 >= Qs || Qs > L) return;  // uniform over the workgroup, before any barrier
@@ -882,13 +887,13 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a)
   if (row >= nrows) return;
   const int t = (int)(row / a.Hq);
   int lo = 0, hi = a.S;  // sequence of token t: last s with cu[s] <= t
-  if (t >= a.cu_seqlens_q[a.S]) return;
+  if (t >= cu_at(a, a.S)) return;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (a.cu_seqlens_q[mid] <= t) lo = mid; else hi = mid;
+    if (cu_at(a, mid) <= t) lo = mid; else hi = mid;
   }
-  const int q0 = a.cu_seqlens_q[lo];
-  const int Qs = a.cu_seqlens_q[lo + 1] - q0;
+  const int q0 = cu_at(a, lo);
+  const int Qs = cu_at(a, lo + 1) - q0;
   const int L = min(a.context_lens[lo], a.max_ctx);
   if (Qs > L) return;  // skipped by the tile kernel as well
   const int TQ = RW / (a.Hq / a.Hkv);
@@ -927,11 +932,11 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillArgs a) {
   int lo = 0, hi = a.S;  // sequence of this row: last s with cu[s] <= row
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (a.cu_seqlens_q[mid] <= row) lo = mid; else hi = mid;
+    if (cu_at(a, mid) <= row) lo = mid; else hi = mid;
   }
   const int s = lo;
-  const int q0 = a.cu_seqlens_q[s];
-  const int Qs = a.cu_seqlens_q[s + 1] - q0;
+  const int q0 = cu_at(a, s);
+  const int Qs = cu_at(a, s + 1) - q0;
   const int L = min(a.context_lens[s], a.max_ctx);
   if (Qs > L) return;
   const int visible = L - Qs + (row - q0) + 1;
