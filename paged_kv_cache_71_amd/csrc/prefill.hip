@@ -874,15 +874,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // Merge of split prefill results ("Flash-Decoding" style log-sum-exp merge of
-// partial softmax results over disjoint KV ranges): one wave per output row
-// (token, query head); rows whose range was not split were written by the
-// tile kernel and are skipped.
+// partial softmax results over disjoint KV ranges): 16 lanes per output row
+// (token, query head), 16 rows per workgroup, 16-byte loads; rows whose range
+// was not split were written by the tile kernel and are skipped.  The splits'
+// (m, l) pairs and partial outputs are loaded CH at a time, so a row costs one
+// memory round trip for up to CH splits:
+//   out = sum_i e^(m_i - M) o_i / sum_i e^(m_i - M) l_i.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a) {
-  constexpr int EPL = D / 64;
+  constexpr int EPL = D / 16;  // outputs per lane: 8 or 4
+  constexpr int NV = EPL / 4;  // float4 loads per lane and split
+  constexpr int CH = 8;
   constexpr int RW = kWaves * 16 * kTileQB;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int c0 = (threadIdx.x & 15) * EPL;
   const int64_t nrows = (int64_t)a.Tq * a.Hq;
   if (row >= nrows) return;
   const int t = (int)(row / a.Hq);
@@ -903,22 +908,52 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a)
   const int nu = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
   if (nu <= 1) return;
   const int64_t stride = nrows;
-  float M = -__builtin_inff();
-  for (int i = 0; i < nu; ++i) M = fmaxf(M, a.ws_ml[(i * stride + row) * 2]);
-  float den = 0.f, acc[EPL];
+  float M = -__builtin_inff(), den = 0.f, acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int i = 0; i < nu; ++i) {
-    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + (i * stride + row) * 2);
-    const float w = fast_exp2(ml.x - M);  // a split no row position reaches: m = -inf, w = 0
-    den += w * ml.y;
-    const float* po = a.ws_o + (i * stride + row) * D + lane * EPL;
+  for (int b0 = 0; b0 < nu; b0 += CH) {
+    float2 ml[CH];
+    float4 po[CH][NV];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += w * po[e];
+    for (int q = 0; q < CH; ++q) {
+      if (b0 + q < nu) {
+        const int64_t r = (int64_t)(b0 + q) * stride + row;
+        ml[q] = *reinterpret_cast<const float2*>(a.ws_ml + r * 2);
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          po[q][v] = *reinterpret_cast<const float4*>(a.ws_o + r * D + c0 + 4 * v);
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int q = 0; q < CH; ++q)
+      if (b0 + q < nu) Mn = fmaxf(Mn, ml[q].x);
+    // a split no row position reaches has m = -inf and weight 0
+    const float rescale = M == -__builtin_inff() ? 0.f : fast_exp2(M - Mn);
+    den *= rescale;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= rescale;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      if (b0 + q < nu) {
+        const float w = fast_exp2(ml[q].x - Mn);
+        den += w * ml[q].y;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          acc[4 * v] += w * po[q][v].x;
+          acc[4 * v + 1] += w * po[q][v].y;
+          acc[4 * v + 2] += w * po[q][v].z;
+          acc[4 * v + 3] += w * po[q][v].w;
+        }
+      }
+    }
+    M = Mn;
   }
   const float inv = 1.f / den;
+  float res[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) store_out(a.out, a.out_dt, row * D + lane * EPL + e, acc[e] * inv);
+  for (int e = 0; e < EPL; ++e) res[e] = acc[e] * inv;
+  store_out_vec<EPL>(a.out, a.out_dt, row * D + c0, res);
 }
 
 // fp32 KV: one wave per (query token, KV head); each lane owns D/64 elements
@@ -999,7 +1034,7 @@ pkv_status launch_tile(const PrefillArgs& a, hipStream_t stream) {
                      stream, a);
   pkv_status st = check_launch("paged_attention_prefill");
   if (st != PKV_OK || a.n_split <= 1) return st;
-  const int64_t mgrid = ((int64_t)a.Tq * a.Hq + 3) / 4;
+  const int64_t mgrid = ((int64_t)a.Tq * a.Hq + 15) / 16;  // 16 rows per workgroup
   if (mgrid > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "prefill merge grid too large");
   hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3((unsigned)mgrid), dim3(256), 0, stream, a);
   return check_launch("paged_attention_prefill (merge)");
