@@ -70,16 +70,21 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{x, y}), h16x2_t));
   }
 }
-// The two 16-bit values of a word back in fp32 (exact).
-template <int DT>
-__device__ __forceinline__ float lo16(uint32_t w) {
-  if constexpr (DT == DT_BF16) return __uint_as_float(w << 16);
-  else return (float)__builtin_bit_cast(_Float16, (uint16_t)w);
-}
-template <int DT>
-__device__ __forceinline__ float hi16(uint32_t w) {
-  if constexpr (DT == DT_BF16) return __uint_as_float(w & 0xffff0000u);
-  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+// The lo part of a bf16 hi/lo split: x - (bf16 value in half H of w), where
+// that value is x rounded to bf16.  The difference has at most 16 significant
+// bits, so it is exact in fp32 whatever the rounding of the sum; one packed
+// dot2 instruction (w . (-1, -0) + x, or w . (+0, -1) + x) replaces an unpack
+// and a subtraction (x is finite, so the zero factor adds nothing).  The
+// low-half constant carries -0 in its high half: as (-1, +0) = 0x0000bf80 the
+// compiler encodes it as the inline constant -1.0, which the hardware reads
+// as the fp32 pattern 0xbf800000, i.e. -1 in the high half (measured: wrong
+// residuals); 0x8000bf80 has no inline form and goes out as a literal.
+template <int H>
+__device__ __forceinline__ float bf16_residual(float x, uint32_t w) {
+  typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));
+  constexpr uint32_t kMinusOne = H == 0 ? 0x8000bf80u : 0xbf800000u;  // -1.0 in half H
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b16x2_t, w),
+                                         __builtin_bit_cast(b16x2_t, kMinusOne), x, false);
 }
 
 template <bool V>
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
       lsum += p0 + p1;
       const uint32_t h = pack2<DT>(p0, p1);
       ph[v / 2] = h;
-      if constexpr (PSPLIT) pl[v / 2] = pack2<DT>(p0 - lo16<DT>(h), p1 - hi16<DT>(h));
+      if constexpr (PSPLIT) pl[v / 2] = pack2<DT>(bf16_residual<0>(p0, h), bf16_residual<1>(p1, h));
     }
     // O^T += V^T P^T over the tile's 32 tokens (two MFMAs of 16 tokens each)
 #pragma unroll
@@ -765,7 +770,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           rs += p0 + p1;
           const uint32_t h = pack2<DT>(p0, p1);
           hw[k / 2] = h;
-          if constexpr (PSPLIT) lw[k / 2] = pack2<DT>(p0 - lo16<DT>(h), p1 - hi16<DT>(h));
+          if constexpr (PSPLIT) lw[k / 2] = pack2<DT>(bf16_residual<0>(p0, h), bf16_residual<1>(p1, h));
         }
         nph[c] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
         if constexpr (PSPLIT) npl[c] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
