@@ -464,7 +464,7 @@ pkv_status pkv_mixed_workspace_size(int32_t S, int32_t num_decode, int32_t Tq,
   }
   const PrefillPlan pplan = plan_prefill(kv_dtype, S - num_decode, Tq - num_decode, max_query_len,
                                          Hq, Hkv, D, B, max_context_len);
-  *bytes = mixed_workspace_size(plan, pplan, S - num_decode);
+  *bytes = mixed_workspace_size(plan, pplan);
   return PKV_OK;
 }
 
@@ -498,7 +498,7 @@ static pkv_status mixed_impl(void* out, pkv_dtype out_dtype, const void* q,
   const PrefillPlan pplan = plan_prefill(fp8 ? (int)DT_FP8 : (int)kv_dtype, S - num_decode,
                                          Tq - num_decode, max_query_len, Hq, Hkv, D, B,
                                          max_context_len);
-  const size_t need = mixed_workspace_size(plan, pplan, S - num_decode);
+  const size_t need = mixed_workspace_size(plan, pplan);
   PKV_REQUIRE(workspace && workspace_bytes >= need, PKV_ERR_WORKSPACE,
               "mixed: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   DecodeArgs da{};

@@ -30,8 +30,7 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace: the decode part's, then the chunks' split partial results (when
 // their plan splits).
-size_t mixed_workspace_size(const DecodePlan& plan, const PrefillPlan& pplan, int32_t S_prefill) {
-  (void)S_prefill;
+size_t mixed_workspace_size(const DecodePlan& plan, const PrefillPlan& pplan) {
   return align_up(plan.workspace_bytes) + pplan.workspace_bytes;
 }
 

@@ -206,7 +206,7 @@ int device_cu_count();
 // Mixed decode + prefill batch (mixed.hip): the decode part (dec.S sequences,
 // plan for them) and the prefill part (pre: the whole batch's pointers, pre.S =
 // number of prefill sequences after the num_decode decodes).
-size_t mixed_workspace_size(const DecodePlan& plan, const PrefillPlan& pplan, int32_t S_prefill);
+size_t mixed_workspace_size(const DecodePlan& plan, const PrefillPlan& pplan);
 pkv_status launch_mixed(int kv_dt, bool fp8, const DecodePlan& plan, const PrefillPlan& pplan,
                         const DecodeArgs& dec, const PrefillArgs& pre, int32_t num_decode,
                         void* workspace, hipStream_t stream);
