@@ -70,21 +70,29 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{x, y}), h16x2_t));
   }
 }
-// The lo part of a bf16 hi/lo split: x - (bf16 value in half H of w), where
-// that value is x rounded to bf16.  The difference has at most 16 significant
-// bits, so it is exact in fp32 whatever the rounding of the sum; one packed
-// dot2 instruction (w . (-1, -0) + x, or w . (+0, -1) + x) replaces an unpack
-// and a subtraction (x is finite, so the zero factor adds nothing).  The
-// low-half constant carries -0 in its high half: as (-1, +0) = 0x0000bf80 the
-// compiler encodes it as the inline constant -1.0, which the hardware reads
-// as the fp32 pattern 0xbf800000, i.e. -1 in the high half (measured: wrong
-// residuals); 0x8000bf80 has no inline form and goes out as a literal.
-template <int H>
-__device__ __forceinline__ float bf16_residual(float x, uint32_t w) {
-  typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));
-  constexpr uint32_t kMinusOne = H == 0 ? 0x8000bf80u : 0xbf800000u;  // -1.0 in half H
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b16x2_t, w),
-                                         __builtin_bit_cast(b16x2_t, kMinusOne), x, false);
+// The lo part of a 16-bit hi/lo split: x - (16-bit value in half H of w),
+// where that value is x rounded to dtype DT.  The difference has at most 16
+// significant bits, so it is exact in fp32 whatever the rounding of the sum;
+// one packed dot2 instruction (w . (-1, -0) + x, or w . (+0, -1) + x)
+// replaces an unpack and a subtraction (x is finite, so the zero factor adds
+// nothing).  The low-half constant carries -0 in its high half: as (-1, +0)
+// = 0x0000bf80 the compiler encodes the bf16 word as the inline constant
+// -1.0, which the hardware reads as the fp32 pattern 0xbf800000, i.e. -1 in
+// the high half (measured: wrong residuals); with -0 above it the word has no
+// inline form and goes out as a literal.
+template <int DT, int H>
+__device__ __forceinline__ float residual16(float x, uint32_t w) {
+  if constexpr (DT == DT_BF16) {
+    typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));
+    constexpr uint32_t kMinusOne = H == 0 ? 0x8000bf80u : 0xbf800000u;  // -1.0 in half H
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b16x2_t, w),
+                                           __builtin_bit_cast(b16x2_t, kMinusOne), x, false);
+  } else {
+    typedef _Float16 h16x2_t __attribute__((ext_vector_type(2)));
+    constexpr uint32_t kMinusOne = H == 0 ? 0x8000bc00u : 0xbc000000u;  // -1.0 in half H
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2_t, w),
+                                  __builtin_bit_cast(h16x2_t, kMinusOne), x, false);
+  }
 }
 
 template <bool V>
@@ -110,9 +118,10 @@ __device__ __forceinline__ u32x4_t as_v(uint4 x) { return u32x4_t{x.x, x.y, x.z,
 //    <= 256 and most tiles skip the rescale.
 //  * O^T = V^T P^T: V is staged in LDS transposed ([d][token], double
 //    buffered, one barrier per tile) and read as the A operand; the weights
-//    P^T come straight out of the score registers as the B operand.  For bf16
-//    the weights are split into hi + lo bf16 parts (two MFMAs), keeping ~16
-//    significant bits; for f16 one f16 operand (11 bits) suffices.
+//    P^T come straight out of the score registers as the B operand, split
+//    into hi + lo 16-bit parts (two MFMAs), keeping ~16 significant bits of
+//    the weights (bf16 and f16 alike: one f16 operand rounds a dominant
+//    weight by up to 2^-12, which times |v| near 9 exceeds the 2e-3 bound).
 //  * Workgroups of one (sequence, KV head) are mapped to the same XCD
 //    (blockIdx % 8), so their shared K/V tiles are served from that XCD's L2.
 template <int DT, int D, bool PSPLIT>
@@ -294,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
       lsum += p0 + p1;
       const uint32_t h = pack2<DT>(p0, p1);
       ph[v / 2] = h;
-      if constexpr (PSPLIT) pl[v / 2] = pack2<DT>(bf16_residual<0>(p0, h), bf16_residual<1>(p1, h));
+      if constexpr (PSPLIT) pl[v / 2] = pack2<DT>(residual16<DT, 0>(p0, h), residual16<DT, 1>(p1, h));
     }
     // O^T += V^T P^T over the tile's 32 tokens (two MFMAs of 16 tokens each)
 #pragma unroll
@@ -362,9 +371,9 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
 //  * O^T += V^T P^T: V^T is the A operand, read from row-major LDS with the
 //    gfx950 transposing read ds_read_b64_tr_b16; P^T is the B operand straight
 //    from the score registers.  Both use the same order of the 32 tile tokens
-//    (4g + k, then 16 + 4g + k), so the product over them is unchanged.  bf16:
-//    P is split into hi + lo bf16 parts (two MFMAs), keeping ~16 significant
-//    bits of the weights.
+//    (4g + k, then 16 + 4g + k), so the product over them is unchanged.  P
+//    is split into hi + lo 16-bit parts (two MFMAs), keeping ~16 significant
+//    bits of the weights, for f16 as for bf16 (see the kernel above).
 //  * Software pipeline: in the step for tile j the matrix cores run
 //    O += P(j-1) V(j-1) and S(j+1) = Q K(j+1)^T while the vector ALU runs the
 //    softmax of S(j), all three independent, so each wave's instruction
@@ -464,7 +473,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   using Chunk = std::conditional_t<CBP == 16, uint4, uint2>;
   static_assert(CBP == 16 || CBP == 8, "staging chunk");
   constexpr int RW = kWaves * 16 * QB;        // query rows per workgroup
-  constexpr bool PSPLIT = DT == DT_BF16;
+  constexpr bool PSPLIT = true;  // hi + lo parts of P for both 16-bit dtypes
   static_assert(NCH >= 1 && kTileKV * CPR % kThreads == 0, "staging split");
   static_assert(16 % (64 / CPR) == 0, "a wave's staged rows must lie in one 16-token half");
 
@@ -770,7 +779,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           rs += p0 + p1;
           const uint32_t h = pack2<DT>(p0, p1);
           hw[k / 2] = h;
-          if constexpr (PSPLIT) lw[k / 2] = pack2<DT>(bf16_residual<0>(p0, h), bf16_residual<1>(p1, h));
+          if constexpr (PSPLIT) lw[k / 2] = pack2<DT>(residual16<DT, 0>(p0, h), residual16<DT, 1>(p1, h));
         }
         nph[c] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
         if constexpr (PSPLIT) npl[c] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
@@ -1056,8 +1065,7 @@ pkv_status launch_mfma(const PrefillArgs& a, hipStream_t stream) {
   const int64_t grid = nqt * a.S * a.Hkv;
   if (grid == 0) return PKV_OK;
   if (grid > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "prefill grid too large");
-  constexpr bool split = DT == DT_BF16;
-  hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, split>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, true>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, a);
   return check_launch("paged_attention_prefill");
 }

@@ -56,7 +56,7 @@ def _prefill_layout(rng, S, Hq, D, max_chunk, max_prior):
         max_prior = max(1, max_prior // 2)
 
 
-@pytest.mark.parametrize("case", range(40))
+@pytest.mark.parametrize("case", range(80))
 def test_random_decode(gpu_lib, case):
     rng = np.random.default_rng(1000 + case)
     Hq, Hkv, D = _heads(rng)
@@ -71,7 +71,7 @@ def test_random_decode(gpu_lib, case):
     check_decode(gpu_lib, b)
 
 
-@pytest.mark.parametrize("case", range(30))
+@pytest.mark.parametrize("case", range(60))
 def test_random_prefill(gpu_lib, case):
     rng = np.random.default_rng(3000 + case)
     Hq, Hkv, D = _heads(rng)
@@ -86,7 +86,7 @@ def test_random_prefill(gpu_lib, case):
     check_prefill(gpu_lib, b)
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(24))
 def test_random_mixed(gpu_lib, case):
     rng = np.random.default_rng(5000 + case)
     Hq, Hkv, D = _heads(rng)
@@ -103,7 +103,7 @@ def test_random_mixed(gpu_lib, case):
     check_mixed(gpu_lib, b)
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(24))
 def test_random_decode_fp8(gpu_lib, case):
     rng = np.random.default_rng(7000 + case)
     Hq, Hkv, D = _heads(rng)
@@ -118,7 +118,7 @@ def test_random_decode_fp8(gpu_lib, case):
     check_decode_fp8(gpu_lib, b, seed=case)
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(24))
 def test_random_prefill_fp8(gpu_lib, case):
     rng = np.random.default_rng(9000 + case)
     Hq, Hkv, D = _heads(rng)
@@ -133,7 +133,7 @@ def test_random_prefill_fp8(gpu_lib, case):
     check_prefill_fp8(gpu_lib, b, seed=case)
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(24))
 def test_random_cascade(gpu_lib, case):
     rng = np.random.default_rng(11000 + case)
     Hq, Hkv, D = _heads(rng)
