@@ -971,7 +971,9 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a)
 }
 
 // fp32 KV: one wave per (query token, KV head); each lane owns D/64 elements
-// of every head of the group and the wave walks the visible tokens one by one.
+// of every head of the group and the wave walks the visible tokens one by one,
+// keeping the softmax's running sums in fp64 (a parity path for fp32 pools:
+// the 1e-5 bound must hold over contexts of thousands of tokens).
 template <int D, int GMAX>
 __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillArgs a) {
   constexpr int EPL = D / 64;
@@ -996,13 +998,14 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillArgs a) {
   const float* vc = static_cast<const float*>(a.v_cache);
   for (int g0 = 0; g0 < G; g0 += GMAX) {
     const int gn = min(GMAX, G - g0);
-    float q[GMAX][EPL], acc[GMAX][EPL], m[GMAX], l[GMAX];
+    float q[GMAX][EPL], m[GMAX];
+    double acc[GMAX][EPL], l[GMAX];
     for (int g = 0; g < GMAX; ++g) {
       m[g] = -__builtin_inff();
-      l[g] = 0.f;
+      l[g] = 0.0;
       for (int e = 0; e < EPL; ++e) {
         q[g][e] = g < gn ? qrow[(int64_t)(g0 + g) * D + lane * EPL + e] : 0.f;
-        acc[g][e] = 0.f;
+        acc[g][e] = 0.0;
       }
     }
     for (int t = 0; t < visible; ++t) {
@@ -1018,12 +1021,15 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillArgs a) {
         float z = 0.f;
         for (int e = 0; e < EPL; ++e) z = fmaf(q[g][e], kv[e], z);
         for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
-        z *= a.scale_log2;
-        const float mn = fmaxf(m[g], z);
+        // the scale enters the exponent through one fma (raw * scale - max), so
+        // a large score is not rounded before the max is taken off
+        const float mn = fmaxf(m[g], z * a.scale_log2);
         const float alpha = fast_exp2(m[g] - mn);
-        const float p = fast_exp2(z - mn);
+        const float p = fast_exp2(__builtin_fmaf(z, a.scale_log2, -mn));
+        // running sums in fp64: over thousands of tokens the fp32 rounding of
+        // a token-by-token sum reaches 1e-5 of a sharp softmax's output
         l[g] = l[g] * alpha + p;
-        for (int e = 0; e < EPL; ++e) acc[g][e] = acc[g][e] * alpha + p * vv[e];
+        for (int e = 0; e < EPL; ++e) acc[g][e] = acc[g][e] * alpha + (double)p * vv[e];
         m[g] = mn;
       }
     }
@@ -1031,7 +1037,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillArgs a) {
     for (int g = 0; g < GMAX; ++g)
       for (int e = 0; e < EPL && g < gn; ++e)
         store_out(a.out, a.out_dt, ((int64_t)row * a.Hq + (int64_t)kvh * G + g0 + g) * D + lane * EPL + e,
-                  acc[g][e] / l[g]);
+                  (float)(acc[g][e] / l[g]));
   }
 }
 

@@ -156,3 +156,12 @@ def test_prefill_context_of_131072_tokens(gpu_lib):
     is split into long splits; sampled rows against the oracle."""
     b = W.varlen_prefill(8, [130816], [256], 32, 8, 128, 16, "bf16")
     check(gpu_lib, b, rows=[0, 1, 127, 128, 255])
+
+
+def test_f32_long_context_sharp_softmax(gpu_lib):
+    """fp32 pools, a 5819-token prior context, a sharp softmax (scale 2.5/sqrt(D)):
+    the 1e-5 bound holds only if the running sums do not collect fp32 rounding
+    token by token (measured 1.2e-5 to 1.7e-5 before fp64 running sums)."""
+    b = W.varlen_prefill(91, [5819, 2672], [178, 72], 8, 1, 64, 32, "f32")
+    b.scale = 2.5 / np.sqrt(64)
+    check(gpu_lib, b)
