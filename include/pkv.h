@@ -10,7 +10,10 @@
  *    DEVICE pointers (hipMalloc'd or torch CUDA tensors on the current device);
  *    the library allocates no device memory and keeps no state beyond a
  *    thread-local error string, the host block managers the caller creates
- *    and a per-device cache of the CU count.
+ *    and caches of the per-device CU count and of kernel occupancies.
+ *  - Threads: the kernel calls may be made from several host threads at once
+ *    (the caches are atomic); calls that overlap on one device need their own
+ *    workspaces.
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  *    stream).  Kernel calls are asynchronous on that stream.
  *  - Errors: scalar arguments are validated on the host before any launch; a

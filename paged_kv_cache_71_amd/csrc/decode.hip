@@ -58,6 +58,7 @@
 //    exactly in registers (gfx950 conversions) right before use, the K scale
 //    of the row's KV head is folded into the score scale and the V scale
 //    into the finished accumulator.
+#include <atomic>
 #include <type_traits>
 
 #include "pkv_internal.h"
@@ -1075,19 +1076,23 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
 
 // ---- host side -----------------------------------------------------------------
 
+// (the caches below may be filled by several host threads at once: atomics,
+// every writer stores the same value)
 template <int DT, int D, int GC, bool UNI, bool MF, bool F8>
 int occupancy_of() {
-  static int occ = -1;
-  if (occ < 0) {
+  static std::atomic<int> occ{-1};
+  int o = occ.load(std::memory_order_relaxed);
+  if (o < 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &n, reinterpret_cast<const void*>(&decode_split_kernel<DT, D, GC, UNI, MF, F8>), kThreads,
             0) != hipSuccess ||
         n < 1)
       n = 1;
-    occ = n;
+    occ.store(n, std::memory_order_relaxed);
+    o = n;
   }
-  return occ;
+  return o;
 }
 
 // Split launch (one resident wave set: CUs x occupancy, capped by grid_cap)
@@ -1164,11 +1169,14 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 int device_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  static int cache[64] = {0};
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  static std::atomic<int> cache[64];  // zero-initialised: not yet queried
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-  if (dev >= 0 && dev < 64 && n > 0) cache[dev] = n;
+  if (dev >= 0 && dev < 64 && n > 0) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 

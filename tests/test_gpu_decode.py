@@ -208,3 +208,41 @@ def test_opt13b_full_size(gpu_lib):
 def test_shared_prefix_full_size_sampled(gpu_lib):
     b = W.shared_prefix_bf16(0)
     check(gpu_lib, b, seqs=list(range(0, 256, 17)))
+
+
+def test_concurrent_host_threads(gpu_lib):
+    """Four host threads call decode at once, each on its own stream with its own
+    workspace (the library's caches are shared): every result equals the same
+    call made alone, bit for bit."""
+    import threading
+    batches = [W.decode_batch(300 + i, [5, 700, 1500, 33, 2048], 32, 8, 128, 16, "bf16") for i in range(4)]
+    devs = [DevBatch(b) for b in batches]
+    alone = [gpu_decode(gpu_lib, d).clone() for d in devs]
+    outs = [None] * 4
+    errors = []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                b, d = batches[i], devs[i]
+                n = gpu_lib.decode_workspace_size(b.S, b.Hq, b.Hkv, b.D, b.B, b.max_context_len)
+                ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+                out = d.out("f32")
+                for _ in range(5):
+                    gpu_lib.paged_attention_decode(out, d.q, d.k_cache, d.v_cache, d.block_tables,
+                                                   d.context_lens, b.max_context_len, b.scale,
+                                                   workspace=ws)
+                s.synchronize()
+                outs[i] = out
+        except Exception as e:  # reported below, on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i in range(4):
+        assert torch.equal(outs[i], alone[i])
