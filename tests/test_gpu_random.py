@@ -2,8 +2,9 @@
 shape (head dim, KV heads, group size, block size), dtype, length mix (empty
 contexts, contexts shorter than a block, long ones), chunk layout and softmax
 scale, for decode, prefill, mixed batches, cascade (shared-prefix) decode and
-the FP8 variants; half of the decode and prefill cases also check that a
-16-bit output is exactly the fp32 output rounded to nearest even.  Each case
+the FP8 variants; every mixed and cascade case and half of the decode and
+prefill cases also check that a 16-bit output is exactly the fp32 output
+rounded to nearest even.  Each case
 prints its parameters before it runs, so a failure names the draw.  The
 fixed-shape tests cover the named configurations; this sweep covers the
 combinations between them."""
@@ -15,6 +16,7 @@ import oracle
 from gpu_util import TOL, TORCH_DT, DevBatch, max_abs
 from paged_kv_cache_71_amd import workloads as W
 from test_gpu_cascade import check as check_cascade
+from test_gpu_cascade import gpu_cascade
 from test_gpu_decode import check as check_decode
 from test_gpu_decode import gpu_decode
 from test_gpu_fp8 import Fp8Dev
@@ -22,6 +24,7 @@ from test_gpu_fp8 import check as check_decode_fp8
 from test_gpu_fp8 import check_prefill as check_prefill_fp8
 from test_gpu_fp8 import oracle_decode as oracle_decode_fp8
 from test_gpu_mixed import check as check_mixed
+from test_gpu_mixed import run_mixed
 from test_gpu_prefill import check as check_prefill
 from test_gpu_prefill import gpu_prefill
 
@@ -120,7 +123,9 @@ def test_random_mixed(gpu_lib, case):
           f"prior={prior.tolist()} chunks={chunks.tolist()}", flush=True)
     b = W.mixed_batch(6000 + case, dl, prior, chunks, Hq, Hkv, D, B, dtype)
     b.scale = _scale(rng, D)
-    check_mixed(gpu_lib, b)
+    out32 = check_mixed(gpu_lib, b)
+    odt = "bf16" if case % 2 == 0 else "f16"
+    assert _same_as_rounded(out32, run_mixed(gpu_lib, DevBatch(b), odt), odt)
 
 
 @pytest.mark.parametrize("case", range(24))
@@ -166,7 +171,10 @@ def test_random_cascade(gpu_lib, case):
           f"prefix_blocks={pblocks} suffixes={suffix.tolist()}", flush=True)
     b = W.grouped_batch(12000 + case, sizes, pblocks, suffix, Hq, Hkv, D, B, dtype)
     b.scale = _scale(rng, D)
-    check_cascade(gpu_lib, b)
+    out32, _, db = check_cascade(gpu_lib, b)
+    odt = "bf16" if case % 2 == 0 else "f16"
+    out16 = gpu_cascade(gpu_lib, db, b.meta["cu_group_seqs"], b.meta["group_prefix_lens"], out_dtype=odt)
+    assert _same_as_rounded(out32, out16, odt)
 
 
 @pytest.mark.parametrize("case", range(16))
