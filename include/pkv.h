@@ -283,7 +283,7 @@ pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const voi
  *   workspace          : pkv_prefill_workspace_size(..., PKV_FP8_E4M3, ...)
  * Every cached element is read as code * scale of its KV head (exact in
  * fp32); the codes are widened to q_dtype exactly and the products run on the
- * matrix cores as in the 16-bit prefill.  Needs block_size >= 16 and at most
+ * matrix cores as in the 16-bit prefill.  Needs block_size >= 8 and at most
  * 128 query heads per KV head (PKV_ERR_UNSUPPORTED otherwise).
  * ------------------------------------------------------------------------ */
 pkv_status pkv_paged_attention_prefill_fp8(void* out, pkv_dtype out_dtype, const void* q,
@@ -337,7 +337,7 @@ pkv_status pkv_paged_attention_mixed(void* out, pkv_dtype out_dtype, const void*
  * v_scale as for pkv_paged_attention_decode_fp8; the workspace is
  * pkv_mixed_workspace_size(..., PKV_FP8_E4M3, ...).  Every row equals what
  * pkv_paged_attention_decode_fp8 / pkv_paged_attention_prefill_fp8 give for
- * it, bit for bit; the chunks need block_size >= 16. */
+ * it, bit for bit; the chunks need block_size >= 8. */
 pkv_status pkv_paged_attention_mixed_fp8(void* out, pkv_dtype out_dtype, const void* q,
                                          pkv_dtype q_dtype, const int32_t* cu_seqlens_q,
                                          int32_t Tq, int32_t num_decode, int32_t max_query_len,

@@ -335,8 +335,8 @@ static pkv_status prefill_args(void* out, pkv_dtype out_dtype, const void* q,
   PKV_REQUIRE(!fp8 || kv_dtype != PKV_F32, PKV_ERR_UNSUPPORTED, "prefill_fp8: q must be f16 or bf16");
   PKV_REQUIRE((int64_t)B * Hkv * D * (fp8 ? 1 : dt_bytes(kv_dtype)) < ((int64_t)1 << 31),
               PKV_ERR_UNSUPPORTED, "prefill: one block of one pool must be smaller than 2 GiB");
-  PKV_REQUIRE(!fp8 || (B >= 16 && Hq / Hkv <= 128), PKV_ERR_UNSUPPORTED,
-              "prefill_fp8: needs block_size >= 16 and at most 128 query heads per KV head "
+  PKV_REQUIRE(!fp8 || (B >= 8 && Hq / Hkv <= 128), PKV_ERR_UNSUPPORTED,
+              "prefill_fp8: needs block_size >= 8 and at most 128 query heads per KV head "
               "(B=%d, G=%d)", B, Hq / Hkv);
   if (S == 0 || Tq == 0) return PKV_OK;
   *empty = false;

@@ -7,12 +7,13 @@
 // chunk itself, already written by reshape_and_cache).
 //
 // Kernels:
-//  * prefill_tile_kernel -- 16-bit or FP8 pools with blocks of >= 16 tokens:
+//  * prefill_tile_kernel -- 16-bit pools with blocks of >= 4 tokens (D = 128)
+//    or >= 8 (D = 64), FP8 pools with blocks of >= 8:
 //    the software-pipelined matrix-core kernel (both products on
 //    v_mfma_f32_16x16x32, K/V staged through LDS); described above it.
 //  * prefill_merge_kernel -- combines the partial results of launches whose
 //    KV ranges were split (plan_prefill: few sequences, long contexts).
-//  * prefill_mfma_kernel -- 16-bit pools with blocks of fewer than 16 tokens
+//  * prefill_mfma_kernel -- 16-bit pools with smaller blocks
 //    (32x32x16 matrix-core kernel, K read straight from the pool).
 //  * prefill_f32_kernel -- fp32 pools, a plain vector-ALU kernel.
 // Positions past a row's causal limit, rows past the chunk and tokens past
@@ -102,8 +103,8 @@ struct BoolTag {
 
 __device__ __forceinline__ u32x4_t as_v(uint4 x) { return u32x4_t{x.x, x.y, x.z, x.w}; }
 
-// Blocks of fewer than 16 tokens (16-bit KV): v_mfma_f32_32x32x16_{bf16,f16},
-// fp32 accumulation.
+// Blocks too small for the tile kernel (16-bit KV: B < 4, or B < 8 with
+// D = 64): v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation.
 //  * Workgroup = 4 waves = 128 query rows of one (sequence, KV head): the rows
 //    are (token, query head of the group) pairs, so the G heads that share a KV
 //    head share every K/V tile (GQA reuse).  Each wave owns 32 rows.
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
 }
 
 // ---------------------------------------------------------------------------
-// Tile kernel (16-bit KV, block size >= 16): both products on the 16x16x32
+// Tile kernel (16-bit or FP8 KV, blocks of >= 4 or 8 tokens): both products on the 16x16x32
 // matrix cores with the query row in lane % 16 throughout.
 //
 //  * Workgroup = 4 waves x 2 x 16 query rows of one (sequence, KV head); a row
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   static_assert(CBP == 16 || CBP == 8, "staging chunk");
   constexpr int RW = kWaves * 16 * QB;        // query rows per workgroup
   constexpr bool PSPLIT = true;  // hi + lo parts of P for both 16-bit dtypes
-  static_assert(NCH >= 1 && kTileKV * CPR % kThreads == 0, "staging split");
+  static_assert(NCH >= 1 && NCH <= 2 && kTileKV * CPR % kThreads == 0, "staging split");
   static_assert(16 % (64 / CPR) == 0, "a wave's staged rows must lie in one 16-token half");
 
   __shared__ __attribute__((aligned(16))) char lk[2][kTileKV * KP];
@@ -574,27 +575,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int32_t* tbv = a.block_tables + (int64_t)s * a.max_nb;
 
   // Staging: chunk i of a thread is column ch % CPR of tile row ch / CPR
-  // (ch = tid + 256 i): CBP pool bytes, CBL bytes in LDS.  The rows a wave stages for one chunk lie in
-  // one 16-token half of the tile, and a half lies in one block (B >= 16), so
-  // a chunk's pool address is a per-wave base plus a per-lane offset.
-  int crow[NCH], ccol[NCH], chalf[NCH];
+  // (ch = tid + 256 i): CBP pool bytes, CBL bytes in LDS.  The rows a wave
+  // stages for one chunk are 64 / CPR consecutive rows, aligned, so they lie
+  // in one block whenever B >= 64 / CPR (the host launches this kernel only
+  // then): a chunk's pool address is a per-wave block base plus a per-lane
+  // offset.  Tiles start at multiples of 32 >= B, so a row's place in its
+  // block is its tile row & (B - 1).
+  const int log2E = log2B < 4 ? log2B : 4;  // tokens per table entry read: min(B, 16)
+  int crow[NCH], ccol[NCH], csel[NCH];
   uint32_t loff[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int ch = tid + kThreads * i;
     crow[i] = ch / CPR;
     ccol[i] = ch - crow[i] * CPR;
-    chalf[i] = __builtin_amdgcn_readfirstlane(crow[i] >> 4);
-    loff[i] = (uint32_t)((crow[i] & 15) * rs32 + ccol[i] * CBP);
+    csel[i] = __builtin_amdgcn_readfirstlane(crow[i] >> log2E);  // entry of this wave's rows
+    loff[i] = (uint32_t)((crow[i] & bmask) * rs32 + ccol[i] * CBP);
   }
-  // Block table entries of tile t: lane 0 the block of its first 16 tokens,
-  // lane 1 of the next 16 (clamped to the last visible token, so the table is
-  // never read past the sequence's blocks).
+  // Block table entries of tile t: lane k the block of tokens 32 t + k min(B,
+  // 16) on (32 / min(B, 16) lanes; clamped to the last visible token, so the
+  // table is never read past the sequence's blocks, and a run of rows past
+  // the context finds the block of the row it is clamped to).
   auto ent_load = [&](int t) __attribute__((always_inline)) -> int {
-    const int kv = min(t * kTileKV + 16 * (lane & 1), kv_end - 1);
+    const int kv = min(t * kTileKV + ((lane << log2E) & (kTileKV - 1)), kv_end - 1);
     return tbv[kv >> log2B];
   };
-  // global -> registers: the chunks of tile t (entries e0, e1 of its halves).
+  // the entries of tile t's two chunk sets (chunk 0, chunk NCH - 1)
+  auto ent_pick = [&](int env, int& e0, int& e1) __attribute__((always_inline)) {
+    e0 = __builtin_amdgcn_readlane(env, csel[0]);
+    e1 = __builtin_amdgcn_readlane(env, csel[NCH - 1]);
+  };
+  // global -> registers: the chunks of tile t (entry e0 for chunk 0, e1 for
+  // chunk 1).
   // Rows past the visible range (last tile only) repeat its last row.  The
   // block base is an unsigned 32 x 32 -> 64-bit product: entries reached here
   // are physical block ids (>= 0) and a block is under 2 GiB (checked on the
@@ -608,17 +620,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (kv0 + kTileKV <= kv_end) {
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        const int h = chalf[i];
-        const char* base = pool + (uint64_t)(uint32_t)(h ? e1 : e0) * (uint32_t)blk_stride +
-                           (uint32_t)(((kv0 + 16 * h) & bmask) * rs32);
+        const char* base = pool + (uint64_t)(uint32_t)(i ? e1 : e0) * (uint32_t)blk_stride;
         dst[i] = ldc(base + loff[i]);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        const int h = chalf[i];
         const int kvc = min(kv0 + crow[i], kv_end - 1);
-        const char* base = pool + (uint64_t)(uint32_t)(h ? e1 : e0) * (uint32_t)blk_stride;
+        const char* base = pool + (uint64_t)(uint32_t)(i ? e1 : e0) * (uint32_t)blk_stride;
         dst[i] = ldc(base + (uint32_t)((kvc & bmask) * rs32 + ccol[i] * CBP));
       }
     }
@@ -676,10 +685,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int en0 = ent_load(t0);
     const int en1 = ent_load(min(t0 + 1, tl));
     ent = ent_load(min(t0 + 2, tl));
-    ea0 = __builtin_amdgcn_readlane(en0, 0);
-    ea1 = __builtin_amdgcn_readlane(en0, 1);
-    eb0 = __builtin_amdgcn_readlane(en1, 0);
-    eb1 = __builtin_amdgcn_readlane(en1, 1);
+    ent_pick(en0, ea0, ea1);
+    ent_pick(en1, eb0, eb1);
   }
   gload(sk, kpool, t0, ea0, ea1);
   lstore(lk[t0 & 1], KP, sk);
@@ -701,8 +708,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if constexpr (LD) {
       lstore(lk[j & 1], KP, sk);
       lstore(lv[j & 1], VP, sv);
-      const int ec0 = __builtin_amdgcn_readlane(ent, 0);
-      const int ec1 = __builtin_amdgcn_readlane(ent, 1);
+      int ec0, ec1;
+      ent_pick(ent, ec0, ec1);
       ent = ent_load(min(j + 4, tl));
       gload(sk, kpool, min(j + 3, tl), ec0, ec1);
       gload(sv, vpool, min(j + 1, tl), ea0, ea1);
@@ -1060,10 +1067,20 @@ pkv_status launch_tile(const PrefillArgs& a, hipStream_t stream) {
   return check_launch("paged_attention_prefill (merge)");
 }
 
+// Whether the tile kernel can stage blocks of B tokens: a wave stages 64 / CPR
+// consecutive rows per chunk (CPR = 16-byte chunks per staged row: 16 for
+// 16-bit D = 128, 8 for D = 64 and for FP8 codes) and they must lie in one
+// block.  So B >= 4 for 16-bit D = 128, B >= 8 otherwise (B <= 32 always).
+bool tile_block_ok(int B, int D, bool fp8) {
+  const int cpr = fp8 ? 8 : D * 2 / 16;
+  return B >= 64 / cpr;
+}
+
 template <int DT, int D>
 pkv_status launch_mfma(const PrefillArgs& a, hipStream_t stream) {
   // blocks of at least 16 tokens and groups that fit a workgroup: tile kernel
-  if (a.B >= 16 && a.Hq / a.Hkv <= kWaves * 16 * kTileQB) return launch_tile<DT, D, false>(a, stream);
+  if (tile_block_ok(a.B, D, false) && a.Hq / a.Hkv <= kWaves * 16 * kTileQB)
+    return launch_tile<DT, D, false>(a, stream);
   const int G = a.Hq / a.Hkv;
   if (G > kRowsPerWG) return fail(PKV_ERR_UNSUPPORTED, "prefill: group size %d > %d", G, kRowsPerWG);
   const int TQ = kRowsPerWG / G;
@@ -1100,7 +1117,8 @@ PrefillPlan plan_prefill(int kv_dt, int32_t S, int32_t Tq, int32_t max_query_len
   constexpr int kMinSplitTiles = 8;
   PrefillPlan p{1, 0, 0};
   const int G = Hkv > 0 ? Hq / Hkv : 0;
-  const bool tile = kv_dt != DT_F32 && B >= 16 && G >= 1 && G <= kWaves * 16 * kTileQB;
+  const bool tile = kv_dt != DT_F32 && tile_block_ok(B, D, kv_dt == DT_FP8) && G >= 1 &&
+                    G <= kWaves * 16 * kTileQB;
   if (!tile || S <= 0 || Tq <= 0 || max_query_len <= 0 || max_ctx <= 0) return p;
   const int TQ = kWaves * 16 * kTileQB / G;
   const int64_t grid0 = (int64_t)((max_query_len + TQ - 1) / TQ) * S * Hkv;
@@ -1120,9 +1138,9 @@ PrefillPlan plan_prefill(int kv_dt, int32_t S, int32_t Tq, int32_t max_query_len
 
 pkv_status launch_prefill(int kv_dt, const PrefillArgs& a, hipStream_t stream) {
   if (kv_dt == DT_FP8) {
-    // FP8 pools: the tile kernel only (blocks of >= 16 tokens, groups that fit
+    // FP8 pools: the tile kernel only (blocks of >= 8 tokens, groups that fit
     // a workgroup), q in f16 or bf16
-    if (a.B < 16 || a.Hq / a.Hkv > kWaves * 16 * kTileQB)
+    if (!tile_block_ok(a.B, a.D, true) || a.Hq / a.Hkv > kWaves * 16 * kTileQB)
       return fail(PKV_ERR_UNSUPPORTED, "prefill_fp8: block_size %d / group %d", a.B, a.Hq / a.Hkv);
     if (a.q_dt == DT_BF16 && a.D == 128) return launch_tile<DT_BF16, 128, true>(a, stream);
     if (a.q_dt == DT_BF16 && a.D == 64) return launch_tile<DT_BF16, 64, true>(a, stream);

@@ -299,10 +299,18 @@ def test_prefill_fp8_one_token_chunks_match_fp8_decode(gpu_lib):
 
 
 def test_prefill_fp8_rejects_small_blocks(gpu_lib):
-    b = W.varlen_prefill(13, [20], [8], 8, 2, 128, 8, "bf16")
+    b = W.varlen_prefill(13, [20], [8], 8, 2, 128, 4, "bf16")
     d = Fp8Dev(b, W.fp8_pools(b, 0))
     with pytest.raises(gpu_lib.PkvError, match="block_size"):
         gpu_prefill_fp8(gpu_lib, d)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64)])
+def test_prefill_fp8_blocks_of_8(gpu_lib, dtype, D):
+    """Blocks of 8 tokens: a wave's 8 staged rows per chunk fill one block, the
+    tile's four entries are read per chunk; long contexts split the range."""
+    b = W.varlen_prefill(17 + D, [0, 9, 300, 2500], [13, 40, 77, 100], 16, 4, D, 8, dtype)
+    check_prefill(gpu_lib, b, seed=D)
 
 
 def test_prefill_fp8_full_size_sampled(gpu_lib):

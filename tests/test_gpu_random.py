@@ -147,7 +147,7 @@ def test_random_decode_fp8(gpu_lib, case):
 def test_random_prefill_fp8(gpu_lib, case):
     rng = np.random.default_rng(9000 + case)
     Hq, Hkv, D = _heads(rng)
-    B = int(rng.choice([16, 32]))
+    B = int(rng.choice([8, 16, 32]))
     q_dtype = str(rng.choice(["f16", "bf16"]))
     S = int(rng.integers(1, 6))
     prior, chunks = _prefill_layout(rng, S, Hq, D, 300, 6000)
