@@ -208,7 +208,7 @@ def test_random_cascade_fp8(gpu_lib, case):
 def test_random_mixed_fp8(gpu_lib, case):
     rng = np.random.default_rng(15000 + case)
     Hq, Hkv, D = _heads(rng)
-    B = int(rng.choice([16, 32]))
+    B = int(rng.choice([8, 16, 32]))
     q_dtype = str(rng.choice(["f16", "bf16"]))
     nd = int(rng.integers(0, 8))
     dl = rng.integers(1, 2000, nd)
