@@ -38,7 +38,7 @@
 //    one tile (vmcnt) instead of draining the queue.
 //  * Each K/V load serves all GC query heads of the group (GQA reuse in
 //    registers).  Matrix-core path (16-bit q, D = 128, groups of 4, 8 or 16
-//    query heads, B >= 16; the Llama-3-8B batch): q . k on
+//    query heads, B >= 8; the Llama-3-8B batch): q . k on
 //    v_mfma_f32_16x16x32 with the row's query heads as the 16 columns, P . V
 //    on v_mfma_f32_16x16x16 over V staged per wave in LDS and read transposed
 //    (ds_read_b64_tr_b16), three tiles in flight per wave.  Vector path (the
@@ -323,14 +323,15 @@ struct Cursor {
 
 // Split kernel.  UNI: every wave-load lies in one block (B >= RPW), so its
 // table entry is one scalar; otherwise each lane looks up its own row's block.
-// MF (16-bit KV, D = 128, a GQA group of 4 query heads, B >= 16): q . k runs on
+// MF (16-bit KV, D = 128, a GQA group of 4 query heads, B >= 16, or 8 with two blocks per tile): q . k runs on
 // the matrix cores; everything else as in the vector path (see below).
 // F8: the pools hold E4M3 codes (DT is then the dtype of q and of the widened
 // elements); the lane layout is DT's, with 8-byte instead of 16-byte loads.
 // The two-waves-per-SIMD bound keeps the matrix-core results in ordinary
 // VGPRs (no accumulation registers, hence no copies out of them before the
 // softmax): FP8 decode 176 -> 173 us on the Llama-3-8B batch, bf16 unchanged.
-template <int DT, int D, int GC, bool UNI, bool MF, bool F8>
+// B8: matrix-core path over blocks of 8 tokens (a 16-token tile spans two)
+template <int DT, int D, int GC, bool UNI, bool MF, bool F8, bool B8 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(
     const DecodeArgs a) {
   using Gm = Geo<DT, D>;
@@ -343,6 +344,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   static_assert(!MF || (DT != DT_F32 && D == 128 && (GC == 4 || GC == 8 || GC == 16) && UNI &&
                         TILE == 16),
                 "matrix-core path: 16-bit q, D = 128, 4, 8 or 16 query heads, one block per tile");
+  static_assert(!B8 || MF, "two blocks per tile on the matrix-core path only");
   constexpr int QN = MF ? D / 32 : GC;  // q registers: k-steps of 32 (MF) or heads
   // tiles in flight per wave: three where the registers allow it
   constexpr int NBUF = (MF || GC <= 2) ? 3 : 2;
@@ -495,6 +497,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       r.e[0] = tb[(c.st + c.j * TILE) >> log2B];
 #pragma unroll
       for (int i = 1; i < NLD; ++i) r.e[i] = r.e[0];
+      // blocks of 8: the block of the tile's second 8 tokens (clamped to the
+      // last token, so a clamped row finds the block that holds it)
+      if constexpr (B8) r.e[1] = tb[min(c.st + c.j * TILE + 8, c.L - 1) >> log2B];
     } else if constexpr (UNI) {
       const cint32_t* tb = (const cint32_t*)(a.block_tables + (int64_t)c.s * a.max_nb);
       const int ts = c.st + c.j * TILE;
@@ -523,6 +528,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       // wave-uniform; unsigned 32 x 32 -> 64 bits: block ids are >= 0 and a
       // block is under 2 GiB (checked on the host)
       const uint64_t base = (uint64_t)(uint32_t)en.e[0] * (uint32_t)blk_stride;
+      // blocks of 8 tokens: a load's token t (already clamped) lies in e[0]'s
+      // block if t - ts < 8, else in e[1]'s -- a per-lane choice of base
+      [[maybe_unused]] const uint64_t base1 = (uint64_t)(uint32_t)en.e[1] * (uint32_t)blk_stride;
+      auto bsel = [&](int t) __attribute__((always_inline)) -> uint64_t {
+        if constexpr (B8) return t - ts >= 8 ? base1 : base;
+        else return base;
+      };
       const int kvoff = c.kvh * D * KS;
       const int tk = min(ts + col, c.L - 1);
       if constexpr (F8) {
@@ -532,16 +544,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         // Each load instruction then reads half of every token's 128-byte
         // line instead of a quarter: half the cache-line requests.
         const unsigned koff = (unsigned)((tk & bmask) * row_stride32 + kvoff + row * 32);
-        const uint4 k0 = ld16_stream(kpool + base + koff);
-        const uint4 k1 = ld16_stream(kpool + base + koff + 16);
+        const uint64_t kbase = bsel(tk);
+        const uint4 k0 = ld16_stream(kpool + kbase + koff);
+        const uint4 k1 = ld16_stream(kpool + kbase + koff + 16);
         kb[0] = make_uint2(k0.x, k0.y);
         kb[1] = make_uint2(k0.z, k0.w);
         kb[2] = make_uint2(k1.x, k1.y);
         kb[3] = make_uint2(k1.z, k1.w);
       } else {
         const unsigned koff = (unsigned)((tk & bmask) * row_stride32 + kvoff + row * LB);
+        const uint64_t kbase = bsel(tk);
 #pragma unroll
-        for (int kk = 0; kk < NLD; ++kk) kb[kk] = ldkv(kpool + base + koff + kk * 4 * LB);
+        for (int kk = 0; kk < NLD; ++kk) kb[kk] = ldkv(kpool + kbase + koff + kk * 4 * LB);
       }
       if constexpr (F8) {
         // FP8 V goes through LDS, so its load layout is free: two 16-byte
@@ -551,7 +565,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int jv = 0; jv < 2; ++jv) {
           const int tv = min(ts + 8 * jv + 2 * row + (col >> 3), c.L - 1);
           const unsigned voff = (unsigned)((tv & bmask) * row_stride32 + kvoff + (col & 7) * 16);
-          const uint4 v4 = ld16_stream(vpool + base + voff);
+          const uint4 v4 = ld16_stream(vpool + bsel(tv) + voff);
           vb[2 * jv] = make_uint2(v4.x, v4.y);
           vb[2 * jv + 1] = make_uint2(v4.z, v4.w);
         }
@@ -560,7 +574,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int i = 0; i < NLD; ++i) {
           const int tv = min(ts + 4 * row + i, c.L - 1);
           const unsigned voff = (unsigned)((tv & bmask) * row_stride32 + kvoff + col * LB);
-          vb[i] = ldkv(vpool + base + voff);
+          vb[i] = ldkv(vpool + bsel(tv) + voff);
         }
       }
     } else if constexpr (UNI) {
@@ -1078,14 +1092,14 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
 
 // (the caches below may be filled by several host threads at once: atomics,
 // every writer stores the same value)
-template <int DT, int D, int GC, bool UNI, bool MF, bool F8>
+template <int DT, int D, int GC, bool UNI, bool MF, bool F8, bool B8 = false>
 int occupancy_of() {
   static std::atomic<int> occ{-1};
   int o = occ.load(std::memory_order_relaxed);
   if (o < 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(&decode_split_kernel<DT, D, GC, UNI, MF, F8>), kThreads,
+            &n, reinterpret_cast<const void*>(&decode_split_kernel<DT, D, GC, UNI, MF, F8, B8>), kThreads,
             0) != hipSuccess ||
         n < 1)
       n = 1;
@@ -1097,18 +1111,18 @@ int occupancy_of() {
 
 // Split launch (one resident wave set: CUs x occupancy, capped by grid_cap)
 // followed by the merge launch.
-template <int DT, int D, int GC, bool UNI, bool MF, bool F8>
+template <int DT, int D, int GC, bool UNI, bool MF, bool F8, bool B8 = false>
 pkv_status launch_split(DecodeArgs a, int grid_cap, int ncu, hipStream_t stream) {
   // Matrix-core path: one workgroup (one wave per SIMD, three tiles in
   // flight each) per CU measured fastest for 16-bit pools -- 3-7% ahead of
   // two per CU on the Llama-3-8B batch; FP8 pools (half the bytes per tile)
   // need two per CU to keep enough bytes in flight (about 190 -> 181 us on the
   // same batch).  Vector path: every resident workgroup.
-  int64_t grid = (int64_t)ncu * (MF ? (F8 ? 2 : 1) : occupancy_of<DT, D, GC, UNI, MF, F8>());
+  int64_t grid = (int64_t)ncu * (MF ? (F8 ? 2 : 1) : occupancy_of<DT, D, GC, UNI, MF, F8, B8>());
   if (grid > grid_cap) grid = grid_cap;
   if (grid < 1) grid = 1;
   a.n_waves = (int)grid * kWaves;
-  hipLaunchKernelGGL((decode_split_kernel<DT, D, GC, UNI, MF, F8>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((decode_split_kernel<DT, D, GC, UNI, MF, F8, B8>), dim3((unsigned)grid),
                      dim3(kThreads), 0, stream, a);
   pkv_status st = check_launch("paged_attention_decode (split)");
   if (st != PKV_OK) return st;
@@ -1122,9 +1136,11 @@ pkv_status launch_split(DecodeArgs a, int grid_cap, int ncu, hipStream_t stream)
 
 template <int DT, int D, int GC, bool F8>
 pkv_status launch_typed(const DecodeArgs& a, int grid_cap, int ncu, bool uni, hipStream_t stream) {
-  // matrix cores: 16-bit q, D = 128, 4, 8 or 16 query heads per row, a tile in one block
+  // matrix cores: 16-bit q, D = 128, 4, 8 or 16 query heads per row, a tile in
+  // one block (B >= 16) or two (B = 8)
   if constexpr (DT != DT_F32 && D == 128 && (GC == 4 || GC == 8 || GC == 16)) {
     if (a.B >= 16) return launch_split<DT, D, GC, true, true, F8>(a, grid_cap, ncu, stream);
+    if (a.B == 8) return launch_split<DT, D, GC, true, true, F8, true>(a, grid_cap, ncu, stream);
   }
   if constexpr (GC == 16) {  // chunks of 16 heads exist on the matrix-core path only
     return fail(PKV_ERR_UNSUPPORTED, "decode: 16-head rows need the matrix-core path");
@@ -1243,7 +1259,7 @@ void attach_decode_workspace(DecodeArgs* a, const DecodePlan& plan, void* worksp
 pkv_status launch_decode(int kv_dt, bool fp8, const DecodePlan& plan, DecodeArgs a,
                          hipStream_t stream) {
   // (kv_dt: the dtype of q; the lane layout follows it, also over FP8 pools)
-  const bool mf = kv_dt != DT_F32 && a.D == 128 && a.B >= 16 && plan.gc_mf > 0;
+  const bool mf = kv_dt != DT_F32 && a.D == 128 && (a.B >= 16 || a.B == 8) && plan.gc_mf > 0;
   a.gc = mf ? plan.gc_mf : plan.gc_vec;
   a.n_hchunks = (a.Hq / a.Hkv) / a.gc;
   a.rows_per_seq = a.Hkv * a.n_hchunks;
