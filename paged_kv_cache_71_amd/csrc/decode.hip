@@ -38,7 +38,7 @@
 //    one tile (vmcnt) instead of draining the queue.
 //  * Each K/V load serves all GC query heads of the group (GQA reuse in
 //    registers).  Matrix-core path (16-bit q, D = 128, groups of 4, 8 or 16
-//    query heads, B >= 8; the Llama-3-8B batch): q . k on
+//    query heads, B >= 4; the Llama-3-8B batch): q . k on
 //    v_mfma_f32_16x16x32 with the row's query heads as the 16 columns, P . V
 //    on v_mfma_f32_16x16x16 over V staged per wave in LDS and read transposed
 //    (ds_read_b64_tr_b16), three tiles in flight per wave.  Vector path (the
@@ -323,15 +323,17 @@ struct Cursor {
 
 // Split kernel.  UNI: every wave-load lies in one block (B >= RPW), so its
 // table entry is one scalar; otherwise each lane looks up its own row's block.
-// MF (16-bit KV, D = 128, a GQA group of 4 query heads, B >= 16, or 8 with two blocks per tile): q . k runs on
+// MF (16-bit KV, D = 128, a GQA group of 4 query heads, B >= 16, or 8 or 4 with
+// two or four blocks per tile): q . k runs on
 // the matrix cores; everything else as in the vector path (see below).
 // F8: the pools hold E4M3 codes (DT is then the dtype of q and of the widened
 // elements); the lane layout is DT's, with 8-byte instead of 16-byte loads.
 // The two-waves-per-SIMD bound keeps the matrix-core results in ordinary
 // VGPRs (no accumulation registers, hence no copies out of them before the
 // softmax): FP8 decode 176 -> 173 us on the Llama-3-8B batch, bf16 unchanged.
-// B8: matrix-core path over blocks of 8 tokens (a 16-token tile spans two)
-template <int DT, int D, int GC, bool UNI, bool MF, bool F8, bool B8 = false>
+// BPT: blocks per 16-token tile on the matrix-core path (1 for B >= 16, 2 for
+// B = 8, 4 for B = 4)
+template <int DT, int D, int GC, bool UNI, bool MF, bool F8, int BPT = 1>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(
     const DecodeArgs a) {
   using Gm = Geo<DT, D>;
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   static_assert(!MF || (DT != DT_F32 && D == 128 && (GC == 4 || GC == 8 || GC == 16) && UNI &&
                         TILE == 16),
                 "matrix-core path: 16-bit q, D = 128, 4, 8 or 16 query heads, one block per tile");
-  static_assert(!B8 || MF, "two blocks per tile on the matrix-core path only");
+  static_assert(BPT == 1 || (MF && (BPT == 2 || BPT == 4)), "several blocks per tile: matrix-core path");
   constexpr int QN = MF ? D / 32 : GC;  // q registers: k-steps of 32 (MF) or heads
   // tiles in flight per wave: three where the registers allow it
   constexpr int NBUF = (MF || GC <= 2) ? 3 : 2;
@@ -497,9 +499,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       r.e[0] = tb[(c.st + c.j * TILE) >> log2B];
 #pragma unroll
       for (int i = 1; i < NLD; ++i) r.e[i] = r.e[0];
-      // blocks of 8: the block of the tile's second 8 tokens (clamped to the
-      // last token, so a clamped row finds the block that holds it)
-      if constexpr (B8) r.e[1] = tb[min(c.st + c.j * TILE + 8, c.L - 1) >> log2B];
+      // blocks of 8 or 4: the blocks of the tile's later 8- or 4-token parts
+      // (clamped to the last token, so a clamped row finds the block holding it)
+#pragma unroll
+      for (int k = 1; k < BPT; ++k) r.e[k] = tb[min(c.st + c.j * TILE + k * (TILE / BPT), c.L - 1) >> log2B];
     } else if constexpr (UNI) {
       const cint32_t* tb = (const cint32_t*)(a.block_tables + (int64_t)c.s * a.max_nb);
       const int ts = c.st + c.j * TILE;
@@ -528,12 +531,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       // wave-uniform; unsigned 32 x 32 -> 64 bits: block ids are >= 0 and a
       // block is under 2 GiB (checked on the host)
       const uint64_t base = (uint64_t)(uint32_t)en.e[0] * (uint32_t)blk_stride;
-      // blocks of 8 tokens: a load's token t (already clamped) lies in e[0]'s
-      // block if t - ts < 8, else in e[1]'s -- a per-lane choice of base
+      // blocks of 8 or 4 tokens: a load's token t (already clamped) lies in
+      // the block of entry (t - ts) >> log2 B -- a per-lane choice of base
       [[maybe_unused]] const uint64_t base1 = (uint64_t)(uint32_t)en.e[1] * (uint32_t)blk_stride;
+      [[maybe_unused]] const uint64_t base2 = (uint64_t)(uint32_t)en.e[2] * (uint32_t)blk_stride;
+      [[maybe_unused]] const uint64_t base3 = (uint64_t)(uint32_t)en.e[3] * (uint32_t)blk_stride;
       auto bsel = [&](int t) __attribute__((always_inline)) -> uint64_t {
-        if constexpr (B8) return t - ts >= 8 ? base1 : base;
-        else return base;
+        if constexpr (BPT == 2) {
+          return t - ts >= 8 ? base1 : base;
+        } else if constexpr (BPT == 4) {
+          // two bit tests, so the choice stays in registers (selects)
+          const int k = (t - ts) >> 2;
+          const uint64_t lo = (k & 1) ? base1 : base;
+          const uint64_t hi = (k & 1) ? base3 : base2;
+          return (k & 2) ? hi : lo;
+        } else {
+          return base;
+        }
       };
       const int kvoff = c.kvh * D * KS;
       const int tk = min(ts + col, c.L - 1);
@@ -1092,14 +1106,14 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
 
 // (the caches below may be filled by several host threads at once: atomics,
 // every writer stores the same value)
-template <int DT, int D, int GC, bool UNI, bool MF, bool F8, bool B8 = false>
+template <int DT, int D, int GC, bool UNI, bool MF, bool F8, int BPT = 1>
 int occupancy_of() {
   static std::atomic<int> occ{-1};
   int o = occ.load(std::memory_order_relaxed);
   if (o < 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(&decode_split_kernel<DT, D, GC, UNI, MF, F8, B8>), kThreads,
+            &n, reinterpret_cast<const void*>(&decode_split_kernel<DT, D, GC, UNI, MF, F8, BPT>), kThreads,
             0) != hipSuccess ||
         n < 1)
       n = 1;
@@ -1111,18 +1125,18 @@ int occupancy_of() {
 
 // Split launch (one resident wave set: CUs x occupancy, capped by grid_cap)
 // followed by the merge launch.
-template <int DT, int D, int GC, bool UNI, bool MF, bool F8, bool B8 = false>
+template <int DT, int D, int GC, bool UNI, bool MF, bool F8, int BPT = 1>
 pkv_status launch_split(DecodeArgs a, int grid_cap, int ncu, hipStream_t stream) {
   // Matrix-core path: one workgroup (one wave per SIMD, three tiles in
   // flight each) per CU measured fastest for 16-bit pools -- 3-7% ahead of
   // two per CU on the Llama-3-8B batch; FP8 pools (half the bytes per tile)
   // need two per CU to keep enough bytes in flight (about 190 -> 181 us on the
   // same batch).  Vector path: every resident workgroup.
-  int64_t grid = (int64_t)ncu * (MF ? (F8 ? 2 : 1) : occupancy_of<DT, D, GC, UNI, MF, F8, B8>());
+  int64_t grid = (int64_t)ncu * (MF ? (F8 ? 2 : 1) : occupancy_of<DT, D, GC, UNI, MF, F8, BPT>());
   if (grid > grid_cap) grid = grid_cap;
   if (grid < 1) grid = 1;
   a.n_waves = (int)grid * kWaves;
-  hipLaunchKernelGGL((decode_split_kernel<DT, D, GC, UNI, MF, F8, B8>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((decode_split_kernel<DT, D, GC, UNI, MF, F8, BPT>), dim3((unsigned)grid),
                      dim3(kThreads), 0, stream, a);
   pkv_status st = check_launch("paged_attention_decode (split)");
   if (st != PKV_OK) return st;
@@ -1137,10 +1151,11 @@ pkv_status launch_split(DecodeArgs a, int grid_cap, int ncu, hipStream_t stream)
 template <int DT, int D, int GC, bool F8>
 pkv_status launch_typed(const DecodeArgs& a, int grid_cap, int ncu, bool uni, hipStream_t stream) {
   // matrix cores: 16-bit q, D = 128, 4, 8 or 16 query heads per row, a tile in
-  // one block (B >= 16) or two (B = 8)
+  // one block (B >= 16), two (B = 8) or four (B = 4)
   if constexpr (DT != DT_F32 && D == 128 && (GC == 4 || GC == 8 || GC == 16)) {
     if (a.B >= 16) return launch_split<DT, D, GC, true, true, F8>(a, grid_cap, ncu, stream);
-    if (a.B == 8) return launch_split<DT, D, GC, true, true, F8, true>(a, grid_cap, ncu, stream);
+    if (a.B == 8) return launch_split<DT, D, GC, true, true, F8, 2>(a, grid_cap, ncu, stream);
+    if (a.B == 4) return launch_split<DT, D, GC, true, true, F8, 4>(a, grid_cap, ncu, stream);
   }
   if constexpr (GC == 16) {  // chunks of 16 heads exist on the matrix-core path only
     return fail(PKV_ERR_UNSUPPORTED, "decode: 16-head rows need the matrix-core path");
@@ -1259,7 +1274,7 @@ void attach_decode_workspace(DecodeArgs* a, const DecodePlan& plan, void* worksp
 pkv_status launch_decode(int kv_dt, bool fp8, const DecodePlan& plan, DecodeArgs a,
                          hipStream_t stream) {
   // (kv_dt: the dtype of q; the lane layout follows it, also over FP8 pools)
-  const bool mf = kv_dt != DT_F32 && a.D == 128 && (a.B >= 16 || a.B == 8) && plan.gc_mf > 0;
+  const bool mf = kv_dt != DT_F32 && a.D == 128 && a.B >= 4 && plan.gc_mf > 0;
   a.gc = mf ? plan.gc_mf : plan.gc_vec;
   a.n_hchunks = (a.Hq / a.Hkv) / a.gc;
   a.rows_per_seq = a.Hkv * a.n_hchunks;
