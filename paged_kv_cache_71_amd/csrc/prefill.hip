@@ -7,8 +7,8 @@
 // chunk itself, already written by reshape_and_cache).
 //
 // Kernels:
-//  * prefill_tile_kernel -- 16-bit pools with blocks of >= 4 tokens (D = 128)
-//    or >= 8 (D = 64), FP8 pools with blocks of >= 8:
+//  * prefill_tile_kernel -- 16-bit pools with blocks of >= 4 tokens, FP8
+//    pools with blocks of >= 8:
 //    the software-pipelined matrix-core kernel (both products on
 //    v_mfma_f32_16x16x32, K/V staged through LDS); described above it.
 //  * prefill_merge_kernel -- combines the partial results of launches whose
@@ -103,8 +103,8 @@ struct BoolTag {
 
 __device__ __forceinline__ u32x4_t as_v(uint4 x) { return u32x4_t{x.x, x.y, x.z, x.w}; }
 
-// Blocks too small for the tile kernel (16-bit KV: B < 4, or B < 8 with
-// D = 64): v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation.
+// Blocks too small for the tile kernel (16-bit KV, B < 4):
+// v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation.
 //  * Workgroup = 4 waves = 128 query rows of one (sequence, KV head): the rows
 //    are (token, query head of the group) pairs, so the G heads that share a KV
 //    head share every K/V tile (GQA reuse).  Each wave owns 32 rows.
@@ -454,7 +454,9 @@ __device__ __forceinline__ float group_max_raw(float x) {
 // F8: the pools hold OCP E4M3 codes (one scale per KV head); they are widened
 // to DT (q's dtype, exact) as they go into LDS, so everything after the
 // staging is the 16-bit kernel.
-template <int DT, int D, bool F8>
+// NARROW (16-bit D = 64 over blocks of 4 tokens): 8-byte staging chunks, so a
+// wave stages 4 rows per chunk and they lie in one block
+template <int DT, int D, bool F8, bool NARROW = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_tile_kernel(
     const PrefillArgs a) {
   constexpr int QB = kTileQB;
@@ -467,7 +469,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // costs the K reads 1.6x)
   constexpr int KP = D * ES + 32;
   constexpr int VP = D * ES + 32;
-  constexpr int CPR = F8 ? 8 : D * ES / 16;      // staging chunks per row
+  static_assert(!NARROW || (!F8 && D == 64), "8-byte chunks: 16-bit D = 64 only");
+  constexpr int CPR = F8 ? 8 : D * ES / (NARROW ? 8 : 16);  // staging chunks per row
   constexpr int CBP = D * ESK / CPR;             // pool bytes per chunk (16, or 8 for FP8 D = 64)
   constexpr int CBL = D * ES / CPR;              // LDS bytes per chunk (16 or 32)
   constexpr int NCH = kTileKV * CPR / kThreads;  // chunks per thread per tile, K and V each
@@ -636,7 +639,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       char* dst = buf + crow[i] * pitch + ccol[i] * CBL;
-      if constexpr (!F8) {
+      if constexpr (!F8 && CBP == 8) {
+        *reinterpret_cast<uint2*>(dst) = src[i];
+      } else if constexpr (!F8) {
         *reinterpret_cast<uint4*>(dst) = src[i];
       } else if constexpr (CBP == 16) {
         *reinterpret_cast<uint4*>(dst) = fp8x8_to16<DT>(make_uint2(src[i].x, src[i].y));
@@ -1048,7 +1053,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillArgs a) {
   }
 }
 
-template <int DT, int D, bool F8>
+template <int DT, int D, bool F8, bool NARROW = false>
 pkv_status launch_tile(const PrefillArgs& a, hipStream_t stream) {
   constexpr int RW = kWaves * 16 * kTileQB;
   const int G = a.Hq / a.Hkv;
@@ -1057,7 +1062,7 @@ pkv_status launch_tile(const PrefillArgs& a, hipStream_t stream) {
   const int64_t grid = nqt * a.S * a.Hkv * a.n_split;
   if (grid == 0) return PKV_OK;
   if (grid > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "prefill grid too large");
-  hipLaunchKernelGGL((prefill_tile_kernel<DT, D, F8>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((prefill_tile_kernel<DT, D, F8, NARROW>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, a);
   pkv_status st = check_launch("paged_attention_prefill");
   if (st != PKV_OK || a.n_split <= 1) return st;
@@ -1068,19 +1073,21 @@ pkv_status launch_tile(const PrefillArgs& a, hipStream_t stream) {
 }
 
 // Whether the tile kernel can stage blocks of B tokens: a wave stages 64 / CPR
-// consecutive rows per chunk (CPR = 16-byte chunks per staged row: 16 for
-// 16-bit D = 128, 8 for D = 64 and for FP8 codes) and they must lie in one
-// block.  So B >= 4 for 16-bit D = 128, B >= 8 otherwise (B <= 32 always).
-bool tile_block_ok(int B, int D, bool fp8) {
-  const int cpr = fp8 ? 8 : D * 2 / 16;
-  return B >= 64 / cpr;
-}
+// consecutive rows per chunk (CPR = staging chunks per row: 16 for 16-bit
+// D = 128, 8 for D = 64 and for FP8 codes, 16 of 8 bytes for the NARROW
+// 16-bit D = 64 kernel) and they must lie in one block.  So B >= 4 for 16-bit
+// pools, B >= 8 for FP8 (B <= 32 always).
+bool tile_block_ok(int B, int /*D*/, bool fp8) { return B >= (fp8 ? 8 : 4); }
 
 template <int DT, int D>
 pkv_status launch_mfma(const PrefillArgs& a, hipStream_t stream) {
   // blocks of at least 16 tokens and groups that fit a workgroup: tile kernel
-  if (tile_block_ok(a.B, D, false) && a.Hq / a.Hkv <= kWaves * 16 * kTileQB)
+  if (tile_block_ok(a.B, D, false) && a.Hq / a.Hkv <= kWaves * 16 * kTileQB) {
+    if constexpr (D == 64) {
+      if (a.B == 4) return launch_tile<DT, D, false, true>(a, stream);
+    }
     return launch_tile<DT, D, false>(a, stream);
+  }
   const int G = a.Hq / a.Hkv;
   if (G > kRowsPerWG) return fail(PKV_ERR_UNSUPPORTED, "prefill: group size %d > %d", G, kRowsPerWG);
   const int TQ = kRowsPerWG / G;

@@ -78,14 +78,15 @@ def test_prefill_split_plan_and_workspace_check(lib):
     """One long sequence cannot fill the GPU with (KV head, query tile) units:
     its KV range is split, which needs a workspace of partial results; the call
     without one fails before launching anything.  f32 pools, blocks too small
-    for the tile kernel (2 tokens; 4 with head_dim 64) and many-sequence
-    batches need none; blocks of 8 run the tile kernel and split alike."""
+    for the tile kernel (2 tokens) and many-sequence batches need none; blocks
+    of 8, and of 4 (head_dim 64: 8-byte staging), run the tile kernel and
+    split alike."""
     need = prefill_ws(lib, 1, 32, 32, 4, 1, 128, 16, 2, 8192)         # one unit, 256 tiles
     assert need > 0 and need % (32 * 4 * 130 * 4) == 0
     assert prefill_ws(lib, 1, 32, 32, 4, 1, 128, 16, 0, 8192) == 0     # f32
     assert prefill_ws(lib, 1, 32, 32, 4, 1, 128, 8, 2, 8192) == need   # block 8: tile kernel
     assert prefill_ws(lib, 1, 32, 32, 4, 1, 128, 2, 2, 8192) == 0      # block 2
-    assert prefill_ws(lib, 1, 32, 32, 4, 1, 64, 4, 2, 8192) == 0       # block 4, head_dim 64
+    assert prefill_ws(lib, 1, 32, 32, 4, 1, 64, 4, 2, 8192) > 0        # block 4, head_dim 64
     assert prefill_ws(lib, 1, 32, 32, 4, 1, 128, 16, 2, 200) == 0      # under two splits of tiles
     assert prefill_ws(lib, 4096, 4096, 1, 32, 8, 128, 16, 2, 8192) == 0  # enough units
     rc = lib.pkv_paged_attention_prefill(FAKE, 0, FAKE, FAKE, 32, 32, FAKE, FAKE, 2, FAKE, 512, FAKE,

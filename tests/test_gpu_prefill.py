@@ -167,10 +167,12 @@ def test_f32_long_context_sharp_softmax(gpu_lib):
     check(gpu_lib, b)
 
 
-@pytest.mark.parametrize("dtype,D,B", [("bf16", 128, 4), ("f16", 128, 8), ("bf16", 64, 8), ("f16", 128, 4)])
+@pytest.mark.parametrize("dtype,D,B", [("bf16", 128, 4), ("f16", 128, 8), ("bf16", 64, 8), ("f16", 128, 4),
+                                     ("bf16", 64, 4), ("f16", 64, 4)])
 def test_tile_kernel_small_blocks(gpu_lib, dtype, D, B):
-    """Blocks of 4 or 8 tokens on the tile kernel: a wave's staged rows of one
-    chunk lie in one block, the tile reads 32 / B table entries (clamped past
-    the context), and long contexts split the KV range."""
+    """Blocks of 4 or 8 tokens on the tile kernel (head_dim 64 over blocks of 4
+    with 8-byte staging chunks): a wave's staged rows of one chunk lie in one
+    block, the tile reads 32 / B table entries (clamped past the context), and
+    long contexts split the KV range."""
     b = W.varlen_prefill(29 + B + D, [0, 3, 5, 300, 3000], [1, 7, 40, 77, 130], 32, 8, D, B, dtype)
     check(gpu_lib, b)
