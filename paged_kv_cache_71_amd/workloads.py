@@ -497,6 +497,14 @@ def varlen_prefill(seed: int, prior, chunks, Hq: int, Hkv: int, D: int, B: int, 
                   chunk_lens=chunks, free_order=free_order)
 
 
+def strided_chunk_rows(cu_seqlens_q, stride: int) -> np.ndarray:
+    """Query rows of a varlen batch to compare: every ``stride``-th row of each
+    chunk from its first, plus its last."""
+    cu = np.asarray(cu_seqlens_q, np.int64)
+    rows = [np.r_[np.arange(a, b, stride), b - 1] for a, b in zip(cu[:-1], cu[1:]) if b > a]
+    return np.unique(np.concatenate(rows)) if rows else np.zeros(0, np.int64)
+
+
 def split_chunks(n_tokens: int, budget: int) -> list[int]:
     """Cut a prompt into prefill chunks of at most ``budget`` tokens, in order."""
     out = []

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+from oracle.parallel import decode_par
 from gpu_util import TOL, DevBatch, max_abs
 from paged_kv_cache_71_amd import workloads as W
 
@@ -30,8 +31,7 @@ def gpu_cascade(pkv, db: DevBatch, cu, plens, max_group_size=None, max_prefix_le
 
 def oracle_decode(b: W.PagedBatch, seqs=None):
     k, v, tables = b.compact_pool()
-    sel = np.arange(b.S) if seqs is None else np.asarray(seqs)
-    return oracle.decode(b.q[sel], k, v, b.dtype, tables[sel], b.context_lens[sel], b.scale)
+    return decode_par(b.q, k, v, b.dtype, tables, b.context_lens, b.scale, seqs=seqs)
 
 
 def check(pkv, b, seqs=None, **kw):
@@ -103,11 +103,12 @@ def test_cascade_shared_prefix_reduced(gpu_lib):
         check(gpu_lib, b)
 
 
-def test_cascade_shared_prefix_full_size_sampled(gpu_lib):
-    """The benchmarked shared-prefix batch (64 prompts x 4 samples)."""
+def test_cascade_shared_prefix_full_size(gpu_lib):
+    """The benchmarked shared-prefix batch (64 prompts x 4 samples): every
+    output element against the oracle."""
     b = W.shared_prefix_bf16(0)
     cu = np.arange(0, b.S + 1, b.meta["n"], dtype=np.int32)
     b.meta["cu_group_seqs"] = cu
     b.meta["group_prefix_lens"] = np.full(len(cu) - 1, (b.meta["prompt_len"] // b.B) * b.B,
                                           np.int32)
-    check(gpu_lib, b, seqs=list(range(0, 256, 17)))
+    check(gpu_lib, b)

@@ -4,6 +4,7 @@ import pytest
 import torch
 
 import oracle
+from oracle.parallel import decode_par
 from gpu_util import TOL, TORCH_DT, DevBatch, max_abs, to_dev, to_host_bits
 from paged_kv_cache_71_amd import workloads as W
 
@@ -21,8 +22,7 @@ def gpu_decode(pkv, db: DevBatch, out_dtype="f32", workspace=None):
 
 def oracle_decode(b: W.PagedBatch, seqs=None):
     k, v, tables = b.compact_pool()
-    sel = np.arange(b.S) if seqs is None else np.asarray(seqs)
-    return oracle.decode(b.q[sel], k, v, b.dtype, tables[sel], b.context_lens[sel], b.scale)
+    return decode_par(b.q, k, v, b.dtype, tables, b.context_lens, b.scale, seqs=seqs)
 
 
 def check(pkv, b, seqs=None, out_dtype="f32"):
@@ -191,23 +191,20 @@ def test_workspace_too_small_is_rejected(gpu_lib):
 
 
 # ---------------------------------------------------------------- full-size workloads
-def test_llama3_8b_full_size_sampled(gpu_lib):
-    """The benchmarked workload (256 sequences, 12 GB pool), sampled sequences
-    checked against the oracle: the longest, the shortest and 14 random ones."""
-    b = W.llama3_8b_bf16(0)
-    order = np.argsort(b.context_lens)
-    seqs = sorted(set([int(order[0]), int(order[-1])] +
-                      np.random.default_rng(0).choice(b.S, 14, replace=False).tolist()))
-    check(gpu_lib, b, seqs=seqs)
+def test_llama3_8b_full_size(gpu_lib):
+    """The benchmarked workload (256 sequences, 12 GB pool): every output
+    element of every sequence against the oracle."""
+    check(gpu_lib, W.llama3_8b_bf16(0))
 
 
 def test_opt13b_full_size(gpu_lib):
     check(gpu_lib, W.opt13b_f16(0))
 
 
-def test_shared_prefix_full_size_sampled(gpu_lib):
-    b = W.shared_prefix_bf16(0)
-    check(gpu_lib, b, seqs=list(range(0, 256, 17)))
+def test_shared_prefix_full_size(gpu_lib):
+    """The shared-prefix batch (64 prompts x 4 samples aliasing 125 blocks):
+    every output element against the oracle."""
+    check(gpu_lib, W.shared_prefix_bf16(0))
 
 
 def test_concurrent_host_threads(gpu_lib):

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+from oracle.parallel import decode_fp8_par, prefill_fp8_rows_par
 from gpu_util import TOL, TORCH_DT, max_abs, to_dev, validate
 from paged_kv_cache_71_amd import workloads as W
 
@@ -47,9 +48,8 @@ def gpu_decode(pkv, d: Fp8Dev, out_dtype="f32"):
 
 def oracle_decode(b: W.PagedBatch, f: W.Fp8Pools, seqs=None):
     _, _, tables = b.compact_pool(extra_poison_blocks=0)   # table entries -> index in block_ids
-    sel = np.arange(b.S) if seqs is None else np.asarray(seqs)
-    return oracle.decode_fp8(b.q[sel], b.dtype, f.k_blocks, f.v_blocks, f.k_scale, f.v_scale,
-                             tables[sel], b.context_lens[sel], b.scale)
+    return decode_fp8_par(b.q, b.dtype, f.k_blocks, f.v_blocks, f.k_scale, f.v_scale, tables,
+                          b.context_lens, b.scale, seqs=seqs)
 
 
 def check(pkv, b, seed=0, seqs=None):
@@ -230,14 +230,10 @@ def test_copy_blocks_fp8_bit_exact(gpu_lib):
 
 
 # ---------------------------------------------------------------- full-size workload
-def test_decode_fp8_llama3_8b_full_size_sampled(gpu_lib):
-    """The benchmarked Llama-3-8B batch with FP8 pools (the bench's FP8 row),
-    the longest, the shortest and 10 random sequences checked."""
-    b = W.llama3_8b_bf16(0)
-    order = np.argsort(b.context_lens)
-    seqs = sorted(set([int(order[0]), int(order[-1])] +
-                      np.random.default_rng(1).choice(b.S, 10, replace=False).tolist()))
-    check(gpu_lib, b, seed=1, seqs=seqs)
+def test_decode_fp8_llama3_8b_full_size(gpu_lib):
+    """The benchmarked Llama-3-8B batch with FP8 pools (the bench's FP8 row):
+    every output element of every sequence against the oracle."""
+    check(gpu_lib, W.llama3_8b_bf16(0), seed=1)
 
 
 # ---------------------------------------------------------------- prefill over FP8 pools
@@ -258,10 +254,12 @@ def check_prefill(pkv, b, seed=0, rows=None):
     f = W.fp8_pools(b, seed)
     out = gpu_prefill_fp8(pkv, Fp8Dev(b, f))
     _, _, tables = b.compact_pool(extra_poison_blocks=0)
-    ref = oracle.prefill_fp8(b.q, b.dtype, b.cu_seqlens_q, f.k_blocks, f.v_blocks, f.k_scale,
-                             f.v_scale, tables, b.context_lens, b.scale, rows=rows)
-    if rows is not None:
-        ref = ref[rows]
+    if rows is None:
+        ref = oracle.prefill_fp8(b.q, b.dtype, b.cu_seqlens_q, f.k_blocks, f.v_blocks, f.k_scale,
+                                 f.v_scale, tables, b.context_lens, b.scale)
+    else:
+        ref = prefill_fp8_rows_par(b.q, b.dtype, b.cu_seqlens_q, f.k_blocks, f.v_blocks,
+                                   f.k_scale, f.v_scale, tables, b.context_lens, b.scale, rows)
         out = out[torch.as_tensor(np.asarray(rows)).cuda()]
     err = max_abs(out, ref)
     assert err <= TOL[b.dtype], f"max abs err {err}"
@@ -313,13 +311,13 @@ def test_prefill_fp8_blocks_of_8(gpu_lib, dtype, D):
     check_prefill(gpu_lib, b, seed=D)
 
 
-def test_prefill_fp8_full_size_sampled(gpu_lib):
+def test_prefill_fp8_full_size_strided_rows(gpu_lib):
     """The benchmarked prefill workload (8 x 512-token chunks after 4k-33k
-    tokens) over FP8 pools, sampled rows against the oracle."""
+    tokens) over FP8 pools: every head of a quarter of the query rows (every
+    fourth row of every chunk from its first, plus its last) against the
+    oracle."""
     b = W.prefill_bf16(0)
-    rng = np.random.default_rng(5)
-    rows = sorted(set([0, 511, 4095, 2048] + rng.choice(b.q.shape[0], 10, replace=False).tolist()))
-    check_prefill(gpu_lib, b, seed=7, rows=rows)
+    check_prefill(gpu_lib, b, seed=7, rows=W.strided_chunk_rows(b.cu_seqlens_q, 4))
 
 
 def test_prefill_fp8_context_of_131072_tokens(gpu_lib):
