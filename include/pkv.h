@@ -19,6 +19,11 @@
  *  - Errors: scalar arguments are validated on the host before any launch; a
  *    failure returns a non-zero pkv_status and leaves all memory untouched.
  *    A failed launch returns PKV_ERR_HIP.  pkv_last_error() gives detail.
+ *  - Alignment: tensor data (q, out, key, value, the pools, workspaces) is read
+ *    and written with 16-byte vector accesses, so those pointers must be
+ *    16-byte aligned; index arrays (tables, lengths, slots, pairs, cu arrays)
+ *    and scales must be aligned to their element size.  Anything else is
+ *    refused with PKV_ERR_INVALID_ARG before any launch.
  *  - Device-resident CONTENTS (block ids, slots, lengths, cu_seqlens) are the
  *    caller's contract and are not validated: out-of-range values are undefined
  *    behaviour.  The host block manager below only ever produces valid ones.
@@ -30,7 +35,8 @@
  *  - Supported instantiations: kv dtype {f32, f16, bf16}; D in {64, 128};
  *    B in {1, 2, 4, 8, 16, 32}; any Hkv >= 1 and Hq a multiple of Hkv.
  *    FP8 pools (PKV_FP8_E4M3) are written by pkv_reshape_and_cache_fp8, read
- *    by pkv_paged_attention_decode_fp8 and copied by pkv_copy_blocks.
+ *    by the _fp8 variants of decode, cascade decode, prefill and the mixed
+ *    batch, and copied by pkv_copy_blocks and pkv_swap_blocks.
  *    Anything else returns PKV_ERR_UNSUPPORTED.
  */
 #ifndef PKV_H_

@@ -20,6 +20,9 @@ bool supported_head_dim(int32_t D) { return D == 64 || D == 128; }
 bool supported_block(int32_t B) {
   return B == 1 || B == 2 || B == 4 || B == 8 || B == 16 || B == 32;
 }
+// Tensor data is read and written with 16-byte vector accesses; index arrays
+// and scales with accesses of their element size.
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 int ilog2(int32_t x) {
   int r = 0;
   while ((1 << r) < x) ++r;
@@ -83,6 +86,11 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
   if (T == 0) return PKV_OK;
   PKV_REQUIRE(key && value && k_cache && v_cache && slot_mapping, PKV_ERR_INVALID_ARG,
               "reshape_and_cache: null pointer");
+  PKV_REQUIRE(aligned(key, 16) && aligned(value, 16) && aligned(k_cache, 16) &&
+                  aligned(v_cache, 16) && aligned(slot_mapping, 8),
+              PKV_ERR_INVALID_ARG,
+              "reshape_and_cache: key, value and the pools must be 16-byte aligned, slot_mapping "
+              "8-byte aligned");
   const int64_t row_bytes = (int64_t)Hkv * D * dt_bytes(kv_dtype);
   return launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, T, row_bytes, B,
                                   static_cast<hipStream_t>(stream));
@@ -104,6 +112,12 @@ pkv_status pkv_reshape_and_cache_fp8(const void* key, const void* value, pkv_dty
   if (T == 0) return PKV_OK;
   PKV_REQUIRE(key && value && k_cache && v_cache && slot_mapping && k_scale && v_scale,
               PKV_ERR_INVALID_ARG, "reshape_and_cache_fp8: null pointer");
+  PKV_REQUIRE(aligned(key, 16) && aligned(value, 16) && aligned(k_cache, 16) &&
+                  aligned(v_cache, 16) && aligned(slot_mapping, 8) && aligned(k_scale, 4) &&
+                  aligned(v_scale, 4),
+              PKV_ERR_INVALID_ARG,
+              "reshape_and_cache_fp8: key, value and the pools must be 16-byte aligned, "
+              "slot_mapping 8-byte, the scales 4-byte aligned");
   return launch_reshape_and_cache_fp8(key, value, in_dtype, k_cache, v_cache, slot_mapping, T, Hkv,
                                       D, k_scale, v_scale, static_cast<hipStream_t>(stream));
 }
@@ -181,6 +195,14 @@ static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv
   PKV_REQUIRE(!fp8 || (k_scale && v_scale), PKV_ERR_INVALID_ARG, "decode_fp8: null scale array");
   PKV_REQUIRE(!cascade || (cg.cu && cg.prefix_lens), PKV_ERR_INVALID_ARG,
               "decode_cascade: null pointer");
+  PKV_REQUIRE(aligned(out, 16) && aligned(q, 16) && aligned(k_cache, 16) && aligned(v_cache, 16) &&
+                  aligned(workspace, 16),
+              PKV_ERR_INVALID_ARG,
+              "decode: out, q, the pools and the workspace must be 16-byte aligned");
+  PKV_REQUIRE(aligned(block_tables, 4) && aligned(context_lens, 4) && aligned(k_scale, 4) &&
+                  aligned(v_scale, 4) && aligned(cg.cu, 4) && aligned(cg.prefix_lens, 4),
+              PKV_ERR_INVALID_ARG,
+              "decode: index arrays and scales must be aligned to their element size");
   DecodePlan plan;
   const pkv_status pst = plan_decode(S, Hq, Hkv, D, B, max_context_len, &plan);
   if (pst != PKV_OK) return pst;
@@ -343,6 +365,12 @@ static pkv_status prefill_args(void* out, pkv_dtype out_dtype, const void* q,
   PKV_REQUIRE(out && q && cu_seqlens_q && k_cache && v_cache && block_tables && context_lens,
               PKV_ERR_INVALID_ARG, "prefill: null pointer");
   PKV_REQUIRE(!fp8 || (k_scale && v_scale), PKV_ERR_INVALID_ARG, "prefill_fp8: null scale array");
+  PKV_REQUIRE(aligned(out, 16) && aligned(q, 16) && aligned(k_cache, 16) && aligned(v_cache, 16),
+              PKV_ERR_INVALID_ARG, "prefill: out, q and the pools must be 16-byte aligned");
+  PKV_REQUIRE(aligned(cu_seqlens_q, 4) && aligned(block_tables, 4) && aligned(context_lens, 4) &&
+                  aligned(k_scale, 4) && aligned(v_scale, 4),
+              PKV_ERR_INVALID_ARG,
+              "prefill: index arrays and scales must be aligned to their element size");
   a->out = out;
   a->q = q;
   a->cu_seqlens_q = cu_seqlens_q;
@@ -418,6 +446,8 @@ pkv_status pkv_paged_attention_prefill(void* out, pkv_dtype out_dtype, const voi
   PKV_REQUIRE(plan.workspace_bytes == 0 || (workspace && workspace_bytes >= plan.workspace_bytes),
               PKV_ERR_WORKSPACE, "prefill: workspace of %zu bytes needed, %zu given",
               plan.workspace_bytes, workspace ? workspace_bytes : (size_t)0);
+  PKV_REQUIRE(aligned(workspace, 16), PKV_ERR_INVALID_ARG,
+              "prefill: the workspace must be 16-byte aligned");
   attach_prefill_plan(plan, workspace, &a);
   return launch_prefill(kv_dtype, a, static_cast<hipStream_t>(stream));
 }
@@ -443,6 +473,8 @@ pkv_status pkv_paged_attention_prefill_fp8(void* out, pkv_dtype out_dtype, const
   PKV_REQUIRE(plan.workspace_bytes == 0 || (workspace && workspace_bytes >= plan.workspace_bytes),
               PKV_ERR_WORKSPACE, "prefill_fp8: workspace of %zu bytes needed, %zu given",
               plan.workspace_bytes, workspace ? workspace_bytes : (size_t)0);
+  PKV_REQUIRE(aligned(workspace, 16), PKV_ERR_INVALID_ARG,
+              "prefill_fp8: the workspace must be 16-byte aligned");
   attach_prefill_plan(plan, workspace, &a);
   return launch_prefill(DT_FP8, a, static_cast<hipStream_t>(stream));
 }
@@ -501,6 +533,8 @@ static pkv_status mixed_impl(void* out, pkv_dtype out_dtype, const void* q,
   const size_t need = mixed_workspace_size(plan, pplan);
   PKV_REQUIRE(workspace && workspace_bytes >= need, PKV_ERR_WORKSPACE,
               "mixed: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  PKV_REQUIRE(aligned(workspace, 16), PKV_ERR_INVALID_ARG,
+              "mixed: the workspace must be 16-byte aligned");
   DecodeArgs da{};
   da.out = out;
   da.q = q;
@@ -601,10 +635,16 @@ pkv_status pkv_swap_blocks(const void* const* src_pools, void* const* dst_pools,
   PKV_REQUIRE(supported_block(B), PKV_ERR_UNSUPPORTED, "swap_blocks: block_size %d", B);
   if (N == 0 || num_pools == 0) return PKV_OK;
   PKV_REQUIRE(src_pools && dst_pools && block_pairs, PKV_ERR_INVALID_ARG, "swap_blocks: null pointer");
+  PKV_REQUIRE(aligned(block_pairs, 8), PKV_ERR_INVALID_ARG,
+              "swap_blocks: block_pairs must be 8-byte aligned");
+  for (int32_t i = 0; i < num_pools; ++i) {
+    PKV_REQUIRE(src_pools[i] && dst_pools[i], PKV_ERR_INVALID_ARG, "swap_blocks: null pool %d", i);
+    PKV_REQUIRE(aligned(src_pools[i], 16) && aligned(dst_pools[i], 16), PKV_ERR_INVALID_ARG,
+                "swap_blocks: pool %d is not 16-byte aligned", i);
+  }
   std::vector<const void*> src(num_pools);
   std::vector<void*> dst(num_pools);
   for (int32_t i = 0; i < num_pools; ++i) {
-    PKV_REQUIRE(src_pools[i] && dst_pools[i], PKV_ERR_INVALID_ARG, "swap_blocks: null pool %d", i);
     const void* d = nullptr;
     pkv_status st = device_view(src_pools[i], &src[i], "swap_blocks (source pool)");
     if (st != PKV_OK) return st;
@@ -632,9 +672,14 @@ pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t
   PKV_REQUIRE(supported_block(B), PKV_ERR_UNSUPPORTED, "copy_blocks: block_size %d", B);
   if (N == 0 || num_layers == 0) return PKV_OK;
   PKV_REQUIRE(k_caches && v_caches && block_pairs, PKV_ERR_INVALID_ARG, "copy_blocks: null pointer");
-  for (int32_t l = 0; l < num_layers; ++l)
+  PKV_REQUIRE(aligned(block_pairs, 8), PKV_ERR_INVALID_ARG,
+              "copy_blocks: block_pairs must be 8-byte aligned");
+  for (int32_t l = 0; l < num_layers; ++l) {
     PKV_REQUIRE(k_caches[l] && v_caches[l], PKV_ERR_INVALID_ARG, "copy_blocks: null pool, layer %d",
                 l);
+    PKV_REQUIRE(aligned(k_caches[l], 16) && aligned(v_caches[l], 16), PKV_ERR_INVALID_ARG,
+                "copy_blocks: pool of layer %d is not 16-byte aligned", l);
+  }
   const int64_t block_bytes = (int64_t)B * Hkv * D * dt_bytes(kv_dtype);
   return launch_copy_blocks(k_caches, v_caches, num_layers, block_pairs, N, block_bytes,
                             static_cast<hipStream_t>(stream));

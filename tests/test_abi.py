@@ -104,3 +104,33 @@ def test_cache_ops_reject_bad_arguments(lib):
     assert lib.pkv_copy_blocks(None, None, 1, None, 0, 16, 8, 128, 2, None) == 0   # N = 0: no-op
     assert lib.pkv_copy_blocks(None, None, 1, FAKE, 3, 16, 8, 128, 2, None) == 1
     assert lib.pkv_copy_blocks(None, None, 1, FAKE, 3, 16, 8, 128, 9, None) == 2
+
+
+MIS = ctypes.c_void_p(0x1008)    # 8-byte but not 16-byte aligned (never dereferenced)
+
+
+def test_misaligned_pointers_are_refused(lib):
+    """Tensor data is moved with 16-byte vector accesses: a pointer that is not
+    16-byte aligned (a view at an odd element offset) is refused before any
+    launch; index arrays need their element alignment only."""
+    need = ctypes.c_size_t(0)
+    lib.pkv_decode_workspace_size(4, 8, 4, 128, 16, 2048, ctypes.byref(need))
+
+    def decode(out=FAKE, q=FAKE, k=FAKE, tables=FAKE, ws=FAKE):
+        return lib.pkv_paged_attention_decode(out, 0, q, k, FAKE, 2, tables, 128, FAKE, 2048, 4, 8,
+                                              4, 128, 16, 0.1, ws, need.value, None)
+    for kw in (dict(out=MIS), dict(q=MIS), dict(k=MIS), dict(ws=MIS),
+               dict(tables=ctypes.c_void_p(0x1002))):
+        assert decode(**kw) == 1 and b"aligned" in lib.pkv_last_error(), kw
+    rc = lib.pkv_paged_attention_prefill(FAKE, 0, MIS, FAKE, 32, 32, FAKE, FAKE, 2, FAKE, 512, FAKE,
+                                         8192, 1, 4, 1, 128, 16, 0.1, None, 0, None)
+    assert rc == 1 and b"aligned" in lib.pkv_last_error()
+    assert lib.pkv_reshape_and_cache(MIS, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 2, None) == 1
+    assert lib.pkv_reshape_and_cache(FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1004), 4, 8, 128, 16,
+                                     10, 2, None) == 1
+    pools = (ctypes.c_void_p * 2)(0x1000, 0x1008)
+    good = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    assert lib.pkv_copy_blocks(pools, good, 2, FAKE, 3, 16, 8, 128, 2, None) == 1
+    assert b"layer 1" in lib.pkv_last_error()
+    assert lib.pkv_copy_blocks(good, good, 2, ctypes.c_void_p(0x1004), 3, 16, 8, 128, 2, None) == 1
+    assert lib.pkv_swap_blocks(good, pools, 2, FAKE, 3, 16, 8, 128, 2, None) == 1
