@@ -9,8 +9,9 @@
  *  - Ownership: every pointer is owned by the caller.  Tensor pointers are
  *    DEVICE pointers (hipMalloc'd or torch CUDA tensors on the current device);
  *    the library allocates no device memory and keeps no state beyond a
- *    thread-local error string, the host block managers the caller creates
- *    and caches of the per-device CU count and of kernel occupancies.
+ *    thread-local error string, the host block managers the caller creates,
+ *    caches of the per-device CU count and of kernel occupancies, and the
+ *    static scratch array of pkv_paged_attention_decode_noalloc.
  *  - Threads: the kernel calls may be made from several host threads at once
  *    (the caches are atomic); calls that overlap on one device need their own
  *    workspaces.
@@ -131,6 +132,32 @@ pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void
                                       int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
                                       float scale, void* workspace, size_t workspace_bytes,
                                       void* stream);
+
+/* ------------------------------------------------------------------------
+ * paged_attention_decode_noalloc -- pkv_paged_attention_decode without a
+ * workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.
+ *
+ * Arguments, result and errors are those of pkv_paged_attention_decode (the
+ * same kernels and launch shapes, so the same bits).  The partial softmax
+ * states live in a static device array of 32 MiB inside the library, one per
+ * device, held until the process ends; a call needs at most
+ * (waves of its launch) x 2 x (query heads per row) x (D + 2) x 4 bytes of it,
+ * about 4.3 MB for 32 query / 8 KV heads at D = 128 on a 256-CU device.  A
+ * call needing more fails with PKV_ERR_WORKSPACE before any launch.  The call
+ * allocates nothing (no hipMalloc, no hipFree).  Every call on a device shares
+ * that device's array and nothing needs to start at zero; calls that overlap
+ * on one device (two streams, two threads) race on it and give undefined
+ * results: serialise them on one stream.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_paged_attention_decode_noalloc(void* out, pkv_dtype out_dtype, const void* q,
+                                              const void* k_cache, const void* v_cache,
+                                              pkv_dtype kv_dtype, const int32_t* block_tables,
+                                              int32_t max_blocks_per_seq,
+                                              const int32_t* context_lens, int32_t max_context_len,
+                                              int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                                              int32_t B, float scale, void* stream);
 
 /* ------------------------------------------------------------------------
  * paged_attention_decode_cascade -- decode for a batch whose sequences come

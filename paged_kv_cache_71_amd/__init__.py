@@ -10,7 +10,7 @@ from ._binding import (BlockManager, PkvError, PkvOOM, copy_blocks, declared_sym
                        decode_cascade_workspace_size, decode_workspace_size, load_library,
                        mixed_workspace_size, paged_attention_decode,
                        paged_attention_decode_cascade, paged_attention_decode_cascade_fp8,
-                       paged_attention_decode_fp8, paged_attention_mixed, paged_attention_mixed_fp8,
+                       paged_attention_decode_fp8, paged_attention_decode_noalloc, paged_attention_mixed, paged_attention_mixed_fp8,
                        paged_attention_prefill,
                        paged_attention_prefill_fp8, prefill_workspace_size,
                        reshape_and_cache, reshape_and_cache_fp8, swap_blocks)
@@ -19,7 +19,8 @@ __all__ = [
     "BlockManager", "PkvError", "PkvOOM", "copy_blocks", "declared_symbols",
     "decode_cascade_workspace_size", "decode_workspace_size", "load_library",
     "mixed_workspace_size", "paged_attention_decode", "paged_attention_decode_cascade",
-    "paged_attention_decode_cascade_fp8", "paged_attention_decode_fp8", "paged_attention_mixed",
+    "paged_attention_decode_cascade_fp8", "paged_attention_decode_fp8",
+    "paged_attention_decode_noalloc", "paged_attention_mixed",
     "paged_attention_mixed_fp8", "paged_attention_prefill",
     "paged_attention_prefill_fp8",
     "prefill_workspace_size", "reshape_and_cache", "reshape_and_cache_fp8", "swap_blocks",

@@ -58,6 +58,8 @@ def load_library(path: str | None = None):
         "pkv_decode_workspace_size": (st, [i32, i32, i32, i32, i32, i32, SZP]),
         "pkv_paged_attention_decode": (st, [P, st, P, P, P, st, P, i32, P, i32, i32, i32, i32, i32,
                                             i32, f32, P, sz, P]),
+        "pkv_paged_attention_decode_noalloc": (st, [P, st, P, P, P, st, P, i32, P, i32, i32, i32,
+                                                    i32, i32, i32, f32, P]),
         "pkv_prefill_workspace_size": (st, [i32, i32, i32, i32, i32, i32, i32, st, i32, SZP]),
         "pkv_paged_attention_prefill": (st, [P, st, P, P, i32, i32, P, P, st, P, i32, P, i32, i32,
                                              i32, i32, i32, i32, f32, P, sz, P]),
@@ -210,6 +212,30 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B,
         float(scale), ws_ptr, ws_bytes, _stream(stream)), "paged_attention_decode")
+    return out
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens,
+                                   max_context_len: int, scale: float, stream=None):
+    """Decode attention like paged_attention_decode, with the partial states in
+    the library's static device scratch instead of a workspace: nothing is
+    allocated.  Calls that overlap on one device race on that scratch."""
+    torch = _torch()
+    lib = load_library()
+    S, Hq, D = q.shape
+    NB, B, Hkv, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("paged_attention_decode_noalloc: shape mismatch")
+    if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("paged_attention_decode_noalloc: q/k/v dtype mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("paged_attention_decode_noalloc: block_tables [S, max_nb] / context_lens [S]")
+    _check(lib.pkv_paged_attention_decode_noalloc(
+        _dev(out, "out"), dtype_code(out), _dev(q, "q"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), dtype_code(k_cache),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B,
+        float(scale), _stream(stream)), "paged_attention_decode_noalloc")
     return out
 
 

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <vector>
 
 #include "pkv_internal.h"
@@ -152,6 +153,39 @@ struct CascadeGroups {
   int32_t n_groups = 0, max_group_size = 0, max_prefix_len = 0;
 };
 
+// The allocation-free decode's scratch: a file-scope device array, one copy on
+// every device the library runs on, held until the process ends.  Host code
+// never uses its name as an address: scratch_address() gives the device's own
+// address of it.  Every call on a device shares that device's copy.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+static std::atomic<void*> g_scratch_ptr[64];  // per device ordinal; null = not yet looked up
+
+// Device address of this device's scratch (looked up once per device, with the
+// device current; concurrent first calls store the same value).
+static pkv_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PKV_ERR_HIP, "decode_noalloc: cannot query the current device");
+  }
+  if (dev < 0 || dev >= 64) return fail(PKV_ERR_UNSUPPORTED, "decode_noalloc: device %d", dev);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(PKV_ERR_HIP, "decode_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return PKV_OK;
+}
+
+// use_scratch: the allocation-free variant; the workspace arguments are unused
+// and the device's static scratch holds the partial states instead.
 static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype kv_dtype,
                               bool fp8, const void* k_cache, const void* v_cache,
                               const float* k_scale, const float* v_scale,
@@ -159,7 +193,8 @@ static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv
                               const int32_t* context_lens, int32_t max_context_len, int32_t S,
                               int32_t Hq, int32_t Hkv, int32_t D, int32_t B, float scale,
                               void* workspace, size_t workspace_bytes, void* stream,
-                              const CascadeGroups& cg = CascadeGroups()) {
+                              const CascadeGroups& cg = CascadeGroups(),
+                              bool use_scratch = false) {
   g_last_error[0] = 0;
   const bool cascade = cg.on;
   PKV_REQUIRE(S >= 0 && Hq > 0 && Hkv > 0 && D > 0 && B > 0, PKV_ERR_INVALID_ARG,
@@ -206,7 +241,7 @@ static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv
   DecodePlan plan;
   const pkv_status pst = plan_decode(S, Hq, Hkv, D, B, max_context_len, &plan);
   if (pst != PKV_OK) return pst;
-  if (!cascade)
+  if (!cascade && !use_scratch)
     PKV_REQUIRE(workspace_bytes >= plan.workspace_bytes && (plan.workspace_bytes == 0 || workspace),
                 PKV_ERR_WORKSPACE, "decode: workspace of %zu bytes needed, %zu given",
                 plan.workspace_bytes, workspace_bytes);
@@ -238,6 +273,23 @@ static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv
     return launch_decode_cascade(kv_dtype, fp8, a, cg.cu, cg.prefix_lens, cg.n_groups,
                                  cg.max_group_size, cg.max_prefix_len, workspace, workspace_bytes,
                                  static_cast<hipStream_t>(stream));
+  if (use_scratch) {
+    // Size the states for the waves the launches will really run on this
+    // device (the same grids as with a caller's workspace, hence the same
+    // bits), then place them in the static scratch.
+    void* ptr = nullptr;
+    pkv_status st = scratch_address(&ptr);
+    if (st != PKV_OK) return st;
+    int waves = 0;
+    st = launch_decode(kv_dtype, fp8, plan, a, static_cast<hipStream_t>(stream), &waves);
+    if (st != PKV_OK) return st;
+    if (waves < plan.max_waves) layout_decode_workspace(&plan, waves);
+    PKV_REQUIRE(plan.workspace_bytes <= kNoAllocScratchBytes, PKV_ERR_WORKSPACE,
+                "decode_noalloc: %zu bytes of partial states needed, the static scratch holds "
+                "%zu (fewer sequences per call, or pkv_paged_attention_decode with a workspace)",
+                plan.workspace_bytes, kNoAllocScratchBytes);
+    attach_decode_workspace(&a, plan, ptr);
+  }
   return launch_decode(kv_dtype, fp8, plan, a, static_cast<hipStream_t>(stream));
 }
 
@@ -253,6 +305,18 @@ pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void
   return decode_impl(out, out_dtype, q, kv_dtype, false, k_cache, v_cache, nullptr, nullptr,
                      block_tables, max_blocks_per_seq, context_lens, max_context_len, S, Hq, Hkv,
                      D, B, scale, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_attention_decode_noalloc(void* out, pkv_dtype out_dtype, const void* q,
+                                              const void* k_cache, const void* v_cache,
+                                              pkv_dtype kv_dtype, const int32_t* block_tables,
+                                              int32_t max_blocks_per_seq,
+                                              const int32_t* context_lens, int32_t max_context_len,
+                                              int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                                              int32_t B, float scale, void* stream) {
+  return decode_impl(out, out_dtype, q, kv_dtype, false, k_cache, v_cache, nullptr, nullptr,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, S, Hq, Hkv,
+                     D, B, scale, nullptr, 0, stream, CascadeGroups(), true);
 }
 
 pkv_status pkv_decode_cascade_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t D,

@@ -1126,7 +1126,7 @@ int occupancy_of() {
 // Split launch (one resident wave set: CUs x occupancy, capped by grid_cap)
 // followed by the merge launch.
 template <int DT, int D, int GC, bool UNI, bool MF, bool F8, int BPT = 1>
-pkv_status launch_split(DecodeArgs a, int grid_cap, int ncu, hipStream_t stream) {
+pkv_status launch_split(DecodeArgs a, int grid_cap, int ncu, hipStream_t stream, int* waves_only) {
   // Matrix-core path: one workgroup (one wave per SIMD, three tiles in
   // flight each) per CU measured fastest for 16-bit pools -- 3-7% ahead of
   // two per CU on the Llama-3-8B batch; FP8 pools (half the bytes per tile)
@@ -1136,6 +1136,10 @@ pkv_status launch_split(DecodeArgs a, int grid_cap, int ncu, hipStream_t stream)
   if (grid > grid_cap) grid = grid_cap;
   if (grid < 1) grid = 1;
   a.n_waves = (int)grid * kWaves;
+  if (waves_only) {  // sizing pass: report the waves, launch nothing
+    if (a.n_waves > *waves_only) *waves_only = a.n_waves;
+    return PKV_OK;
+  }
   hipLaunchKernelGGL((decode_split_kernel<DT, D, GC, UNI, MF, F8, BPT>), dim3((unsigned)grid),
                      dim3(kThreads), 0, stream, a);
   pkv_status st = check_launch("paged_attention_decode (split)");
@@ -1149,39 +1153,45 @@ pkv_status launch_split(DecodeArgs a, int grid_cap, int ncu, hipStream_t stream)
 }
 
 template <int DT, int D, int GC, bool F8>
-pkv_status launch_typed(const DecodeArgs& a, int grid_cap, int ncu, bool uni, hipStream_t stream) {
+pkv_status launch_typed(const DecodeArgs& a, int grid_cap, int ncu, bool uni, hipStream_t stream,
+                        int* waves_only) {
   // matrix cores: 16-bit q, D = 128, 4, 8 or 16 query heads per row, a tile in
   // one block (B >= 16), two (B = 8) or four (B = 4)
   if constexpr (DT != DT_F32 && D == 128 && (GC == 4 || GC == 8 || GC == 16)) {
-    if (a.B >= 16) return launch_split<DT, D, GC, true, true, F8>(a, grid_cap, ncu, stream);
-    if (a.B == 8) return launch_split<DT, D, GC, true, true, F8, 2>(a, grid_cap, ncu, stream);
-    if (a.B == 4) return launch_split<DT, D, GC, true, true, F8, 4>(a, grid_cap, ncu, stream);
+    if (a.B >= 16)
+      return launch_split<DT, D, GC, true, true, F8>(a, grid_cap, ncu, stream, waves_only);
+    if (a.B == 8)
+      return launch_split<DT, D, GC, true, true, F8, 2>(a, grid_cap, ncu, stream, waves_only);
+    if (a.B == 4)
+      return launch_split<DT, D, GC, true, true, F8, 4>(a, grid_cap, ncu, stream, waves_only);
   }
   if constexpr (GC == 16) {  // chunks of 16 heads exist on the matrix-core path only
     return fail(PKV_ERR_UNSUPPORTED, "decode: 16-head rows need the matrix-core path");
   } else {
-    if (uni) return launch_split<DT, D, GC, true, false, F8>(a, grid_cap, ncu, stream);
-    return launch_split<DT, D, GC, false, false, F8>(a, grid_cap, ncu, stream);
+    if (uni) return launch_split<DT, D, GC, true, false, F8>(a, grid_cap, ncu, stream, waves_only);
+    return launch_split<DT, D, GC, false, false, F8>(a, grid_cap, ncu, stream, waves_only);
   }
 }
 
 template <int DT, int D, bool F8>
-pkv_status launch_gc(const DecodeArgs& a, int grid_cap, int ncu, bool uni, hipStream_t stream) {
+pkv_status launch_gc(const DecodeArgs& a, int grid_cap, int ncu, bool uni, hipStream_t stream,
+                     int* waves_only) {
   switch (a.gc) {
-    case 1: return launch_typed<DT, D, 1, F8>(a, grid_cap, ncu, uni, stream);
-    case 2: return launch_typed<DT, D, 2, F8>(a, grid_cap, ncu, uni, stream);
-    case 4: return launch_typed<DT, D, 4, F8>(a, grid_cap, ncu, uni, stream);
-    case 8: return launch_typed<DT, D, 8, F8>(a, grid_cap, ncu, uni, stream);
-    case 16: return launch_typed<DT, D, 16, F8>(a, grid_cap, ncu, uni, stream);
+    case 1: return launch_typed<DT, D, 1, F8>(a, grid_cap, ncu, uni, stream, waves_only);
+    case 2: return launch_typed<DT, D, 2, F8>(a, grid_cap, ncu, uni, stream, waves_only);
+    case 4: return launch_typed<DT, D, 4, F8>(a, grid_cap, ncu, uni, stream, waves_only);
+    case 8: return launch_typed<DT, D, 8, F8>(a, grid_cap, ncu, uni, stream, waves_only);
+    case 16: return launch_typed<DT, D, 16, F8>(a, grid_cap, ncu, uni, stream, waves_only);
   }
   return fail(PKV_ERR_UNSUPPORTED, "decode: head chunk %d", a.gc);
 }
 
 template <int DT, bool F8>
-pkv_status launch_d(const DecodeArgs& a, int grid_cap, int ncu, bool uni, hipStream_t stream) {
+pkv_status launch_d(const DecodeArgs& a, int grid_cap, int ncu, bool uni, hipStream_t stream,
+                    int* waves_only) {
   switch (a.D) {
-    case 64: return launch_gc<DT, 64, F8>(a, grid_cap, ncu, uni, stream);
-    case 128: return launch_gc<DT, 128, F8>(a, grid_cap, ncu, uni, stream);
+    case 64: return launch_gc<DT, 64, F8>(a, grid_cap, ncu, uni, stream, waves_only);
+    case 128: return launch_gc<DT, 128, F8>(a, grid_cap, ncu, uni, stream, waves_only);
   }
   return fail(PKV_ERR_UNSUPPORTED, "decode: head_dim %d", a.D);
 }
@@ -1252,15 +1262,21 @@ pkv_status plan_decode(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t /*
   int64_t grid = (tiles + kWaves - 1) / kWaves;
   if (grid > kMaxGrid) grid = kMaxGrid;
   if (grid < 1) grid = 1;
-  plan->max_waves = (int)grid * kWaves;
+  plan->gc_max = gc_max;
+  plan->D = D;
+  layout_decode_workspace(plan, (int)grid * kWaves);
+  return PKV_OK;
+}
+
+void layout_decode_workspace(DecodePlan* plan, int max_waves) {
+  plan->max_waves = max_waves;
   // states: two slots per wave, gc heads each (whichever path runs)
-  const size_t states = (size_t)plan->max_waves * 2 * gc_max;
+  const size_t states = (size_t)plan->max_waves * 2 * plan->gc_max;
   plan->ws_ps_off = 0;
-  plan->ws_rec_off = align_up(((size_t)sc + 1) * sizeof(int32_t));
+  plan->ws_rec_off = align_up(((size_t)plan->seqs_per_launch + 1) * sizeof(int32_t));
   plan->ws_ml_off = plan->ws_rec_off + align_up((size_t)plan->max_waves * sizeof(int4));
   plan->ws_acc_off = plan->ws_ml_off + align_up(states * 2 * sizeof(float));
-  plan->workspace_bytes = plan->ws_acc_off + states * (size_t)D * sizeof(float);
-  return PKV_OK;
+  plan->workspace_bytes = plan->ws_acc_off + states * (size_t)plan->D * sizeof(float);
 }
 
 void attach_decode_workspace(DecodeArgs* a, const DecodePlan& plan, void* workspace) {
@@ -1272,7 +1288,7 @@ void attach_decode_workspace(DecodeArgs* a, const DecodePlan& plan, void* worksp
 }
 
 pkv_status launch_decode(int kv_dt, bool fp8, const DecodePlan& plan, DecodeArgs a,
-                         hipStream_t stream) {
+                         hipStream_t stream, int* waves_only) {
   // (kv_dt: the dtype of q; the lane layout follows it, also over FP8 pools)
   const bool mf = kv_dt != DT_F32 && a.D == 128 && a.B >= 4 && plan.gc_mf > 0;
   a.gc = mf ? plan.gc_mf : plan.gc_vec;
@@ -1304,15 +1320,15 @@ pkv_status launch_decode(int kv_dt, bool fp8, const DecodePlan& plan, DecodeArgs
     pkv_status st;
     if (fp8) {
       switch (kv_dt) {
-        case DT_F16: st = launch_d<DT_F16, true>(b, (int)cap, ncu, uni, stream); break;
-        case DT_BF16: st = launch_d<DT_BF16, true>(b, (int)cap, ncu, uni, stream); break;
+        case DT_F16: st = launch_d<DT_F16, true>(b, (int)cap, ncu, uni, stream, waves_only); break;
+        case DT_BF16: st = launch_d<DT_BF16, true>(b, (int)cap, ncu, uni, stream, waves_only); break;
         default: return fail(PKV_ERR_UNSUPPORTED, "decode_fp8: q dtype %d", kv_dt);
       }
     } else {
       switch (kv_dt) {
-        case DT_F32: st = launch_d<DT_F32, false>(b, (int)cap, ncu, uni, stream); break;
-        case DT_F16: st = launch_d<DT_F16, false>(b, (int)cap, ncu, uni, stream); break;
-        case DT_BF16: st = launch_d<DT_BF16, false>(b, (int)cap, ncu, uni, stream); break;
+        case DT_F32: st = launch_d<DT_F32, false>(b, (int)cap, ncu, uni, stream, waves_only); break;
+        case DT_F16: st = launch_d<DT_F16, false>(b, (int)cap, ncu, uni, stream, waves_only); break;
+        case DT_BF16: st = launch_d<DT_BF16, false>(b, (int)cap, ncu, uni, stream, waves_only); break;
         default: return fail(PKV_ERR_UNSUPPORTED, "decode: kv dtype %d", kv_dt);
       }
     }

@@ -116,11 +116,15 @@ struct DecodePlan {
   int gc_mf;            // ... on the matrix-core path (4, 8 or 16 dividing G; 0: none)
   int max_waves;        // waves of the largest split launch (sizes the workspace)
   int seqs_per_launch;  // sequences handled by one split + merge launch pair
+  int gc_max, D;        // largest head chunk of either path; head dim (state sizes)
   size_t ws_ps_off, ws_rec_off, ws_ml_off, ws_acc_off;  // workspace layout (bytes)
   size_t workspace_bytes;
 };
 pkv_status plan_decode(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
                        int32_t max_context_len, DecodePlan* plan);
+// Lay the workspace out for at most max_waves waves per launch (plan_decode
+// uses the argument-only bound; a launch never uses more than plan.max_waves).
+void layout_decode_workspace(DecodePlan* plan, int max_waves);
 struct DecodeArgs;
 // point the workspace fields of a at the plan's layout inside ws
 void attach_decode_workspace(DecodeArgs* a, const DecodePlan& plan, void* ws);
@@ -150,9 +154,11 @@ struct DecodeArgs {
   const int32_t* seq_start;
   float* lse;
 };
-// q_dt: dtype of q (and of the pools unless fp8); fp8: the pools hold E4M3 codes
+// q_dt: dtype of q (and of the pools unless fp8); fp8: the pools hold E4M3 codes.
+// waves_only != null: launch nothing, store the most waves any split launch of
+// this call would run (on the current device) in *waves_only.
 pkv_status launch_decode(int q_dt, bool fp8, const DecodePlan& plan, DecodeArgs a,
-                         hipStream_t stream);
+                         hipStream_t stream, int* waves_only = nullptr);
 
 // Cascade decode (cascade.hip): groups of sequences sharing a prefix.
 pkv_status cascade_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
