@@ -326,8 +326,14 @@ def main():
         d.reshape()
         d.decode()
 
-    for _ in range(args.warmup):
+    # W untimed warm-up steps, continued (still untimed) until 300 ms of steps
+    # have run: the clocks take tens of milliseconds of load to settle
+    t0, n_warm = time.time(), 0
+    while n_warm < args.warmup or (time.time() - t0) * 1e3 < 300.0:
         step()
+        n_warm += 1
+        if n_warm % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     # the timed region: exactly K steps, events at its two ends only (an event
     # recorded between launches costs the stream a few microseconds)
@@ -340,21 +346,23 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
-    # the same K steps again with an event around every decode launch (the
-    # decode kernels' duration for the roofline) and after every step
+    # at least 100 more steps (K if larger) with an event around every decode
+    # launch (the decode kernels' duration for the roofline) and after every
+    # step: the distribution of step times
+    n_ev = max(100, args.steps)
     dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+              for _ in range(n_ev)]
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev + 1)]
     torch.cuda.synchronize()
     step_ev[0].record(stream)
-    for i in range(args.steps):
+    for i in range(n_ev):
         d.reshape()
         dec_ev[i][0].record(stream)
         d.decode()
         dec_ev[i][1].record(stream)
         step_ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    step_ms = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)])
+    step_ms = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(n_ev)])
     dec_ms = float(np.mean([a.elapsed_time(z) for a, z in dec_ev]))
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (dec_ms * 1e-3) / 1e9
@@ -382,6 +390,8 @@ def main():
             "context_tokens": int(b.context_lens.sum()),
             "kv_bytes_per_step": kv_bytes,
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+            "warmup_steps_run": n_warm,
+            "evented_steps": n_ev,
             "evented_step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5)
                                             for q in (10, 50, 90)],
         },
@@ -412,7 +422,7 @@ def main():
         # without leaving dirty lines whose write-back would be charged to decode
         flush = torch.ones(1 << 29, dtype=torch.float32, device=dev)
         fl = []
-        for _ in range(10):
+        for _ in range(100):
             flush.sum()
             a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
@@ -420,8 +430,12 @@ def main():
             z.record(stream)
             fl.append((a, z))
         torch.cuda.synchronize()
-        fms = float(np.mean([a.elapsed_time(z) for a, z in fl]))
-        rows["decode_llama3_8b_flushed"] = {"ms": round(fms, 5), "GB/s": round(kv_bytes / fms / 1e6, 1)}
+        ft = np.array([a.elapsed_time(z) for a, z in fl])
+        fms = float(np.median(ft))
+        rows["decode_llama3_8b_flushed"] = {
+            "ms_median": round(fms, 5), "GB/s": round(kv_bytes / fms / 1e6, 1),
+            "ms_p10_p90": [round(float(np.percentile(ft, q)), 5) for q in (10, 90)],
+            "launches": len(fl)}
         del flush
         rms, _ = time_fn(d.reshape, 20)
         rb = 2 * 2 * b.new_k.size * 2   # read + write of K and V rows
@@ -559,27 +573,45 @@ def measured_traffic():
     return rec.get("traffic_bytes_per_step")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(b, sample_tokens):
-    """The fp64 oracle as it is, on a bounded sample of the same workload: the
-    first sequences of the batch until ``sample_tokens`` context tokens."""
-    import oracle
+    """The fp64 oracle as it is, on a bounded sample of the same workload (the
+    first sequences of the batch until ``sample_tokens`` context tokens; all of
+    them by default), run on every core of this process's affinity mask: the
+    sample's sequences are cut into parts of similar length, one oracle call per
+    part (the oracle itself is unchanged; its result is that of one call)."""
+    from oracle.parallel import decode_par, host_threads
     k, v, tables = b.compact_pool()
     n = b.S
     if sample_tokens:
         n = min(b.S, int(np.searchsorted(np.cumsum(b.context_lens), sample_tokens) + 1))
     sel = np.arange(n)
-    runs, t0 = 0, time.perf_counter()
-    # about 10-20 s of CPU work: whole passes until 10 s have gone by (at most 10)
-    while runs < 10 and (runs == 0 or time.perf_counter() - t0 < 10.0):
-        oracle.decode(b.q[sel], k, v, b.dtype, tables[sel], b.context_lens[sel], b.scale)
-        runs += 1
-    dt = (time.perf_counter() - t0) / runs
+    threads = host_threads(cap=1 << 16)
+    times, t0 = [], time.perf_counter()
+    # about 10 s of wall time: whole passes until 10 s have gone by (3 to 30)
+    while len(times) < 30 and (len(times) < 3 or time.perf_counter() - t0 < 10.0):
+        t1 = time.perf_counter()
+        decode_par(b.q, k, v, b.dtype, tables, b.context_lens, b.scale, seqs=sel, threads=threads)
+        times.append(time.perf_counter() - t1)
+    dt = float(np.median(times))
     tokens = int(b.context_lens[sel].sum())
     bytes_ = tokens * 2 * b.Hkv * b.D * 2
-    log(f"[bench] cpu oracle: {n} sequences, {tokens} tokens, {dt:.2f} s per pass x {runs}")
-    return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    log(f"[bench] cpu oracle: {n} sequences, {tokens} tokens, {threads} threads, "
+        f"median {dt:.2f} s per pass of {len(times)}")
+    return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
             "sample": f"{n} of {b.S} sequences ({tokens} context tokens, {bytes_ / 1e6:.0f} MB of "
-                      f"KV), single-threaded fp64 C oracle, mean of {runs} passes of {dt:.2f} s"}
+                      f"KV), fp64 C oracle on {threads} threads (one per core of the affinity "
+                      f"mask, {cpu_model()}), median of {len(times)} passes of {dt:.2f} s"}
 
 
 if __name__ == "__main__":
