@@ -391,6 +391,25 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 constexpr int kTileKV = 32;                 // KV tokens per tile
 constexpr int kWaitLgkm0 = 0xC07F;          // s_waitcnt: LDS/scalar count 0, others at max
 constexpr int kTileQB = 2;                  // q blocks of 16 rows per wave
+// The tile kernel adds the lo parts of the weights (second P.V product) only
+// on tiles where some row's largest weight exceeds kLoShare of that row's
+// running total; see the softmax step.
+constexpr float kLoShare = 0.01f;
+
+// x + a.lo + a.hi of the two 16-bit values of DT packed in a (one dot2 against
+// (1, 1); ones must hold that pair in a VGPR, see tile kernel).
+template <int DT>
+__device__ __forceinline__ float add_pair16(uint32_t a, uint32_t ones, float x) {
+  if constexpr (DT == DT_BF16) {
+    typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b16x2_t, a),
+                                           __builtin_bit_cast(b16x2_t, ones), x, false);
+  } else {
+    typedef _Float16 h16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2_t, a), __builtin_bit_cast(h16x2_t, ones),
+                                  x, false);
+  }
+}
 
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma16(const u32x4_t a, const u32x4_t b, f32x4_t c) {
@@ -700,10 +719,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   f32x4_t SA[2][QB], SB[2][QB];   // S of the tile being softmaxed / of the next one
   u32x4_t PAh[QB], PAl[QB], PBh[QB], PBl[QB];  // P of the previous tile / of this one
+  bool FA = false, FB = false;   // whether that P has its lo parts (uniform)
+  // (1, 1) in DT, as a VGPR: as an inline constant the compiler would encode
+  // the 32-bit word as a float constant with different half words
+  uint32_t ones;
+  if constexpr (DT == DT_BF16) asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(ones));
+  else asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(ones));
 
   auto step = [&](const int j, auto ld_tag, auto pv_tag, auto qk_tag, auto sm_tag, auto mask_tag,
                   f32x4_t (&s_cur)[2][QB], f32x4_t (&s_nxt)[2][QB], const u32x4_t (&pph)[QB],
-                  const u32x4_t (&ppl)[QB], u32x4_t (&nph)[QB], u32x4_t (&npl)[QB])
+                  const u32x4_t (&ppl)[QB], u32x4_t (&nph)[QB], u32x4_t (&npl)[QB], bool pflag,
+                  bool& nflag)
       __attribute__((always_inline)) {
     constexpr bool LD = decltype(ld_tag)::value;
     constexpr bool PV = decltype(pv_tag)::value;
@@ -748,9 +774,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const uint2 hi = lds_read_tr16(vp + 16 * VP);
         const u32x4_t va = u32x4_t{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-        for (int c = 0; c < QB; ++c) {
-          o[d][c] = mfma16<DT>(va, pph[c], o[d][c]);
-          if constexpr (PSPLIT) o[d][c] = mfma16<DT>(va, ppl[c], o[d][c]);
+        for (int c = 0; c < QB; ++c) o[d][c] = mfma16<DT>(va, pph[c], o[d][c]);
+      }
+      if (pflag) {  // the lo parts of P(j-1): a second pass over the same V tile
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) {
+          const char* vp = V + (4 * g4 + (n >> 2)) * VP + (16 * d + 4 * (n & 3)) * ES;
+          const uint2 lo = lds_read_tr16(vp);
+          const uint2 hi = lds_read_tr16(vp + 16 * VP);
+          const u32x4_t va = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+          for (int c = 0; c < QB; ++c) o[d][c] = mfma16<DT>(va, ppl[c], o[d][c]);
         }
       }
     }
@@ -758,6 +792,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int kv0 = j * kTileKV;
       float alpha[QB];
       bool grow_any = false;
+      bool need_lo = false;
+      float pk[QB][8];  // this tile's weights (kept for their lo parts)
 #pragma unroll
       for (int c = 0; c < QB; ++c) {
         float r[8];
@@ -778,7 +814,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         grow_any |= grow;
         const float mu = m[c] == -__builtin_inff() ? 0.f : m[c];
         float rs = 0.f;
-        uint32_t hw[4], lw[4];
+        uint32_t hw[4];
 #pragma unroll
         for (int k = 0; k < 8; k += 2) {
           float p0 = fast_exp2(__builtin_fmaf(r[k], sl, -mu));
@@ -788,21 +824,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             p0 = kv <= pos[c] ? p0 : 0.f;
             p1 = kv + 1 <= pos[c] ? p1 : 0.f;
           }
-          rs += p0 + p1;
+          pk[c][k] = p0;
+          pk[c][k + 1] = p1;
           const uint32_t h = pack2<DT>(p0, p1);
           hw[k / 2] = h;
-          if constexpr (PSPLIT) lw[k / 2] = pack2<DT>(residual16<DT, 0>(p0, h), residual16<DT, 1>(p1, h));
+          rs = add_pair16<DT>(h, ones, rs);  // the sum of the weights as rounded
         }
         nph[c] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-        if constexpr (PSPLIT) npl[c] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
         lsum[c] = lsum[c] * alpha[c] + rs;
+        if constexpr (PSPLIT) {
+          // Rounding a weight w to 16 bits moves the row's result by about
+          // w * eps * (v - o) / total weight (the total is a sum of the same
+          // rounded weights, so a dominant weight's rounding cancels).  Where
+          // the largest weight of every row is at most kLoShare of the row's
+          // total so far (the final total is larger still), the result moves
+          // by far less than the tolerance and the lo parts are skipped; else
+          // this tile carries them (about 16 significant bits per weight).
+          float lrow = lsum[c];
+          pair_sum<16>(lrow);
+          pair_sum<32>(lrow);
+          const float pmax = fast_exp2(__builtin_fmaf(t, sl, -mu));  // 0 (or NaN) if all masked
+          need_lo |= pmax > kLoShare * lrow;
+        }
       }
       // keep the weights' computation here, beside the matrix-core work it
       // overlaps (else it sinks past the rescale branch below)
 #pragma unroll
-      for (int c = 0; c < QB; ++c) {
-        asm volatile("" ::"v"(nph[c]), "v"(lsum[c]));
-        if constexpr (PSPLIT) asm volatile("" ::"v"(npl[c]));
+      for (int c = 0; c < QB; ++c) asm volatile("" ::"v"(nph[c]), "v"(lsum[c]));
+      nflag = PSPLIT && __builtin_amdgcn_ballot_w64(need_lo) != 0;
+      if (nflag) {
+#pragma unroll
+        for (int c = 0; c < QB; ++c) {
+          uint32_t lw[4];
+          float rl = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; k += 2) {
+            const uint32_t h = nph[c][k / 2];
+            lw[k / 2] = pack2<DT>(residual16<DT, 0>(pk[c][k], h), residual16<DT, 1>(pk[c][k + 1], h));
+            rl = add_pair16<DT>(lw[k / 2], ones, rl);
+          }
+          npl[c] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+          lsum[c] += rl;
+          asm volatile("" ::"v"(npl[c]), "v"(lsum[c]));
+        }
       }
       // O now includes P(j-1) V(j-1): bring it to the new max
       if (__builtin_amdgcn_ballot_w64(grow_any)) {
@@ -824,34 +888,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       PAh[c] = PBh[c];
       if constexpr (PSPLIT) PAl[c] = PBl[c];
     }
+    FA = FB;
   };
 
   // step t0-1: S(t0) into SB; step t0: softmax(t0), S(t0+1) into SA, P(t0) into PA
-  step(t0 - 1, T{}, F{}, T{}, F{}, F{}, SA, SB, PAh, PAl, PBh, PBl);
-  step(t0, T{}, F{}, T{}, T{}, T{}, SB, SA, PBh, PBl, PAh, PAl);
+  step(t0 - 1, T{}, F{}, T{}, F{}, F{}, SA, SB, PAh, PAl, PBh, PBl, FA, FB);
+  step(t0, T{}, F{}, T{}, T{}, T{}, SB, SA, PBh, PBl, PAh, PAl, FB, FA);
   if (tl > t0) {
     // steady state, unrolled by two so S and P alternate between the A and B
     // registers; tiles wholly at or before every row's position skip the mask
     const int nfree = pos_min == 0x7fffffff ? tl : max(t0 + 1, min(tl, (pos_min + 1) / kTileKV));
     int j = t0 + 1;
     for (; j + 1 < nfree; j += 2) {
-      step(j, T{}, T{}, T{}, T{}, F{}, SA, SB, PAh, PAl, PBh, PBl);
-      step(j + 1, T{}, T{}, T{}, T{}, F{}, SB, SA, PBh, PBl, PAh, PAl);
+      step(j, T{}, T{}, T{}, T{}, F{}, SA, SB, PAh, PAl, PBh, PBl, FA, FB);
+      step(j + 1, T{}, T{}, T{}, T{}, F{}, SB, SA, PBh, PBl, PAh, PAl, FB, FA);
     }
     if (j < nfree) {
-      step(j, T{}, T{}, T{}, T{}, F{}, SA, SB, PAh, PAl, PBh, PBl);
+      step(j, T{}, T{}, T{}, T{}, F{}, SA, SB, PAh, PAl, PBh, PBl, FA, FB);
       copy_back();
       ++j;
     }
     for (; j < tl; ++j) {
-      step(j, T{}, T{}, T{}, T{}, T{}, SA, SB, PAh, PAl, PBh, PBl);
+      step(j, T{}, T{}, T{}, T{}, T{}, SA, SB, PAh, PAl, PBh, PBl, FA, FB);
       copy_back();
     }
     // last tile: no next S; P(tl) into PB, then its product
-    step(tl, T{}, T{}, F{}, T{}, T{}, SA, SB, PAh, PAl, PBh, PBl);
-    step(tl + 1, F{}, T{}, F{}, F{}, F{}, SA, SB, PBh, PBl, PAh, PAl);
+    step(tl, T{}, T{}, F{}, T{}, T{}, SA, SB, PAh, PAl, PBh, PBl, FA, FB);
+    step(tl + 1, F{}, T{}, F{}, F{}, F{}, SA, SB, PBh, PBl, PAh, PAl, FB, FA);
   } else {
-    step(t0 + 1, F{}, T{}, F{}, F{}, F{}, SA, SB, PAh, PAl, PBh, PBl);
+    step(t0 + 1, F{}, T{}, F{}, F{}, F{}, SA, SB, PAh, PAl, PBh, PBl, FA, FB);
   }
 
   // total weight of each row (the four lane groups hold different tokens)
