@@ -396,21 +396,6 @@ constexpr int kTileQB = 2;                  // q blocks of 16 rows per wave
 // running total; see the softmax step.
 constexpr float kLoShare = 0.01f;
 
-// x + a.lo + a.hi of the two 16-bit values of DT packed in a (one dot2 against
-// (1, 1); ones must hold that pair in a VGPR, see tile kernel).
-template <int DT>
-__device__ __forceinline__ float add_pair16(uint32_t a, uint32_t ones, float x) {
-  if constexpr (DT == DT_BF16) {
-    typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b16x2_t, a),
-                                           __builtin_bit_cast(b16x2_t, ones), x, false);
-  } else {
-    typedef _Float16 h16x2_t __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2_t, a), __builtin_bit_cast(h16x2_t, ones),
-                                  x, false);
-  }
-}
-
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma16(const u32x4_t a, const u32x4_t b, f32x4_t c) {
   if constexpr (DT == DT_BF16)
@@ -458,6 +443,13 @@ __device__ __forceinline__ void pair_sum(float& x) {
 __device__ __forceinline__ float max3_raw(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// max(a, b) in one instruction (no canonicalising of the operands; a quiet
+// NaN operand yields the other one).
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
 // Row max across the four lane groups (lanes n, n + 16, n + 32, n + 48).
@@ -614,18 +606,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     csel[i] = __builtin_amdgcn_readfirstlane(crow[i] >> log2E);  // entry of this wave's rows
     loff[i] = (uint32_t)((crow[i] & bmask) * rs32 + ccol[i] * CBP);
   }
-  // Block table entries of tile t: lane k the block of tokens 32 t + k min(B,
-  // 16) on (32 / min(B, 16) lanes; clamped to the last visible token, so the
+  // Block table entry of chunk i's rows in tile t: the block of token
+  // 32 t + min(B, 16) csel[i], clamped to the last visible token (so the
   // table is never read past the sequence's blocks, and a run of rows past
-  // the context finds the block of the row it is clamped to).
-  auto ent_load = [&](int t) __attribute__((always_inline)) -> int {
-    const int kv = min(t * kTileKV + ((lane << log2E) & (kTileKV - 1)), kv_end - 1);
-    return tbv[kv >> log2B];
-  };
-  // the entries of tile t's two chunk sets (chunk 0, chunk NCH - 1)
-  auto ent_pick = [&](int env, int& e0, int& e1) __attribute__((always_inline)) {
-    e0 = __builtin_amdgcn_readlane(env, csel[0]);
-    e1 = __builtin_amdgcn_readlane(env, csel[NCH - 1]);
+  // the context finds the block of the row it is clamped to).  Wave-uniform:
+  // a scalar load through the constant address space, no vector work.
+  const cint32_t* tbs = (const cint32_t*)tbv;
+  auto ent = [&](int t, int i) __attribute__((always_inline)) -> int {
+    const int kv = min(t * kTileKV + (csel[i] << log2E), kv_end - 1);
+    return tbs[kv >> log2B];
   };
   // global -> registers: the chunks of tile t (entry e0 for chunk 0, e1 for
   // chunk 1).
@@ -639,19 +628,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   auto gload = [&](Chunk (&dst)[NCH], const char* pool, int t, int e0, int e1)
       __attribute__((always_inline)) {
     const int kv0 = t * kTileKV;
-    if (kv0 + kTileKV <= kv_end) {
+    const bool full = kv0 + kTileKV <= kv_end;
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const char* base = pool + (uint64_t)(uint32_t)(i ? e1 : e0) * (uint32_t)blk_stride;
-        dst[i] = ldc(base + loff[i]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int kvc = min(kv0 + crow[i], kv_end - 1);
-        const char* base = pool + (uint64_t)(uint32_t)(i ? e1 : e0) * (uint32_t)blk_stride;
-        dst[i] = ldc(base + (uint32_t)((kvc & bmask) * rs32 + ccol[i] * CBP));
-      }
+    for (int i = 0; i < NCH; ++i) {
+      // uniform block base (scalar registers) + a 32-bit per-lane offset
+      const char* base = pool + (uint64_t)(uint32_t)(i ? e1 : e0) * (uint32_t)blk_stride;
+      uint32_t off = loff[i];
+      if (!full) off = (uint32_t)((min(kv0 + crow[i], kv_end - 1) & bmask) * rs32 + ccol[i] * CBP);
+      dst[i] = ldc(base + off);
     }
   };
   auto lstore = [&](char* buf, int pitch, const Chunk (&src)[NCH]) __attribute__((always_inline)) {
@@ -679,22 +663,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     asm volatile("" ::: "memory");
   };
 
-  f32x4_t o[NDB][QB];
+  // o[d][c]: O^T blocks of q block c; o[NDB][c]: the row sums of the weights
+  f32x4_t o[NDB + 1][QB];
 #pragma unroll
-  for (int d = 0; d < NDB; ++d)
+  for (int d = 0; d <= NDB; ++d)
 #pragma unroll
     for (int c = 0; c < QB; ++c) o[d][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m[QB], lsum[QB];
+  // running maxima (log2 units); -FLT_MAX before a row's first visible token:
+  // the first visible score always grows it, and weights are only formed
+  // from visible scores (masked ones are selected to 0)
+  float m[QB];
 #pragma unroll
-  for (int c = 0; c < QB; ++c) {
-    m[c] = -__builtin_inff();
-    lsum[c] = 0.f;
-  }
+  for (int c = 0; c < QB; ++c) m[c] = -__FLT_MAX__;
 
   // Software pipeline over KV tiles.  Step j (j = -1 .. ntiles):
   //   1. stage K(j+2) and V(j) into LDS (loaded during step j-1), then issue
   //      the loads of K(j+3) and V(j+1) and of the table entries of tile j+4;
-  //   2. matrix cores: O^T += V(j-1)^T P(j-1)^T and S(j+1)^T = K(j+1) Q^T;
+  //   2. matrix cores: O^T += V(j-1)^T P(j-1)^T (with the row sums of
+  //      P(j-1)) and S(j+1)^T = K(j+1) Q^T;
   //   3. vector ALU, independent of 2: softmax of S(j) into P(j);
   //   4. rare: rescale O when some row's max grew; barrier.
   // So the softmax of one tile runs while the matrix cores work on the tiles
@@ -704,13 +690,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   Chunk sk[NCH], sv[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) sv[i] = Chunk{};
-  int ea0, ea1, eb0, eb1, ent;  // entries of tiles j+1 and j+2; vector of tile j+3
-  {
-    const int en0 = ent_load(t0);
-    const int en1 = ent_load(min(t0 + 1, tl));
-    ent = ent_load(min(t0 + 2, tl));
-    ent_pick(en0, ea0, ea1);
-    ent_pick(en1, eb0, eb1);
+  // entries (chunk 0, chunk NCH - 1) of tiles j+1, j+2 and j+3 at step j
+  int ea0 = ent(t0, 0), ea1 = ent(t0, NCH - 1);
+  int eb0 = ent(min(t0 + 1, tl), 0), eb1 = ent(min(t0 + 1, tl), NCH - 1);
+  int en0 = ent(min(t0 + 2, tl), 0), en1 = ent(min(t0 + 2, tl), NCH - 1);
+  // The 32 bytes of skew after each V row in LDS hold 16 ones of DT (staging
+  // writes only the first D elements of a row): read as d-block NDB of V^T,
+  // they make the P.V product also sum every row's weights.
+  if (tid < 2 * kTileKV * 2) {
+    const uint32_t one2 = DT == DT_BF16 ? 0x3f803f80u : 0x3c003c00u;
+    *reinterpret_cast<uint4*>(lv[tid >> 6] + ((tid >> 1) & 31) * VP + D * ES + (tid & 1) * 16) =
+        make_uint4(one2, one2, one2, one2);
   }
   gload(sk, kpool, t0, ea0, ea1);
   lstore(lk[t0 & 1], KP, sk);
@@ -720,11 +710,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   f32x4_t SA[2][QB], SB[2][QB];   // S of the tile being softmaxed / of the next one
   u32x4_t PAh[QB], PAl[QB], PBh[QB], PBl[QB];  // P of the previous tile / of this one
   bool FA = false, FB = false;   // whether that P has its lo parts (uniform)
-  // (1, 1) in DT, as a VGPR: as an inline constant the compiler would encode
-  // the 32-bit word as a float constant with different half words
-  uint32_t ones;
-  if constexpr (DT == DT_BF16) asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(ones));
-  else asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(ones));
 
   auto step = [&](const int j, auto ld_tag, auto pv_tag, auto qk_tag, auto sm_tag, auto mask_tag,
                   f32x4_t (&s_cur)[2][QB], f32x4_t (&s_nxt)[2][QB], const u32x4_t (&pph)[QB],
@@ -739,9 +724,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if constexpr (LD) {
       lstore(lk[j & 1], KP, sk);
       lstore(lv[j & 1], VP, sv);
-      int ec0, ec1;
-      ent_pick(ent, ec0, ec1);
-      ent = ent_load(min(j + 4, tl));
+      const int ec0 = en0, ec1 = en1;
+      en0 = ent(min(j + 4, tl), 0);
+      en1 = ent(min(j + 4, tl), NCH - 1);
       gload(sk, kpool, min(j + 3, tl), ec0, ec1);
       gload(sv, vpool, min(j + 1, tl), ea0, ea1);
       ea0 = eb0;
@@ -749,51 +734,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       eb0 = ec0;
       eb1 = ec1;
     }
+    // K fragments of tile j+1, read before the P.V products are issued so
+    // their LDS latency hides behind them (1.116 -> 1.072 ms on 8 x 512
+    // chunks, against reading each pair right before its two products)
+    u32x4_t kfr[2][NKK];
     if constexpr (QK) {
-      // S^T blocks: s_nxt[mb][c] holds S[16 mb + 4 g4 + i][q col n of block c]
       const char* K = lk[(j + 1) & 1];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int c = 0; c < QB; ++c) s_nxt[mb][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const u32x4_t ka = as_v(*reinterpret_cast<const uint4*>(K + (16 * mb + n) * KP + 64 * kk + 16 * g4));
-#pragma unroll
-          for (int c = 0; c < QB; ++c) s_nxt[mb][c] = mfma16<DT>(ka, qf[c][kk], s_nxt[mb][c]);
-        }
-      }
+        for (int kk = 0; kk < NKK; ++kk)
+          kfr[mb][kk] = as_v(*reinterpret_cast<const uint4*>(K + (16 * mb + n) * KP + 64 * kk + 16 * g4));
     }
-    if constexpr (PV) {
-      // O^T += V^T P^T: A = V^T rows d0 + n, tokens 4 g4 + k and 16 + 4 g4 + k
-      const char* V = lv[(j - 1) & 1];
+    // O^T += V^T P^T over the D columns of V and a block of ones (the LDS
+    // rows' skew, see below), so o[NDB][c] holds every row's sum of its
+    // weights as they entered the product.  A = V^T rows 16 d + n, tokens
+    // 4 g4 + k and 16 + 4 g4 + k.
+    const char* V = lv[(j - 1) & 1];
+    auto pv_pass = [&](const u32x4_t (&pp)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) {
+      for (int d = 0; d <= NDB; ++d) {
         const char* vp = V + (4 * g4 + (n >> 2)) * VP + (16 * d + 4 * (n & 3)) * ES;
         const uint2 lo = lds_read_tr16(vp);
         const uint2 hi = lds_read_tr16(vp + 16 * VP);
         const u32x4_t va = u32x4_t{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-        for (int c = 0; c < QB; ++c) o[d][c] = mfma16<DT>(va, pph[c], o[d][c]);
+        for (int c = 0; c < QB; ++c) o[d][c] = mfma16<DT>(va, pp[c], o[d][c]);
       }
-      if (pflag) {  // the lo parts of P(j-1): a second pass over the same V tile
+    };
+    // each row's total weight through P(j-2) (P(j-1) is added below)
+    float lprev[QB];
+    if constexpr (SM) {
 #pragma unroll
-        for (int d = 0; d < NDB; ++d) {
-          const char* vp = V + (4 * g4 + (n >> 2)) * VP + (16 * d + 4 * (n & 3)) * ES;
-          const uint2 lo = lds_read_tr16(vp);
-          const uint2 hi = lds_read_tr16(vp + 16 * VP);
-          const u32x4_t va = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+      for (int c = 0; c < QB; ++c) lprev[c] = o[NDB][c][0];
+    }
+    if constexpr (PV) pv_pass(pph);
+    if constexpr (QK) {
+      // S^T blocks: s_nxt[mb][c] holds S[16 mb + 4 g4 + i][q col n of block c]
 #pragma unroll
-          for (int c = 0; c < QB; ++c) o[d][c] = mfma16<DT>(va, ppl[c], o[d][c]);
-        }
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int c = 0; c < QB; ++c) s_nxt[mb][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+          for (int c = 0; c < QB; ++c) s_nxt[mb][c] = mfma16<DT>(kfr[mb][kk], qf[c][kk], s_nxt[mb][c]);
       }
     }
+    bool grow[QB], grow_any = false, need_lo = false;
+    float mold[QB], pk[QB][8];  // previous maxima; this tile's weights (for their lo parts)
     if constexpr (SM) {
       const int kv0 = j * kTileKV;
-      float alpha[QB];
-      bool grow_any = false;
-      bool need_lo = false;
-      float pk[QB][8];  // this tile's weights (kept for their lo parts)
 #pragma unroll
       for (int c = 0; c < QB; ++c) {
         float r[8];
@@ -807,13 +798,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           }
         const float t = group_max_raw(
             max3_raw(max3_raw(r[0], r[1], r[2]), max3_raw(r[3], r[4], r[5]), max3_raw(r[6], r[7], r[7])));
-        const float mn = fmaxf(m[c], t * sl);
-        const bool grow = mn > m[c] + kRescaleThreshold;
-        alpha[c] = grow ? fast_exp2(m[c] - mn) : 1.f;
-        m[c] = grow ? mn : m[c];
-        grow_any |= grow;
-        const float mu = m[c] == -__builtin_inff() ? 0.f : m[c];
-        float rs = 0.f;
+        const float mn = max_raw(m[c], t * sl);  // t * sl: NaN only when all masked and scale 0
+        grow[c] = mn > m[c] + kRescaleThreshold;
+        mold[c] = m[c];
+        m[c] = grow[c] ? mn : m[c];
+        grow_any |= grow[c];
+        const float mu = m[c];
         uint32_t hw[4];
 #pragma unroll
         for (int k = 0; k < 8; k += 2) {
@@ -826,54 +816,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           }
           pk[c][k] = p0;
           pk[c][k + 1] = p1;
-          const uint32_t h = pack2<DT>(p0, p1);
-          hw[k / 2] = h;
-          rs = add_pair16<DT>(h, ones, rs);  // the sum of the weights as rounded
+          hw[k / 2] = pack2<DT>(p0, p1);
         }
         nph[c] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-        lsum[c] = lsum[c] * alpha[c] + rs;
         if constexpr (PSPLIT) {
           // Rounding a weight w to 16 bits moves the row's result by about
-          // w * eps * (v - o) / total weight (the total is a sum of the same
+          // w * eps * (v - o) / total weight (the total is the sum of the same
           // rounded weights, so a dominant weight's rounding cancels).  Where
           // the largest weight of every row is at most kLoShare of the row's
-          // total so far (the final total is larger still), the result moves
-          // by far less than the tolerance and the lo parts are skipped; else
-          // this tile carries them (about 16 significant bits per weight).
-          float lrow = lsum[c];
-          pair_sum<16>(lrow);
-          pair_sum<32>(lrow);
+          // total (a lower bound of it: the total two tiles back), the result
+          // moves by far less than the tolerance and the lo parts are
+          // skipped; else this tile carries them (about 16 significant bits
+          // per weight).  A grown maximum (a new dominant token) always does.
           const float pmax = fast_exp2(__builtin_fmaf(t, sl, -mu));  // 0 (or NaN) if all masked
-          need_lo |= pmax > kLoShare * lrow;
+          need_lo |= grow[c] || pmax > kLoShare * lprev[c];
         }
       }
-      // keep the weights' computation here, beside the matrix-core work it
-      // overlaps (else it sinks past the rescale branch below)
-#pragma unroll
-      for (int c = 0; c < QB; ++c) asm volatile("" ::"v"(nph[c]), "v"(lsum[c]));
+    }
+    // the lo parts of P(j-1): a second pass over the same V tile
+    if constexpr (PV) {
+      if (pflag) pv_pass(ppl);
+    }
+    if constexpr (SM) {
       nflag = PSPLIT && __builtin_amdgcn_ballot_w64(need_lo) != 0;
       if (nflag) {
 #pragma unroll
         for (int c = 0; c < QB; ++c) {
           uint32_t lw[4];
-          float rl = 0.f;
 #pragma unroll
           for (int k = 0; k < 8; k += 2) {
             const uint32_t h = nph[c][k / 2];
             lw[k / 2] = pack2<DT>(residual16<DT, 0>(pk[c][k], h), residual16<DT, 1>(pk[c][k + 1], h));
-            rl = add_pair16<DT>(lw[k / 2], ones, rl);
           }
           npl[c] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
-          lsum[c] += rl;
-          asm volatile("" ::"v"(npl[c]), "v"(lsum[c]));
         }
       }
-      // O now includes P(j-1) V(j-1): bring it to the new max
+      // O now includes P(j-1) V(j-1): bring it (and the row sums) to the new max
       if (__builtin_amdgcn_ballot_w64(grow_any)) {
 #pragma unroll
-        for (int d = 0; d < NDB; ++d)
+        for (int c = 0; c < QB; ++c) {
+          const float alpha = grow[c] ? fast_exp2(mold[c] - m[c]) : 1.f;
 #pragma unroll
-          for (int c = 0; c < QB; ++c) o[d][c] *= alpha[c];
+          for (int d = 0; d <= NDB; ++d) o[d][c] *= alpha;
+        }
       }
     }
     if constexpr (LD) lds_barrier();
@@ -919,12 +904,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     step(t0 + 1, F{}, T{}, F{}, F{}, F{}, SA, SB, PAh, PAl, PBh, PBl, FA, FB);
   }
 
-  // total weight of each row (the four lane groups hold different tokens)
+  // total weight of each row: the ones block of O (in every lane of the row)
+  float lsum[QB];
 #pragma unroll
-  for (int c = 0; c < QB; ++c) {
-    pair_sum<16>(lsum[c]);
-    pair_sum<32>(lsum[c]);
-  }
+  for (int c = 0; c < QB; ++c) lsum[c] = o[NDB][c][0];
   if (partial) {
     // unnormalised output, running max and weight sum of this split
     const int64_t rec = (int64_t)sp * a.Tq * a.Hq;
