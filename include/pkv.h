@@ -83,7 +83,8 @@ const char* pkv_version(void);
  *   k_cache,
  *   v_cache      : device pools [NB, B, Hkv, D] of kv_dtype, written in place
  *   slot_mapping : device int64 [T]; slot < 0 means "skip this token"
- *                  (padding); otherwise 0 <= slot < NB * B
+ *                  (padding); a slot at or beyond NB * B is skipped too (no
+ *                  write outside the pools), otherwise 0 <= slot < NB * B
  * Bytes are copied unchanged (bit-exact).  T == 0 is a no-op.
  * ------------------------------------------------------------------------ */
 pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,

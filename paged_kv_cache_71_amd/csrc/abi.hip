@@ -54,6 +54,60 @@ using namespace pkv;
     if (!(cond)) return fail(status, __VA_ARGS__); \
   } while (0)
 
+namespace pkv {
+
+// A cache write's arguments (both reshape entry points).
+// fp8: the pools hold E4M3 codes and key/value (of in_dtype) are quantized
+// with the per-head scales; else the pools and key/value are of in_dtype.
+struct CacheWrite {
+  const void* key;
+  const void* value;
+  const int64_t* slot_mapping;
+  int32_t T;
+  int64_t NB;
+  pkv_dtype in_dtype;
+  bool fp8;
+  const float* k_scale;
+  const float* v_scale;
+};
+
+static pkv_status check_cache_write(const char* who, const CacheWrite& cw, const void* k_cache,
+                                    const void* v_cache, int32_t Hkv, int32_t D, int32_t B) {
+  PKV_REQUIRE(cw.T >= 0, PKV_ERR_INVALID_ARG, "%s: T = %d", who, cw.T);
+  PKV_REQUIRE(Hkv > 0 && D > 0 && B > 0 && cw.NB > 0, PKV_ERR_INVALID_ARG,
+              "%s: Hkv=%d D=%d B=%d NB=%lld must be positive", who, Hkv, D, B, (long long)cw.NB);
+  PKV_REQUIRE(supported_dtype(cw.in_dtype), PKV_ERR_UNSUPPORTED, "%s: dtype %d", who,
+              (int)cw.in_dtype);
+  PKV_REQUIRE(supported_head_dim(D), PKV_ERR_UNSUPPORTED, "%s: head_dim %d", who, D);
+  PKV_REQUIRE(supported_block(B), PKV_ERR_UNSUPPORTED, "%s: block_size %d", who, B);
+  PKV_REQUIRE(cw.NB <= INT64_MAX / B, PKV_ERR_INVALID_ARG, "%s: NB x B overflows", who);
+  if (cw.T == 0) return PKV_OK;
+  PKV_REQUIRE(cw.key && cw.value && k_cache && v_cache && cw.slot_mapping &&
+                  (!cw.fp8 || (cw.k_scale && cw.v_scale)),
+              PKV_ERR_INVALID_ARG, "%s: null pointer", who);
+  PKV_REQUIRE(aligned(cw.key, 16) && aligned(cw.value, 16) && aligned(k_cache, 16) &&
+                  aligned(v_cache, 16) && aligned(cw.slot_mapping, 8) && aligned(cw.k_scale, 4) &&
+                  aligned(cw.v_scale, 4),
+              PKV_ERR_INVALID_ARG,
+              "%s: key, value and the pools must be 16-byte aligned, slot_mapping 8-byte, the "
+              "scales 4-byte aligned", who);
+  return PKV_OK;
+}
+
+// (checked arguments) the write's launch
+static pkv_status launch_cache_write(const CacheWrite& cw, void* k_cache, void* v_cache,
+                                     int32_t Hkv, int32_t D, int32_t B, hipStream_t stream) {
+  const int64_t nslots = cw.NB * B;
+  if (cw.fp8)
+    return launch_reshape_and_cache_fp8(cw.key, cw.value, cw.in_dtype, k_cache, v_cache,
+                                        cw.slot_mapping, cw.T, Hkv, D, nslots, cw.k_scale,
+                                        cw.v_scale, stream);
+  return launch_reshape_and_cache(cw.key, cw.value, k_cache, v_cache, cw.slot_mapping, cw.T,
+                                  (int64_t)Hkv * D * dt_bytes(cw.in_dtype), nslots, stream);
+}
+
+}  // namespace pkv
+
 extern "C" {
 
 const char* pkv_status_string(pkv_status s) {
@@ -76,25 +130,10 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
                                  const int64_t* slot_mapping, int32_t T, int32_t Hkv, int32_t D,
                                  int32_t B, int64_t NB, pkv_dtype kv_dtype, void* stream) {
   g_last_error[0] = 0;
-  PKV_REQUIRE(T >= 0, PKV_ERR_INVALID_ARG, "reshape_and_cache: T = %d", T);
-  PKV_REQUIRE(Hkv > 0 && D > 0 && B > 0 && NB > 0, PKV_ERR_INVALID_ARG,
-              "reshape_and_cache: Hkv=%d D=%d B=%d NB=%lld must be positive", Hkv, D, B,
-              (long long)NB);
-  PKV_REQUIRE(supported_dtype(kv_dtype), PKV_ERR_UNSUPPORTED, "reshape_and_cache: dtype %d",
-              (int)kv_dtype);
-  PKV_REQUIRE(supported_head_dim(D), PKV_ERR_UNSUPPORTED, "reshape_and_cache: head_dim %d", D);
-  PKV_REQUIRE(supported_block(B), PKV_ERR_UNSUPPORTED, "reshape_and_cache: block_size %d", B);
-  if (T == 0) return PKV_OK;
-  PKV_REQUIRE(key && value && k_cache && v_cache && slot_mapping, PKV_ERR_INVALID_ARG,
-              "reshape_and_cache: null pointer");
-  PKV_REQUIRE(aligned(key, 16) && aligned(value, 16) && aligned(k_cache, 16) &&
-                  aligned(v_cache, 16) && aligned(slot_mapping, 8),
-              PKV_ERR_INVALID_ARG,
-              "reshape_and_cache: key, value and the pools must be 16-byte aligned, slot_mapping "
-              "8-byte aligned");
-  const int64_t row_bytes = (int64_t)Hkv * D * dt_bytes(kv_dtype);
-  return launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, T, row_bytes, B,
-                                  static_cast<hipStream_t>(stream));
+  const pkv::CacheWrite cw{key, value, slot_mapping, T, NB, kv_dtype, false, nullptr, nullptr};
+  const pkv_status st = pkv::check_cache_write("reshape_and_cache", cw, k_cache, v_cache, Hkv, D, B);
+  if (st != PKV_OK) return st;
+  return pkv::launch_cache_write(cw, k_cache, v_cache, Hkv, D, B, static_cast<hipStream_t>(stream));
 }
 
 pkv_status pkv_reshape_and_cache_fp8(const void* key, const void* value, pkv_dtype in_dtype,
@@ -102,25 +141,11 @@ pkv_status pkv_reshape_and_cache_fp8(const void* key, const void* value, pkv_dty
                                      int32_t T, int32_t Hkv, int32_t D, int32_t B, int64_t NB,
                                      const float* k_scale, const float* v_scale, void* stream) {
   g_last_error[0] = 0;
-  PKV_REQUIRE(T >= 0, PKV_ERR_INVALID_ARG, "reshape_and_cache_fp8: T = %d", T);
-  PKV_REQUIRE(Hkv > 0 && D > 0 && B > 0 && NB > 0, PKV_ERR_INVALID_ARG,
-              "reshape_and_cache_fp8: Hkv=%d D=%d B=%d NB=%lld must be positive", Hkv, D, B,
-              (long long)NB);
-  PKV_REQUIRE(supported_dtype(in_dtype), PKV_ERR_UNSUPPORTED,
-              "reshape_and_cache_fp8: input dtype %d", (int)in_dtype);
-  PKV_REQUIRE(supported_head_dim(D), PKV_ERR_UNSUPPORTED, "reshape_and_cache_fp8: head_dim %d", D);
-  PKV_REQUIRE(supported_block(B), PKV_ERR_UNSUPPORTED, "reshape_and_cache_fp8: block_size %d", B);
-  if (T == 0) return PKV_OK;
-  PKV_REQUIRE(key && value && k_cache && v_cache && slot_mapping && k_scale && v_scale,
-              PKV_ERR_INVALID_ARG, "reshape_and_cache_fp8: null pointer");
-  PKV_REQUIRE(aligned(key, 16) && aligned(value, 16) && aligned(k_cache, 16) &&
-                  aligned(v_cache, 16) && aligned(slot_mapping, 8) && aligned(k_scale, 4) &&
-                  aligned(v_scale, 4),
-              PKV_ERR_INVALID_ARG,
-              "reshape_and_cache_fp8: key, value and the pools must be 16-byte aligned, "
-              "slot_mapping 8-byte, the scales 4-byte aligned");
-  return launch_reshape_and_cache_fp8(key, value, in_dtype, k_cache, v_cache, slot_mapping, T, Hkv,
-                                      D, k_scale, v_scale, static_cast<hipStream_t>(stream));
+  const pkv::CacheWrite cw{key, value, slot_mapping, T, NB, in_dtype, true, k_scale, v_scale};
+  const pkv_status st =
+      pkv::check_cache_write("reshape_and_cache_fp8", cw, k_cache, v_cache, Hkv, D, B);
+  if (st != PKV_OK) return st;
+  return pkv::launch_cache_write(cw, k_cache, v_cache, Hkv, D, B, static_cast<hipStream_t>(stream));
 }
 
 pkv_status pkv_decode_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,

@@ -28,24 +28,49 @@ namespace pkv {
 namespace {
 
 constexpr int kCopyThreads = 256;
+constexpr int kTokensPerGroup = kCopyThreads / 64;  // reshape: one wave per token
 
-// One workgroup per token; thread i copies 16-byte chunks i, i+256, ... of the
-// token's K row and V row.  Negative slots (padding) are skipped.
+// One wave per token, four tokens per workgroup; lane i copies the 16-byte
+// chunks i, i + 64, ... of the token's K row and V row (a bf16 row of 8 heads
+// x 128 is 128 chunks: two of K and two of V per lane, all four loads in
+// flight together).  The row's first chunks are loaded without waiting for
+// the slot (the loads do not depend on it); tokens whose slot lies outside
+// [0, nslots) -- negative slots are padding -- store nothing.
 __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_kernel(
     const uint4* __restrict__ key, const uint4* __restrict__ value, uint4* __restrict__ k_cache,
-    uint4* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int64_t row_chunks) {
-  const int64_t t = blockIdx.x;
+    uint4* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int32_t T,
+    int64_t nslots, int32_t row_chunks) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t t = (int64_t)blockIdx.x * kTokensPerGroup + wave;
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
   const int64_t slot = slot_mapping[t];
-  if (slot < 0) return;
+  const bool keep = slot >= 0 && slot < nslots;
   const uint4* ks = key + t * row_chunks;
   const uint4* vs = value + t * row_chunks;
   uint4* kd = k_cache + slot * row_chunks;
   uint4* vd = v_cache + slot * row_chunks;
-  for (int64_t i = threadIdx.x; i < row_chunks; i += kCopyThreads) {
-    const uint4 kk = ks[i];
-    const uint4 vv = vs[i];
-    kd[i] = kk;
-    vd[i] = vv;
+  for (int i0 = 0; i0 < row_chunks; i0 += 128) {
+    const int i1 = i0 + lane, i2 = i1 + 64;
+    uint4 k1{}, v1{}, k2{}, v2{};
+    if (i1 < row_chunks) {
+      k1 = ks[i1];
+      v1 = vs[i1];
+    }
+    if (i2 < row_chunks) {
+      k2 = ks[i2];
+      v2 = vs[i2];
+    }
+    if (keep) {
+      if (i1 < row_chunks) {
+        kd[i1] = k1;
+        vd[i1] = v1;
+      }
+      if (i2 < row_chunks) {
+        kd[i2] = k2;
+        vd[i2] = v2;
+      }
+    }
   }
 }
 
@@ -70,42 +95,67 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
   return sign | (r - (120u << 3));
 }
 
+// the 8 elements e0 .. e0 + 7 of row as fp32 (e0 a multiple of 8; 16-byte
+// aligned: one 16-byte load for 16-bit inputs, two for f32)
 template <int IDT>
-__device__ __forceinline__ float elem_f32(const void* row, int64_t i) {
-  if constexpr (IDT == DT_F32) return static_cast<const float*>(row)[i];
-  else if constexpr (IDT == DT_BF16)
-    return __uint_as_float((uint32_t) static_cast<const uint16_t*>(row)[i] << 16);
-  else return (float)__builtin_bit_cast(_Float16, static_cast<const uint16_t*>(row)[i]);
+__device__ __forceinline__ void load8_f32(const void* row, int64_t e0, float (&x)[8]) {
+  if constexpr (IDT == DT_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(row) + e0);
+    const float4 a = p[0], b = p[1];
+    x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w, x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
+  } else {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + e0);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (IDT == DT_BF16) {
+        x[2 * j] = __uint_as_float(w[j] << 16);
+        x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+      } else {
+        x[2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] & 0xffffu));
+        x[2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] >> 16));
+      }
+    }
+  }
 }
 
-// One workgroup per token; thread i quantizes 8-element groups i, i+256, ...
-// of the token's K row and V row (one group = 8 code bytes, one 8-byte store;
-// D is a multiple of 8, so a group lies in one KV head).
+// One wave per token, four tokens per workgroup; lane i quantizes the
+// 8-element groups i, i + 64, ... of the token's K row and V row (one group =
+// one 16-byte load of a 16-bit input, 8 code bytes, one 8-byte store; D is a
+// multiple of 8, so a group lies in one KV head).  Slots as in the copy above.
 template <int IDT>
 __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_fp8_kernel(
     const void* __restrict__ key, const void* __restrict__ value, uint8_t* __restrict__ k_cache,
-    uint8_t* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping,
-    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int32_t Hkv,
-    int32_t D) {
-  const int64_t t = blockIdx.x;
+    uint8_t* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int32_t T,
+    int64_t nslots, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    int32_t Hkv, int32_t D) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t t = (int64_t)blockIdx.x * kTokensPerGroup + wave;
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
   const int64_t slot = slot_mapping[t];
-  if (slot < 0) return;
+  const bool keep = slot >= 0 && slot < nslots;
   const int64_t row = (int64_t)Hkv * D;
-  const int64_t ngroups = row / 8;
-  for (int64_t gi = threadIdx.x; gi < ngroups; gi += kCopyThreads) {
-    const int64_t e0 = gi * 8;
+  const int ngroups = (int)(row / 8);
+  const char* krow = static_cast<const char*>(key) + t * row * dt_bytes(IDT);
+  const char* vrow = static_cast<const char*>(value) + t * row * dt_bytes(IDT);
+  for (int gi = lane; gi < ngroups; gi += 64) {
+    const int64_t e0 = (int64_t)gi * 8;
+    float kx[8], vx[8];
+    load8_f32<IDT>(krow, e0, kx);
+    load8_f32<IDT>(vrow, e0, vx);
     const int h = (int)(e0 / D);
     const float ks = k_scale[h], vs = v_scale[h];
     uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float kx = elem_f32<IDT>(key, t * row + e0 + j) / ks;
-      const float vx = elem_f32<IDT>(value, t * row + e0 + j) / vs;
-      kw[j >> 2] |= e4m3_code(kx) << (8 * (j & 3));
-      vw[j >> 2] |= e4m3_code(vx) << (8 * (j & 3));
+      kw[j >> 2] |= e4m3_code(kx[j] / ks) << (8 * (j & 3));
+      vw[j >> 2] |= e4m3_code(vx[j] / vs) << (8 * (j & 3));
     }
-    *reinterpret_cast<uint2*>(k_cache + slot * row + e0) = make_uint2(kw[0], kw[1]);
-    *reinterpret_cast<uint2*>(v_cache + slot * row + e0) = make_uint2(vw[0], vw[1]);
+    if (keep) {
+      *reinterpret_cast<uint2*>(k_cache + slot * row + e0) = make_uint2(kw[0], kw[1]);
+      *reinterpret_cast<uint2*>(v_cache + slot * row + e0) = make_uint2(vw[0], vw[1]);
+    }
   }
 }
 
@@ -184,36 +234,43 @@ pkv_status launch_swap_blocks(const void* const* src_pools, void* const* dst_poo
   return PKV_OK;
 }
 
+// workgroups of a reshape launch: one per kTokensPerGroup tokens
+static unsigned reshape_grid(int32_t T) {
+  return (unsigned)(((int64_t)T + kTokensPerGroup - 1) / kTokensPerGroup);
+}
+
 pkv_status launch_reshape_and_cache(const void* key, const void* value, void* k_cache,
                                     void* v_cache, const int64_t* slot_mapping, int32_t T,
-                                    int64_t row_bytes, int32_t /*B*/, hipStream_t stream) {
+                                    int64_t row_bytes, int64_t nslots, hipStream_t stream) {
   if (T == 0) return PKV_OK;
-  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(T), dim3(kCopyThreads), 0, stream,
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(reshape_grid(T)), dim3(kCopyThreads), 0, stream,
                      static_cast<const uint4*>(key), static_cast<const uint4*>(value),
-                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), slot_mapping,
-                     row_bytes / 16);
+                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), slot_mapping, T,
+                     nslots, (int32_t)(row_bytes / 16));
   return check_launch("reshape_and_cache");
 }
 
 pkv_status launch_reshape_and_cache_fp8(const void* key, const void* value, int in_dt,
                                         void* k_cache, void* v_cache, const int64_t* slot_mapping,
-                                        int32_t T, int32_t Hkv, int32_t D, const float* k_scale,
-                                        const float* v_scale, hipStream_t stream) {
+                                        int32_t T, int32_t Hkv, int32_t D, int64_t nslots,
+                                        const float* k_scale, const float* v_scale,
+                                        hipStream_t stream) {
   if (T == 0) return PKV_OK;
+  const dim3 grid(reshape_grid(T));
   uint8_t* kc = static_cast<uint8_t*>(k_cache);
   uint8_t* vc = static_cast<uint8_t*>(v_cache);
   switch (in_dt) {
     case DT_F32:
-      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DT_F32>, dim3(T), dim3(kCopyThreads), 0,
-                         stream, key, value, kc, vc, slot_mapping, k_scale, v_scale, Hkv, D);
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DT_F32>, grid, dim3(kCopyThreads), 0, stream,
+                         key, value, kc, vc, slot_mapping, T, nslots, k_scale, v_scale, Hkv, D);
       break;
     case DT_F16:
-      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DT_F16>, dim3(T), dim3(kCopyThreads), 0,
-                         stream, key, value, kc, vc, slot_mapping, k_scale, v_scale, Hkv, D);
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DT_F16>, grid, dim3(kCopyThreads), 0, stream,
+                         key, value, kc, vc, slot_mapping, T, nslots, k_scale, v_scale, Hkv, D);
       break;
     case DT_BF16:
-      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DT_BF16>, dim3(T), dim3(kCopyThreads), 0,
-                         stream, key, value, kc, vc, slot_mapping, k_scale, v_scale, Hkv, D);
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DT_BF16>, grid, dim3(kCopyThreads), 0, stream,
+                         key, value, kc, vc, slot_mapping, T, nslots, k_scale, v_scale, Hkv, D);
       break;
     default:
       return fail(PKV_ERR_UNSUPPORTED, "reshape_and_cache_fp8: input dtype %d", in_dt);

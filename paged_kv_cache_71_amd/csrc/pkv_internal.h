@@ -94,14 +94,16 @@ __device__ __forceinline__ void store_out_vec(void* out, int out_dt, int64_t idx
 }
 
 // ---- launchers (one per kernel family) -------------------------------------------
+// nslots = NB * B: tokens with a slot outside [0, nslots) are skipped
 pkv_status launch_reshape_and_cache(const void* key, const void* value, void* k_cache,
                                     void* v_cache, const int64_t* slot_mapping, int32_t T,
-                                    int64_t row_bytes, int32_t B, hipStream_t stream);
+                                    int64_t row_bytes, int64_t nslots, hipStream_t stream);
 
 pkv_status launch_reshape_and_cache_fp8(const void* key, const void* value, int in_dt,
                                         void* k_cache, void* v_cache, const int64_t* slot_mapping,
-                                        int32_t T, int32_t Hkv, int32_t D, const float* k_scale,
-                                        const float* v_scale, hipStream_t stream);
+                                        int32_t T, int32_t Hkv, int32_t D, int64_t nslots,
+                                        const float* k_scale, const float* v_scale,
+                                        hipStream_t stream);
 
 pkv_status launch_swap_blocks(const void* const* src_pools, void* const* dst_pools,
                               int32_t num_pools, const int64_t* pairs, int32_t N,

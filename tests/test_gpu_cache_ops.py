@@ -38,6 +38,55 @@ def test_reshape_and_cache_bit_exact(gpu_lib, dtype, D, B, Hkv):
     assert to_host_bits(vc).tobytes() == v_ref.tobytes()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_reshape_and_cache_skips_slots_outside_the_pool(gpu_lib, dtype):
+    """Slots at or beyond NB * B are skipped like padding: nothing is written
+    outside the pools, and the in-range tokens land as usual."""
+    rng = np.random.default_rng(3)
+    NB, B, Hkv, D, T = 20, 16, 2, 64, 40
+    k0, v0 = _rand_bits(rng, (NB, B, Hkv, D), dtype), _rand_bits(rng, (NB, B, Hkv, D), dtype)
+    key, val = _rand_bits(rng, (T, Hkv, D), dtype), _rand_bits(rng, (T, Hkv, D), dtype)
+    slots = rng.permutation(NB * B)[:T].astype(np.int64)
+    slots[[0, 7, 19]] = [NB * B, NB * B + 1, 1 << 40]
+    slots[5] = -3
+    # pools with a guard block on each side, to see any write outside them
+    kg = to_dev(np.concatenate([k0[:1], k0, k0[:1]]), dtype)
+    vg = to_dev(np.concatenate([v0[:1], v0, v0[:1]]), dtype)
+    gpu_lib.reshape_and_cache(to_dev(key, dtype), to_dev(val, dtype), kg[1:NB + 1], vg[1:NB + 1],
+                              torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    keep = (slots >= 0) & (slots < NB * B)
+    k_ref, v_ref = k0.copy(), v0.copy()
+    oracle.reshape_and_cache(key[keep], val[keep], k_ref, v_ref, slots[keep], dtype)
+    kh, vh = to_host_bits(kg), to_host_bits(vg)
+    assert kh[1:NB + 1].tobytes() == k_ref.tobytes() and vh[1:NB + 1].tobytes() == v_ref.tobytes()
+    assert kh[0].tobytes() == k0[0].tobytes() and kh[NB + 1].tobytes() == k0[0].tobytes()
+    assert vh[0].tobytes() == v0[0].tobytes() and vh[NB + 1].tobytes() == v0[0].tobytes()
+
+
+def test_reshape_and_cache_fp8_skips_slots_outside_the_pool(gpu_lib):
+    rng = np.random.default_rng(4)
+    NB, B, Hkv, D, T = 20, 16, 2, 128, 40
+    k0 = W.fp8_codes(rng, (NB + 2, B, Hkv, D))
+    v0 = W.fp8_codes(rng, (NB + 2, B, Hkv, D))
+    key = W.to_storage(rng.standard_normal((T, Hkv, D), dtype=np.float32), "bf16")
+    val = W.to_storage(rng.standard_normal((T, Hkv, D), dtype=np.float32), "bf16")
+    ks = rng.uniform(0.004, 0.02, Hkv).astype(np.float32)
+    vs = rng.uniform(0.004, 0.02, Hkv).astype(np.float32)
+    slots = rng.permutation(NB * B)[:T].astype(np.int64)
+    slots[[1, 8, 30]] = [NB * B, NB * B + 7, 1 << 41]
+    kg, vg = torch.from_numpy(k0.copy()).cuda(), torch.from_numpy(v0.copy()).cuda()
+    gpu_lib.reshape_and_cache_fp8(to_dev(key, "bf16"), to_dev(val, "bf16"), kg[1:NB + 1],
+                                  vg[1:NB + 1], torch.from_numpy(slots).cuda(),
+                                  torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda())
+    torch.cuda.synchronize()
+    keep = slots < NB * B
+    k_ref, v_ref = k0.copy(), v0.copy()
+    oracle.reshape_and_cache_fp8(key[keep], val[keep], "bf16", k_ref[1:NB + 1], v_ref[1:NB + 1],
+                                 slots[keep], ks, vs)
+    assert np.array_equal(kg.cpu().numpy(), k_ref) and np.array_equal(vg.cpu().numpy(), v_ref)
+
+
 def test_reshape_and_cache_decode_step_tokens(gpu_lib):
     """The decode step's new tokens of a Llama-3-8B-shaped batch."""
     b = W.llama3_8b_bf16(1, S=20, NB=4000)

@@ -19,7 +19,7 @@ from test_gpu_cascade import check as check_cascade
 from test_gpu_cascade import gpu_cascade
 from test_gpu_decode import check as check_decode
 from test_gpu_decode import gpu_decode
-from test_gpu_fp8 import Fp8Dev
+from gpu_util import Fp8Dev
 from test_gpu_fp8 import check as check_decode_fp8
 from test_gpu_fp8 import check_prefill as check_prefill_fp8
 from test_gpu_fp8 import oracle_decode as oracle_decode_fp8
