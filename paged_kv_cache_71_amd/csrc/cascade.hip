@@ -44,7 +44,11 @@ struct CascadeLayout {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// One workgroup per group g.
+constexpr int kGatherSplit = 8;  // workgroups per group for the query copy
+
+// grid = (groups, kGatherSplit): workgroup (g, y) copies every kGatherSplit-th
+// stretch of group g's query rows; y = 0 also writes the group's prefix
+// length, its table and its members' suffix starts and group index.
 __global__ __launch_bounds__(kThreads) void cascade_gather_kernel(
     const char* __restrict__ q, const int32_t* __restrict__ cu, const int32_t* __restrict__ plen,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ context_lens, int32_t max_nb,
@@ -55,17 +59,13 @@ __global__ __launch_bounds__(kThreads) void cascade_gather_kernel(
   const int s0 = cu[g];
   const int n = cu[g + 1] - s0;
   if (n <= 0) {  // empty group: nothing of it is ever read
-    if (threadIdx.x == 0) plens[g] = 0;
+    if (threadIdx.x == 0 && blockIdx.y == 0) plens[g] = 0;
     return;
   }
-  // the prefix never exceeds any member's context nor the host bound
-  int P = min(max(plen[g], 0), max_prefix);
-  for (int m = 0; m < n; ++m) P = min(P, max(context_lens[s0 + m], 0));
-  P = (P / B) * B;
   const int G = Hq / Hkv;
   const int chunks = D * es / 16;  // 16-byte chunks per query row
   const int rows = Hkv * NM * G;
-  for (int i = threadIdx.x; i < rows * chunks; i += kThreads) {
+  for (int i = blockIdx.y * kThreads + threadIdx.x; i < rows * chunks; i += kGatherSplit * kThreads) {
     const int r = i / chunks, c = i - r * chunks;
     const int kvh = r / (NM * G);
     const int m = (r / G) % NM;
@@ -76,6 +76,11 @@ __global__ __launch_bounds__(kThreads) void cascade_gather_kernel(
     uint4* dst = reinterpret_cast<uint4*>(qg + (((int64_t)g * rows + r) * D) * es);
     dst[c] = src[c];
   }
+  if (blockIdx.y != 0) return;
+  // the prefix never exceeds any member's context nor the host bound
+  int P = min(max(plen[g], 0), max_prefix);
+  for (int m = 0; m < n; ++m) P = min(P, max(context_lens[s0 + m], 0));
+  P = (P / B) * B;
   const int nb = P / B;
   for (int j = threadIdx.x; j < max_pnb; j += kThreads)
     ptab[(int64_t)g * max_pnb + j] = j < nb ? tables[(int64_t)s0 * max_nb + j] : -1;
@@ -187,7 +192,7 @@ pkv_status launch_decode_cascade(int kv_dt, bool fp8, const DecodeArgs& base, co
   float* o_s = reinterpret_cast<float*>(ws + L.o_s);
   float* lse_s = reinterpret_cast<float*>(ws + L.lse_s);
 
-  hipLaunchKernelGGL(cascade_gather_kernel, dim3(n_groups), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(cascade_gather_kernel, dim3(n_groups, kGatherSplit), dim3(kThreads), 0, stream,
                      static_cast<const char*>(base.q), cu_group_seqs, group_prefix_lens,
                      base.block_tables, base.context_lens, base.max_nb, ws + L.qg, ptab,
                      L.max_pnb, plens, seq_start, seq_group, NM, base.Hq, base.Hkv, base.D, base.B,
