@@ -1128,11 +1128,11 @@ int occupancy_of() {
 template <int DT, int D, int GC, bool UNI, bool MF, bool F8, int BPT = 1>
 pkv_status launch_split(DecodeArgs a, int grid_cap, int ncu, hipStream_t stream, int* waves_only) {
   // Matrix-core path: one workgroup (one wave per SIMD, three tiles in
-  // flight each) per CU measured fastest for 16-bit pools -- 3-7% ahead of
-  // two per CU on the Llama-3-8B batch; FP8 pools (half the bytes per tile)
-  // need two per CU to keep enough bytes in flight (about 190 -> 181 us on the
-  // same batch).  Vector path: every resident workgroup.
-  int64_t grid = (int64_t)ncu * (MF ? (F8 ? 2 : 1) : occupancy_of<DT, D, GC, UNI, MF, F8, BPT>());
+  // flight each) per CU measured fastest -- 3-7% ahead of two per CU on the
+  // Llama-3-8B batch for 16-bit pools, 168.5 -> 163.8 us for FP8 pools (four
+  // tiles in flight at one workgroup: 162-164 us; at two workgroups, 171).
+  // Vector path: every resident workgroup.
+  int64_t grid = (int64_t)ncu * (MF ? 1 : occupancy_of<DT, D, GC, UNI, MF, F8, BPT>());
   if (grid > grid_cap) grid = grid_cap;
   if (grid < 1) grid = 1;
   a.n_waves = (int)grid * kWaves;
