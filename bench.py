@@ -446,6 +446,19 @@ def main():
         del d
         torch.cuda.empty_cache()
 
+        # one GPU's share of the same batch at tensor parallelism 8: 4 query
+        # heads over 1 KV head of every block (an eighth of the bytes)
+        sb = W.llama3_8b_tp8_shard(args.seed)
+        sd = Dev(sb)
+        ms, _ = time_fn(sd.decode, 100)
+        rows["decode_llama3_8b_tp8_shard"] = {"ms": round(ms, 5),
+                                              "GB/s": round(sb.kv_read_bytes() / ms / 1e6, 1),
+                                              "kv_bytes": sb.kv_read_bytes()}
+        log(f"[bench] decode_llama3_8b_tp8_shard: {ms * 1e3:.1f} us")
+        sd.free()
+        del sd
+        torch.cuda.empty_cache()
+
         for name, gen in (("decode_opt13b_f16", lambda: W.opt13b_f16(args.seed)),
                           ("decode_shared_prefix_bf16", lambda: W.shared_prefix_bf16(args.seed))):
             bb = gen()

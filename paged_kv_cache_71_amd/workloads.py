@@ -321,6 +321,20 @@ def llama3_8b_bf16(seed: int = 0, S: int = 256, median: float = 1024.0, hi: int 
                   free_order=free_order)
 
 
+def llama3_8b_tp8_shard(seed: int = 0, S: int = 256, median: float = 1024.0,
+                        hi: int = 8192) -> PagedBatch:
+    """One GPU's share of the Llama-3-8B decode layer at tensor parallelism 8:
+    4 query heads over 1 KV head, the same lengths, block count and block
+    placement as ``llama3_8b_bf16(seed)`` (each GPU holds one KV head of every
+    block)."""
+    rng = np.random.default_rng(seed)
+    lengths = lognormal_lengths(rng, S, median=median, hi=hi)
+    NB = pool_blocks_for(16, 8, 128, "bf16")
+    free_order = rng.permutation(NB)
+    return _build("llama3_8b_tp8_shard", rng, lengths, 4, 1, 128, 16, NB, "bf16", q_rows=S,
+                  free_order=free_order)
+
+
 def shared_prefix_bf16(seed: int = 0, prompts: int = 64, n: int = 4, prompt_len: int = 2000,
                        max_suffix: int = 512, NB: int | None = None) -> PagedBatch:
     """Shared-prefix decode batch after forking: each prompt's ``n`` samples alias

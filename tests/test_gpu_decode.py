@@ -197,6 +197,13 @@ def test_llama3_8b_full_size(gpu_lib):
     check(gpu_lib, W.llama3_8b_bf16(0))
 
 
+def test_llama3_8b_tp8_shard_full_size(gpu_lib):
+    """One GPU's share of the benchmarked batch at tensor parallelism 8 (4 query
+    heads over 1 KV head of every block, same lengths and block placement):
+    every output element against the oracle."""
+    check(gpu_lib, W.llama3_8b_tp8_shard(0))
+
+
 def test_opt13b_full_size(gpu_lib):
     check(gpu_lib, W.opt13b_f16(0))
 

@@ -111,3 +111,15 @@ def test_new_token_values_are_the_cached_ones():
     for s in range(3):
         L = int(b.context_lens[s])
         assert b.new_slots[s] == b.block_tables[s, (L - 1) // 4] * 4 + (L - 1) % 4
+
+
+def test_tp8_shard_is_one_kv_head_of_the_llama_batch():
+    """The tensor-parallel share keeps the batch's lengths, tables and block
+    placement, with 4 query heads over 1 KV head: an eighth of the bytes."""
+    full = W.llama3_8b_bf16(0)
+    shard = W.llama3_8b_tp8_shard(0)
+    assert (shard.Hq, shard.Hkv, shard.D, shard.B) == (4, 1, 128, 16)
+    assert np.array_equal(shard.context_lens, full.context_lens)
+    assert np.array_equal(shard.block_tables, full.block_tables)
+    assert shard.NB == full.NB
+    assert shard.kv_read_bytes() * 8 == full.kv_read_bytes()
