@@ -391,10 +391,17 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 constexpr int kTileKV = 32;                 // KV tokens per tile
 constexpr int kWaitLgkm0 = 0xC07F;          // s_waitcnt: LDS/scalar count 0, others at max
 constexpr int kTileQB = 2;                  // q blocks of 16 rows per wave
+// Waves per tile-kernel workgroup.  16-bit D = 128 runs 8 waves, two per
+// SIMD, as two groups of four that take turns between a step's matrix part
+// and its vector part (see the kernel); the other instantiations (whose
+// staging does not split over 512 threads) run 4 waves, two workgroups per CU.
+__host__ __device__ constexpr int tile_waves(int D, bool F8, bool NARROW) {
+  return (!F8 && !NARROW && D == 128) ? 8 : 4;
+}
 // The tile kernel adds the lo parts of the weights (second P.V product) only
-// on tiles where some row's largest weight exceeds kLoShare of that row's
-// running total; see the softmax step.
-constexpr float kLoShare = 0.01f;
+// on tiles where some row's largest weight exceeds 1% of that row's running
+// total (kLog2LoShare = log2(0.01)); see the softmax step.
+constexpr float kLog2LoShare = -6.6438562f;
 
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma16(const u32x4_t a, const u32x4_t b, f32x4_t c) {
@@ -445,13 +452,6 @@ __device__ __forceinline__ float max3_raw(float a, float b, float c) {
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
-// max(a, b) in one instruction (no canonicalising of the operands; a quiet
-// NaN operand yields the other one).
-__device__ __forceinline__ float max_raw(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
 // Row max across the four lane groups (lanes n, n + 16, n + 32, n + 48).
 __device__ __forceinline__ float group_max_raw(float x) {
   const unsigned u = __float_as_uint(x);
@@ -468,8 +468,11 @@ __device__ __forceinline__ float group_max_raw(float x) {
 // NARROW (16-bit D = 64 over blocks of 4 tokens): 8-byte staging chunks, so a
 // wave stages 4 rows per chunk and they lie in one block
 template <int DT, int D, bool F8, bool NARROW = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_tile_kernel(
+__global__ __launch_bounds__(64 * tile_waves(D, F8, NARROW)) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_tile_kernel(
     const PrefillArgs a) {
+  constexpr int TW = tile_waves(D, F8, NARROW);
+  constexpr int TT = 64 * TW;      // threads
+  constexpr bool PP = TW == 8;     // two groups of four waves, one phase apart
   constexpr int QB = kTileQB;
   constexpr int ES = 2;            // q and LDS element bytes
   constexpr int ESK = F8 ? 1 : 2;  // pool element bytes
@@ -484,12 +487,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int CPR = F8 ? 8 : D * ES / (NARROW ? 8 : 16);  // staging chunks per row
   constexpr int CBP = D * ESK / CPR;             // pool bytes per chunk (16, or 8 for FP8 D = 64)
   constexpr int CBL = D * ES / CPR;              // LDS bytes per chunk (16 or 32)
-  constexpr int NCH = kTileKV * CPR / kThreads;  // chunks per thread per tile, K and V each
+  constexpr int NCH = kTileKV * CPR / TT;  // chunks per thread per tile, K and V each
   using Chunk = std::conditional_t<CBP == 16, uint4, uint2>;
   static_assert(CBP == 16 || CBP == 8, "staging chunk");
-  constexpr int RW = kWaves * 16 * QB;        // query rows per workgroup
+  constexpr int RW = TW * 16 * QB;        // query rows per workgroup
   constexpr bool PSPLIT = true;  // hi + lo parts of P for both 16-bit dtypes
-  static_assert(NCH >= 1 && NCH <= 2 && kTileKV * CPR % kThreads == 0, "staging split");
+  static_assert(NCH >= 1 && NCH <= 2 && kTileKV * CPR % TT == 0, "staging split");
   static_assert(16 % (64 / CPR) == 0, "a wave's staged rows must lie in one 16-token half");
 
   __shared__ __attribute__((aligned(16))) char lk[2][kTileKV * KP];
@@ -600,7 +603,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   uint32_t loff[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int ch = tid + kThreads * i;
+    const int ch = tid + TT * i;
     crow[i] = ch / CPR;
     ccol[i] = ch - crow[i] * CPR;
     csel[i] = __builtin_amdgcn_readfirstlane(crow[i] >> log2E);  // entry of this wave's rows
@@ -694,14 +697,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   int ea0 = ent(t0, 0), ea1 = ent(t0, NCH - 1);
   int eb0 = ent(min(t0 + 1, tl), 0), eb1 = ent(min(t0 + 1, tl), NCH - 1);
   int en0 = ent(min(t0 + 2, tl), 0), en1 = ent(min(t0 + 2, tl), NCH - 1);
-  // The 32 bytes of skew after each V row in LDS hold 16 ones of DT (staging
-  // writes only the first D elements of a row): read as d-block NDB of V^T,
-  // they make the P.V product also sum every row's weights.
-  if (tid < 2 * kTileKV * 2) {
-    const uint32_t one2 = DT == DT_BF16 ? 0x3f803f80u : 0x3c003c00u;
-    *reinterpret_cast<uint4*>(lv[tid >> 6] + ((tid >> 1) & 31) * VP + D * ES + (tid & 1) * 16) =
-        make_uint4(one2, one2, one2, one2);
-  }
   gload(sk, kpool, t0, ea0, ea1);
   lstore(lk[t0 & 1], KP, sk);
   gload(sk, kpool, min(t0 + 1, tl), eb0, eb1);
@@ -746,18 +741,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int kk = 0; kk < NKK; ++kk)
           kfr[mb][kk] = as_v(*reinterpret_cast<const uint4*>(K + (16 * mb + n) * KP + 64 * kk + 16 * g4));
     }
-    // O^T += V^T P^T over the D columns of V and a block of ones (the LDS
-    // rows' skew, see below), so o[NDB][c] holds every row's sum of its
-    // weights as they entered the product.  A = V^T rows 16 d + n, tokens
-    // 4 g4 + k and 16 + 4 g4 + k.
+    // O^T += V^T P^T over the D columns of V and a block of ones (an A
+    // operand of 1.0 in every element, from registers), so o[NDB][c] holds
+    // every row's sum of its weights as they entered the product.  A = V^T
+    // rows 16 d + n, tokens 4 g4 + k and 16 + 4 g4 + k.
     const char* V = lv[(j - 1) & 1];
     auto pv_pass = [&](const u32x4_t (&pp)[QB]) __attribute__((always_inline)) {
 #pragma unroll
       for (int d = 0; d <= NDB; ++d) {
-        const char* vp = V + (4 * g4 + (n >> 2)) * VP + (16 * d + 4 * (n & 3)) * ES;
-        const uint2 lo = lds_read_tr16(vp);
-        const uint2 hi = lds_read_tr16(vp + 16 * VP);
-        const u32x4_t va = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        u32x4_t va;
+        if (d < NDB) {
+          const char* vp = V + (4 * g4 + (n >> 2)) * VP + (16 * d + 4 * (n & 3)) * ES;
+          const uint2 lo = lds_read_tr16(vp);
+          const uint2 hi = lds_read_tr16(vp + 16 * VP);
+          va = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        } else {
+          const uint32_t one2 = DT == DT_BF16 ? 0x3f803f80u : 0x3c003c00u;
+          va = u32x4_t{one2, one2, one2, one2};
+        }
 #pragma unroll
         for (int c = 0; c < QB; ++c) o[d][c] = mfma16<DT>(va, pp[c], o[d][c]);
       }
@@ -769,6 +770,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int c = 0; c < QB; ++c) lprev[c] = o[NDB][c][0];
     }
     if constexpr (PV) pv_pass(pph);
+    // two groups: the lo parts of P(j-1) join this step's matrix part
+    if constexpr (PP && PV) {
+      if (pflag) pv_pass(ppl);
+    }
     if constexpr (QK) {
       // S^T blocks: s_nxt[mb][c] holds S[16 mb + 4 g4 + i][q col n of block c]
 #pragma unroll
@@ -781,7 +786,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           for (int c = 0; c < QB; ++c) s_nxt[mb][c] = mfma16<DT>(kfr[mb][kk], qf[c][kk], s_nxt[mb][c]);
       }
     }
-    bool grow[QB], grow_any = false, need_lo = false;
+    // two groups: the matrix part ends here (its results are taken as
+    // complete, so the compiler moves none of it, nor of the vector part,
+    // across the barrier); the other group's matrix part runs while this
+    // group's vector part does
+    if constexpr (PP && LD) {
+#pragma unroll
+      for (int c = 0; c < QB; ++c) {
+#pragma unroll
+        for (int d = 0; d <= NDB; ++d) asm volatile("" ::"v"(o[d][c]));
+        if constexpr (QK) asm volatile("" ::"v"(s_nxt[0][c]), "v"(s_nxt[1][c]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bool grow[QB];
+    uint64_t grow_mask = 0, lo_mask = 0;  // lanes whose row's max grew / that want the lo parts
     float mold[QB], pk[QB][8];  // previous maxima; this tile's weights (for their lo parts)
     if constexpr (SM) {
       const int kv0 = j * kTileKV;
@@ -798,11 +819,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           }
         const float t = group_max_raw(
             max3_raw(max3_raw(r[0], r[1], r[2]), max3_raw(r[3], r[4], r[5]), max3_raw(r[6], r[7], r[7])));
-        const float mn = max_raw(m[c], t * sl);  // t * sl: NaN only when all masked and scale 0
-        grow[c] = mn > m[c] + kRescaleThreshold;
+        // the max grows (lazily) when the tile's exceeds it by the threshold,
+        // and is then the tile's; tsl is NaN only when all masked and scale 0
+        // (no growth then)
+        const float tsl = t * sl;
+        grow[c] = tsl > m[c] + kRescaleThreshold;
         mold[c] = m[c];
-        m[c] = grow[c] ? mn : m[c];
-        grow_any |= grow[c];
+        m[c] = grow[c] ? tsl : m[c];
+        grow_mask |= __builtin_amdgcn_ballot_w64(grow[c]);
         const float mu = m[c];
         uint32_t hw[4];
 #pragma unroll
@@ -823,22 +847,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           // Rounding a weight w to 16 bits moves the row's result by about
           // w * eps * (v - o) / total weight (the total is the sum of the same
           // rounded weights, so a dominant weight's rounding cancels).  Where
-          // the largest weight of every row is at most kLoShare of the row's
+          // the largest weight of every row is at most 1% of the row's
           // total (a lower bound of it: the total two tiles back), the result
           // moves by far less than the tolerance and the lo parts are
           // skipped; else this tile carries them (about 16 significant bits
           // per weight).  A grown maximum (a new dominant token) always does.
-          const float pmax = fast_exp2(__builtin_fmaf(t, sl, -mu));  // 0 (or NaN) if all masked
-          need_lo |= grow[c] || pmax > kLoShare * lprev[c];
+          // The test is taken in log2 units: the row's largest weight is
+          // 2^(tsl - mu); log2(0.01 * total) comes from the total's bits
+          // (e + f - 127 for 2^(e - 127) (1 + f), at most 0.087 below log2,
+          // so it errs towards carrying the lo parts).  All masked or scale
+          // 0: -inf or NaN, no lo parts.
+          const float lg = (float)__float_as_int(lprev[c]) * 0x1p-23f + (kLog2LoShare - 127.f);
+          lo_mask |= __builtin_amdgcn_ballot_w64(tsl - mu > lg);
         }
       }
     }
     // the lo parts of P(j-1): a second pass over the same V tile
-    if constexpr (PV) {
+    if constexpr (!PP && PV) {
       if (pflag) pv_pass(ppl);
     }
     if constexpr (SM) {
-      nflag = PSPLIT && __builtin_amdgcn_ballot_w64(need_lo) != 0;
+      nflag = PSPLIT && (lo_mask | grow_mask) != 0;
       if (nflag) {
 #pragma unroll
         for (int c = 0; c < QB; ++c) {
@@ -852,7 +881,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
       }
       // O now includes P(j-1) V(j-1): bring it (and the row sums) to the new max
-      if (__builtin_amdgcn_ballot_w64(grow_any)) {
+      if (grow_mask) {
 #pragma unroll
         for (int c = 0; c < QB; ++c) {
           const float alpha = grow[c] ? fast_exp2(mold[c] - m[c]) : 1.f;
@@ -876,6 +905,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     FA = FB;
   };
 
+  // Two groups (8 waves): waves 4-7 run one phase behind waves 0-3 -- one
+  // barrier more here, waves 0-3 one more after the loop -- so while one
+  // group issues a step's matrix part the other issues its vector part.
+  // Every staging step has two barriers (after each part).  A tile's staging
+  // is written half by each group, in consecutive phases, and read two
+  // phases later; buffer reuse keeps the one-group distances (K(t) written
+  // in the steps of tile t-2, V(t) in those of tile t, both read in the next).
+  if constexpr (PP) {
+    if (wave >= 4) __builtin_amdgcn_s_barrier();
+  }
   // step t0-1: S(t0) into SB; step t0: softmax(t0), S(t0+1) into SA, P(t0) into PA
   step(t0 - 1, T{}, F{}, T{}, F{}, F{}, SA, SB, PAh, PAl, PBh, PBl, FA, FB);
   step(t0, T{}, F{}, T{}, T{}, T{}, SB, SA, PBh, PBl, PAh, PAl, FB, FA);
@@ -902,6 +941,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     step(tl + 1, F{}, T{}, F{}, F{}, F{}, SA, SB, PBh, PBl, PAh, PAl, FB, FA);
   } else {
     step(t0 + 1, F{}, T{}, F{}, F{}, F{}, SA, SB, PAh, PAl, PBh, PBl, FA, FB);
+  }
+  if constexpr (PP) {
+    if (wave < 4) __builtin_amdgcn_s_barrier();
   }
 
   // total weight of each row: the ones block of O (in every lane of the row)
@@ -1103,14 +1145,15 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillArgs a) {
 
 template <int DT, int D, bool F8, bool NARROW = false>
 pkv_status launch_tile(const PrefillArgs& a, hipStream_t stream) {
-  constexpr int RW = kWaves * 16 * kTileQB;
+  constexpr int TW = tile_waves(D, F8, NARROW);
+  constexpr int RW = TW * 16 * kTileQB;
   const int G = a.Hq / a.Hkv;
   const int TQ = RW / G;
   const int64_t nqt = (a.max_query_len + TQ - 1) / TQ;
   const int64_t grid = nqt * a.S * a.Hkv * a.n_split;
   if (grid == 0) return PKV_OK;
   if (grid > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "prefill grid too large");
-  hipLaunchKernelGGL((prefill_tile_kernel<DT, D, F8, NARROW>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((prefill_tile_kernel<DT, D, F8, NARROW>), dim3((unsigned)grid), dim3(64 * TW), 0,
                      stream, a);
   pkv_status st = check_launch("paged_attention_prefill");
   if (st != PKV_OK || a.n_split <= 1) return st;
@@ -1175,10 +1218,14 @@ PrefillPlan plan_prefill(int kv_dt, int32_t S, int32_t Tq, int32_t max_query_len
   const bool tile = kv_dt != DT_F32 && tile_block_ok(B, D, kv_dt == DT_FP8) && G >= 1 &&
                     G <= kWaves * 16 * kTileQB;
   if (!tile || S <= 0 || Tq <= 0 || max_query_len <= 0 || max_ctx <= 0) return p;
-  const int TQ = kWaves * 16 * kTileQB / G;
+  const int TW = tile_waves(D, kv_dt == DT_FP8, false);  // the NARROW kernel runs 4 as well
+  const int TQ = TW * 16 * kTileQB / G;
   const int64_t grid0 = (int64_t)((max_query_len + TQ - 1) / TQ) * S * Hkv;
   const int max_tiles = (max_ctx + kTileKV - 1) / kTileKV;
-  const int64_t target = 2 * (int64_t)std::max(device_cu_count(), 1);
+  // eight waves per CU: two 4-wave workgroups or one 8-wave workgroup (a
+  // size query with no device to ask plans for the whole 256-CU gfx950)
+  const int cu = device_cu_count();
+  const int64_t target = (8 / TW) * (int64_t)(cu > 0 ? cu : 256);
   if (grid0 >= target) return p;
   int ns = (int)std::min<int64_t>((target + grid0 - 1) / grid0, std::max(1, max_tiles / kMinSplitTiles));
   if (ns <= 1) return p;
