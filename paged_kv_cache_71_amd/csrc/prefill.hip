@@ -720,8 +720,13 @@ __global__ __launch_bounds__(64 * tile_waves(D, F8, NARROW)) __attribute__((amdg
       lstore(lk[j & 1], KP, sk);
       lstore(lv[j & 1], VP, sv);
       const int ec0 = en0, ec1 = en1;
-      en0 = ent(min(j + 4, tl), 0);
-      en1 = ent(min(j + 4, tl), NCH - 1);
+      // two groups: the entries of tile j+4 are fetched in the vector part,
+      // so no scalar load is pending while the matrix part waits for its LDS
+      // reads (the shared counter would make it wait for all of them)
+      if constexpr (!PP) {
+        en0 = ent(min(j + 4, tl), 0);
+        en1 = ent(min(j + 4, tl), NCH - 1);
+      }
       gload(sk, kpool, min(j + 3, tl), ec0, ec1);
       gload(sv, vpool, min(j + 1, tl), ea0, ea1);
       ea0 = eb0;
@@ -800,6 +805,8 @@ __global__ __launch_bounds__(64 * tile_waves(D, F8, NARROW)) __attribute__((amdg
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
+      en0 = ent(min(j + 4, tl), 0);
+      en1 = ent(min(j + 4, tl), NCH - 1);
     }
     bool grow[QB];
     uint64_t grow_mask = 0, lo_mask = 0;  // lanes whose row's max grew / that want the lo parts
