@@ -393,8 +393,10 @@ constexpr int kWaitLgkm0 = 0xC07F;          // s_waitcnt: LDS/scalar count 0, ot
 constexpr int kTileQB = 2;                  // q blocks of 16 rows per wave
 // Waves per tile-kernel workgroup.  16-bit D = 128 runs 8 waves, two per
 // SIMD, as two groups of four that take turns between a step's matrix part
-// and its vector part (see the kernel); the other instantiations (whose
-// staging does not split over 512 threads) run 4 waves, two workgroups per CU.
+// and its vector part (see the kernel); the other instantiations run 4 waves,
+// two workgroups per CU: D = 64, whose 16-byte staging does not split over
+// 512 threads, and FP8 pools (8 waves with 8-byte code chunks measured
+// 1.171 against 1.135 ms on the 8 x 512 batch).
 __host__ __device__ constexpr int tile_waves(int D, bool F8, bool NARROW) {
   return (!F8 && !NARROW && D == 128) ? 8 : 4;
 }
@@ -1003,12 +1005,13 @@ __global__ __launch_bounds__(64 * tile_waves(D, F8, NARROW)) __attribute__((amdg
 // (m, l) pairs and partial outputs are loaded CH at a time, so a row costs one
 // memory round trip for up to CH splits:
 //   out = sum_i e^(m_i - M) o_i / sum_i e^(m_i - M) l_i.
-template <int D>
+// RW: query rows per workgroup of the tile kernel whose partials are merged
+// (a row's query tile, hence its split count, follows from it).
+template <int D, int RW>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a) {
   constexpr int EPL = D / 16;  // outputs per lane: 8 or 4
   constexpr int NV = EPL / 4;  // float4 loads per lane and split
   constexpr int CH = 8;
-  constexpr int RW = kWaves * 16 * kTileQB;
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int c0 = (threadIdx.x & 15) * EPL;
   const int64_t nrows = (int64_t)a.Tq * a.Hq;
@@ -1166,7 +1169,7 @@ pkv_status launch_tile(const PrefillArgs& a, hipStream_t stream) {
   if (st != PKV_OK || a.n_split <= 1) return st;
   const int64_t mgrid = ((int64_t)a.Tq * a.Hq + 15) / 16;  // 16 rows per workgroup
   if (mgrid > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "prefill merge grid too large");
-  hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3((unsigned)mgrid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prefill_merge_kernel<D, RW>), dim3((unsigned)mgrid), dim3(256), 0, stream, a);
   return check_launch("paged_attention_prefill (merge)");
 }
 

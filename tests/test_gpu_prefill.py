@@ -133,6 +133,20 @@ def test_split_long_contexts(gpu_lib, dtype, D, B):
     check(gpu_lib, b)
 
 
+@pytest.mark.parametrize("dtype,D,B", [("bf16", 128, 8), ("f16", 128, 16), ("bf16", 64, 16)])
+def test_split_rows_of_a_query_tile_that_spans_more_splits(gpu_lib, dtype, D, B):
+    """Group size 4 with eight-wave workgroups: a workgroup's query tile is 64
+    tokens, and the 77-token chunk after 300 cached tokens reaches one more KV
+    split with its whole first tile than with its first 32 tokens.  Every row
+    of a tile takes the tile's split count (its last split holds none of the
+    first rows' tokens), so the merge must count splits per tile as the tile
+    kernel does; counting them per 32 tokens left those rows unwritten."""
+    b = W.varlen_prefill(17 + D, [0, 9, 300, 2500], [13, 40, 77, 100], 16, 4, D, B, dtype)
+    assert gpu_lib.prefill_workspace_size(b.S, b.q.shape[0], 100, 16, 4, D, B, dtype,
+                                          b.max_context_len) > 0, "expected a split launch"
+    check(gpu_lib, b)
+
+
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
 def test_split_merge_low_precision_output(gpu_lib, out_dtype):
     """The merge kernel's 16-bit output is the round-to-nearest-even of its
