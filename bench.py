@@ -149,6 +149,34 @@ def main():
         t = np.array([a.elapsed_time(z) for a, z in evs])
         return float(t.mean()), float(np.median(t))
 
+    def graph_time(fn, n_inner=32, reps=20):
+        """Device ms per call of a launch-bound call: n_inner calls captured in
+        one graph and replayed back to back, so no host work sits between the
+        launches (the call-level rows above include the binding's host time)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n_inner):
+                fn()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        z.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(z) / (reps * n_inner)
+        del g
+        return ms
+
     def mixed_row():
         """The Llama-3-8B decode batch plus one 512-token prefill chunk (after
         8192 cached tokens) in one batch: the mixed call against the decode and
@@ -439,7 +467,10 @@ def main():
         del flush
         rms, _ = time_fn(d.reshape, 20)
         rb = 2 * 2 * b.new_k.size * 2   # read + write of K and V rows
-        rows["reshape_and_cache_256_tokens"] = {"ms": round(rms, 5), "GB/s": round(rb / rms / 1e6, 1)}
+        rgms = graph_time(d.reshape)
+        rows["reshape_and_cache_256_tokens"] = {"ms": round(rms, 5), "GB/s": round(rb / rms / 1e6, 1),
+                                                "graph_ms_per_call": round(rgms, 5),
+                                                "graph_GB/s": round(rb / rgms / 1e6, 1)}
 
         rows["decode_llama3_8b_fp8"] = fp8_row(b, d, dec_ms)
         d.free()
@@ -483,7 +514,10 @@ def main():
                                  .astype(np.int64)).to(dev)
         ms, _ = time_fn(lambda: pkv.copy_blocks([kc], [vc], pairs), 20)
         cb = 192 * 2 * 2 * B * Hkv * D * 2
-        rows["copy_blocks_192_pairs"] = {"ms": round(ms, 5), "GB/s": round(cb / ms / 1e6, 1)}
+        gms = graph_time(lambda: pkv.copy_blocks([kc], [vc], pairs))
+        rows["copy_blocks_192_pairs"] = {"ms": round(ms, 5), "GB/s": round(cb / ms / 1e6, 1),
+                                         "graph_ms_per_call": round(gms, 5),
+                                         "graph_GB/s": round(cb / gms / 1e6, 1)}
 
         # swap-out of 1024 scattered blocks (K and V, 64 KiB per block) to a
         # pinned host pool: one swap_blocks launch against one copy per block
