@@ -3,7 +3,10 @@
 A step is one decode step of the Llama-3-8B-shaped layer batch (256 sequences,
 32 query / 8 KV heads, head_dim 128, block 16, bf16 KV, log-normal context
 lengths with median 1024 clipped to [16, 8192], blocks scattered over a 12 GB
-pool): reshape_and_cache of the 256 new tokens, then paged_attention_decode.
+pool): the 256 new tokens' K/V written to their slots and every sequence's
+attention over its cache, in one pkv_decode_step call (the cache write rides
+in the decode kernel's launch; the two calls made separately, reshape_and_cache
+then paged_attention_decode, are timed as a row beside it).
 The headline metric is the achieved KV-read bandwidth of that step:
 algorithmic K+V bytes (every valid token of every sequence, once per KV head)
 divided by the step time.
@@ -112,6 +115,12 @@ def main():
 
         def reshape(self):
             pkv.reshape_and_cache(self.new_k, self.new_v, self.k, self.v, self.slots)
+
+        def step(self):
+            b = self.b
+            assert self.new_k.shape[0] == b.S, "decode_step: one new token per sequence"
+            pkv.decode_step(self.out, self.q, self.new_k, self.new_v, self.slots, self.k, self.v,
+                            self.tables, self.lens, b.max_context_len, b.scale, workspace=self.ws)
 
         def decode(self):
             b = self.b
@@ -350,9 +359,7 @@ def main():
     kv_bytes = b.kv_read_bytes()
     stream = torch.cuda.current_stream()
 
-    def step():
-        d.reshape()
-        d.decode()
+    step = d.step
 
     # W untimed warm-up steps, continued (still untimed) until 300 ms of steps
     # have run: the clocks take tens of milliseconds of load to settle
@@ -374,24 +381,19 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
-    # at least 100 more steps (K if larger) with an event around every decode
-    # launch (the decode kernels' duration for the roofline) and after every
-    # step: the distribution of step times
+    # at least 100 more steps (K if larger) with an event after every step
+    # (its launches: the decode kernels' duration for the roofline): the
+    # distribution of step times
     n_ev = max(100, args.steps)
-    dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n_ev)]
     step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev + 1)]
     torch.cuda.synchronize()
     step_ev[0].record(stream)
     for i in range(n_ev):
-        d.reshape()
-        dec_ev[i][0].record(stream)
-        d.decode()
-        dec_ev[i][1].record(stream)
+        step()
         step_ev[i + 1].record(stream)
     torch.cuda.synchronize()
     step_ms = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(n_ev)])
-    dec_ms = float(np.mean([a.elapsed_time(z) for a, z in dec_ev]))
+    dec_ms = float(np.mean(step_ms))
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (dec_ms * 1e-3) / 1e9
     log(f"[bench] step {ms_per_step * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us, "
@@ -411,9 +413,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "llama3_8b_gqa_decode_bf16: one decode step (reshape_and_cache + "
-                        "paged_attention_decode), 256 sequences, 32 q / 8 kv heads, head_dim 128, "
-                        "block 16, log-normal lengths median 1024 clipped [16, 8192], 12 GB pool",
+            "workload": "llama3_8b_gqa_decode_bf16: one decode step (the new tokens' cache "
+                        "write + paged attention, pkv_decode_step), 256 sequences, 32 q / 8 kv "
+                        "heads, head_dim 128, block 16, log-normal lengths median 1024 clipped "
+                        "[16, 8192], 12 GB pool",
             "sequences": b.S,
             "context_tokens": int(b.context_lens.sum()),
             "kv_bytes_per_step": kv_bytes,
@@ -430,7 +433,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(),
-            "kernel": "paged_attention_decode (decode_split_kernel + decode_merge_kernel launches)",
+            "kernel": "decode_step (decode_split_kernel with the cache write + "
+                      "decode_merge_kernel launches)",
             "ms_per_launch": round(dec_ms, 5),
         },
     }
@@ -465,6 +469,13 @@ def main():
             "ms_p10_p90": [round(float(np.percentile(ft, q)), 5) for q in (10, 90)],
             "launches": len(fl)}
         del flush
+        def two_calls():
+            d.reshape()
+            d.decode()
+
+        tms, _ = time_fn(two_calls, 20)
+        rows["decode_step_as_two_calls"] = {"ms": round(tms, 5),
+                                            "GB/s": round(kv_bytes / tms / 1e6, 1)}
         rms, _ = time_fn(d.reshape, 20)
         rb = 2 * 2 * b.new_k.size * 2   # read + write of K and V rows
         rgms = graph_time(d.reshape)
@@ -589,7 +600,8 @@ def record_traffic(fetch_csv, write_csv):
     per = {}
     for k, short in (("decode_split_kernel", "split"), ("decode_merge_kernel", "merge"),
                      ("reshape_and_cache_kernel", "reshape")):
-        per[short] = {"read": round(fetch[k] * 1024 * fs), "write": round(write[k] * 1024 * ws)}
+        if k in fetch and k in write:  # (no reshape launch when the step is one call)
+            per[short] = {"read": round(fetch[k] * 1024 * fs), "write": round(write[k] * 1024 * ws)}
     step = sum(per[k]["read"] + per[k]["write"] for k in ("split", "merge"))
     rec = {
         "workload": "Llama-3-8B-shaped decode, bf16 KV, 256 sequences, 32 q / 8 kv heads, head_dim 128, block 16",

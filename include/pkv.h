@@ -135,6 +135,42 @@ pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void
                                       void* stream);
 
 /* ------------------------------------------------------------------------
+ * decode_step -- one decode step in one call: the new token of every
+ * sequence is written to the pools and attended, as pkv_reshape_and_cache
+ * (T = S) followed by pkv_paged_attention_decode.
+ *
+ * Defined by "LLM inference, part 3" ch. 13 sec. 1 (each step the new
+ * tokens' K/V go to the slots the host computed, then attention reads the
+ * cache through the block table) and CS349D lecture 3 sec. 3.2 (the block
+ * write fused into the attention kernel's pass).
+ *
+ *   key, value   : device [S, Hkv, D] of kv_dtype; row s is the K (V) of the
+ *                  newest token of sequence s, token context_lens[s] - 1
+ *   slot_mapping : device int64 [S]; that token's slot (slots outside
+ *                  [0, NB * B) are not written, as in pkv_reshape_and_cache)
+ *   k_cache,
+ *   v_cache      : device pools [NB, B, Hkv, D] of kv_dtype, written in place
+ *   (the other arguments and the workspace as for pkv_paged_attention_decode;
+ *   kv_dtype f32, f16 or bf16)
+ * Precondition: for every s with context_lens[s] >= 1, slot_mapping[s] is the
+ * slot the block table gives token context_lens[s] - 1 of sequence s, and no
+ * other sequence reads that slot (the ordinary step of a block manager that
+ * copies shared blocks before writing).  Then out and both pools are
+ * bit-identical to the two calls made in order.  On the matrix-core path
+ * (16-bit pools, D = 128, B >= 4, 4, 8 or 16 query heads per KV head) it is one
+ * pass: the attention takes token context_lens[s] - 1 from key/value directly
+ * while the same launch stores those rows in their slots; elsewhere the cache
+ * write runs as its own launch first.  Errors as for both calls.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_decode_step(void* out, pkv_dtype out_dtype, const void* q, const void* key,
+                           const void* value, const int64_t* slot_mapping, void* k_cache,
+                           void* v_cache, int64_t NB, pkv_dtype kv_dtype,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t max_context_len, int32_t S,
+                           int32_t Hq, int32_t Hkv, int32_t D, int32_t B, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * paged_attention_decode_noalloc -- pkv_paged_attention_decode without a
  * workspace argument, for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid

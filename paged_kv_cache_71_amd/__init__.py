@@ -7,7 +7,8 @@ benchmark.  Loading is lazy: ``load_library()`` (or the first call) loads the
 library and raises if it has not been built.
 """
 from ._binding import (BlockManager, PkvError, PkvOOM, copy_blocks, declared_symbols,
-                       decode_cascade_workspace_size, decode_workspace_size, load_library,
+                       decode_cascade_workspace_size, decode_step, decode_workspace_size,
+                       load_library,
                        mixed_workspace_size, paged_attention_decode,
                        paged_attention_decode_cascade, paged_attention_decode_cascade_fp8,
                        paged_attention_decode_fp8, paged_attention_decode_noalloc, paged_attention_mixed, paged_attention_mixed_fp8,
@@ -17,7 +18,7 @@ from ._binding import (BlockManager, PkvError, PkvOOM, copy_blocks, declared_sym
 
 __all__ = [
     "BlockManager", "PkvError", "PkvOOM", "copy_blocks", "declared_symbols",
-    "decode_cascade_workspace_size", "decode_workspace_size", "load_library",
+    "decode_cascade_workspace_size", "decode_step", "decode_workspace_size", "load_library",
     "mixed_workspace_size", "paged_attention_decode", "paged_attention_decode_cascade",
     "paged_attention_decode_cascade_fp8", "paged_attention_decode_fp8",
     "paged_attention_decode_noalloc", "paged_attention_mixed",

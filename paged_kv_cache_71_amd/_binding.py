@@ -64,6 +64,8 @@ def load_library(path: str | None = None):
                                             i32, f32, P, sz, P]),
         "pkv_paged_attention_decode_noalloc": (st, [P, st, P, P, P, st, P, i32, P, i32, i32, i32,
                                                     i32, i32, i32, f32, P]),
+        "pkv_decode_step": (st, [P, st, P, P, P, P, P, P, i64, st, P, i32, P, i32, i32, i32, i32,
+                                 i32, i32, f32, P, sz, P]),
         "pkv_prefill_workspace_size": (st, [i32, i32, i32, i32, i32, i32, i32, st, i32, SZP]),
         "pkv_paged_attention_prefill": (st, [P, st, P, P, i32, i32, P, P, st, P, i32, P, i32, i32,
                                              i32, i32, i32, i32, f32, P, sz, P]),
@@ -216,6 +218,39 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B,
         float(scale), ws_ptr, ws_bytes, _stream(stream)), "paged_attention_decode")
+    return out
+
+
+def decode_step(out, q, key, value, slot_mapping, k_cache, v_cache, block_tables, context_lens,
+                max_context_len: int, scale: float, workspace=None, stream=None):
+    """One decode step: the new tokens' K/V rows (``key``/``value`` [S, Hkv, D],
+    token context_lens[s] - 1 of each sequence) are written to their slots and
+    attended, as reshape_and_cache followed by paged_attention_decode.
+    ``workspace`` (uint8 device tensor) is allocated here if not given."""
+    torch = _torch()
+    lib = load_library()
+    S, Hq, D = q.shape
+    NB, B, Hkv, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("decode_step: shape mismatch")
+    if key.shape != (S, Hkv, D) or value.shape != key.shape or slot_mapping.shape != (S,):
+        raise ValueError("decode_step: key/value must be [S, Hkv, D], slot_mapping [S]")
+    if not (q.dtype == key.dtype == value.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("decode_step: q/key/value/pool dtype mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("decode_step: block_tables [S, max_nb] / context_lens [S]")
+    need = decode_workspace_size(S, Hq, Hkv, D, B, max_context_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pkv_decode_step(
+        _dev(out, "out"), dtype_code(out), _dev(q, "q"), _dev(key, "key"), _dev(value, "value"),
+        _dev(slot_mapping, "slot_mapping", torch.int64), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), NB, dtype_code(k_cache),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B,
+        float(scale), ws_ptr, ws_bytes, _stream(stream)), "decode_step")
     return out
 
 

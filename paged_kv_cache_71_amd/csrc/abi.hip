@@ -209,8 +209,18 @@ static pkv_status scratch_address(void** out) {
   return PKV_OK;
 }
 
+// The decode step's new tokens (pkv_decode_step): one K and one V row per
+// sequence and the slots they are written to.
+struct StepTokens {
+  const void* key = nullptr;
+  const void* value = nullptr;
+  const int64_t* slot_mapping = nullptr;
+  int64_t NB = 0;
+};
+
 // use_scratch: the allocation-free variant; the workspace arguments are unused
 // and the device's static scratch holds the partial states instead.
+// step: a decode step (the new tokens written to the pools and attended).
 static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype kv_dtype,
                               bool fp8, const void* k_cache, const void* v_cache,
                               const float* k_scale, const float* v_scale,
@@ -219,7 +229,7 @@ static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv
                               int32_t Hq, int32_t Hkv, int32_t D, int32_t B, float scale,
                               void* workspace, size_t workspace_bytes, void* stream,
                               const CascadeGroups& cg = CascadeGroups(),
-                              bool use_scratch = false) {
+                              bool use_scratch = false, const StepTokens* step = nullptr) {
   g_last_error[0] = 0;
   const bool cascade = cg.on;
   PKV_REQUIRE(S >= 0 && Hq > 0 && Hkv > 0 && D > 0 && B > 0, PKV_ERR_INVALID_ARG,
@@ -248,6 +258,14 @@ static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv
                 cg.n_groups, cg.max_group_size, S);
     PKV_REQUIRE(cg.max_prefix_len >= 0, PKV_ERR_INVALID_ARG,
                 "decode_cascade: negative max_prefix_len %d", cg.max_prefix_len);
+  }
+  if (step) {
+    const pkv::CacheWrite cw{step->key, step->value, step->slot_mapping, S, step->NB,
+                             kv_dtype, false, nullptr, nullptr};
+    const pkv_status st = pkv::check_cache_write("decode_step", cw, k_cache, v_cache, Hkv, D, B);
+    if (st != PKV_OK) return st;
+    PKV_REQUIRE((int64_t)S * Hkv * D * dt_bytes(kv_dtype) / 16 < ((int64_t)1 << 31),
+                PKV_ERR_UNSUPPORTED, "decode_step: %d new rows of %d x %d elements", S, Hkv, D);
   }
   if (S == 0) return PKV_OK;
   PKV_REQUIRE(out && q && k_cache && v_cache && block_tables && context_lens, PKV_ERR_INVALID_ARG,
@@ -294,6 +312,12 @@ static pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv
   a.v_scale = v_scale;
   a.seq_start = nullptr;
   a.lse = nullptr;
+  if (step) {
+    a.new_k = step->key;
+    a.new_v = step->value;
+    a.slot_mapping = step->slot_mapping;
+    a.nslots = step->NB * B;
+  }
   if (cascade)
     return launch_decode_cascade(kv_dtype, fp8, a, cg.cu, cg.prefix_lens, cg.n_groups,
                                  cg.max_group_size, cg.max_prefix_len, workspace, workspace_bytes,
@@ -342,6 +366,20 @@ pkv_status pkv_paged_attention_decode_noalloc(void* out, pkv_dtype out_dtype, co
   return decode_impl(out, out_dtype, q, kv_dtype, false, k_cache, v_cache, nullptr, nullptr,
                      block_tables, max_blocks_per_seq, context_lens, max_context_len, S, Hq, Hkv,
                      D, B, scale, nullptr, 0, stream, CascadeGroups(), true);
+}
+
+pkv_status pkv_decode_step(void* out, pkv_dtype out_dtype, const void* q, const void* key,
+                           const void* value, const int64_t* slot_mapping, void* k_cache,
+                           void* v_cache, int64_t NB, pkv_dtype kv_dtype,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t max_context_len, int32_t S,
+                           int32_t Hq, int32_t Hkv, int32_t D, int32_t B, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  const StepTokens step{key, value, slot_mapping, NB};
+  return decode_impl(out, out_dtype, q, kv_dtype, false, k_cache, v_cache, nullptr, nullptr,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, S, Hq, Hkv,
+                     D, B, scale, workspace, workspace_bytes, stream, CascadeGroups(), false,
+                     &step);
 }
 
 pkv_status pkv_decode_cascade_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t D,

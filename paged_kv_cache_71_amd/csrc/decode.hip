@@ -398,6 +398,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int i = tid; i <= S; i += kThreads) a.ws_ps[i] = sm_ps[i];
   }
 
+  // ---- decode step (16-bit pools, matrix-core path): the new tokens' K/V
+  // rows go to their slots, one 16-byte chunk of K and one of V per thread and
+  // round.  The first round is loaded here and stored when the wave is done
+  // with its range, so neither its loads nor its stores hold up the tiles.
+  // No wave of this launch reads those slots -- token L - 1 of every row is
+  // taken from new_k/new_v (see issue) -- so the stores need no ordering
+  // against the attention's loads.
+  constexpr bool STEP = MF && !F8;
+  const bool step_on = STEP && a.new_k != nullptr;  // uniform
+  const int rc = a.Hkv * D * KS / 16;                // 16-byte chunks per token row
+  const int n_items = step_on ? S * rc : 0;          // < 2^31 (checked on the host)
+  const int gid = blockIdx.x * kThreads + tid;
+  uint4 nk{}, nv{};
+  int64_t nslot = -1;
+  if (gid < n_items) {
+    nslot = a.slot_mapping[gid / rc];
+    nk = reinterpret_cast<const uint4*>(a.new_k)[gid];
+    nv = reinterpret_cast<const uint4*>(a.new_v)[gid];
+  }
+  auto put_new_rows = [&]() __attribute__((always_inline)) {
+    if (!step_on) return;
+    uint4* const kw = static_cast<uint4*>(const_cast<void*>(a.k_cache));
+    uint4* const vw = static_cast<uint4*>(const_cast<void*>(a.v_cache));
+    auto put = [&](int i, int64_t slot, const uint4& k4, const uint4& v4) __attribute__((always_inline)) {
+      if (slot >= 0 && slot < a.nslots) {
+        const int64_t d = slot * rc + (i % rc);
+        kw[d] = k4;
+        vw[d] = v4;
+      }
+    };
+    if (gid < n_items) put(gid, nslot, nk, nv);
+    // (batches with more chunks than the grid has threads)
+    const int nthreads = gridDim.x * kThreads;
+    for (int i = gid + nthreads; i < n_items; i += nthreads)
+      put(i, a.slot_mapping[i / rc], reinterpret_cast<const uint4*>(a.new_k)[i],
+          reinterpret_cast<const uint4*>(a.new_v)[i]);
+  };
+
   // sequences with nothing to attend: all-zero output, -inf log-sum-exp
   for (int i = blockIdx.x; i < S; i += gridDim.x) {
     if (rfl(sm_len[i]) != 0) continue;
@@ -422,6 +460,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int x1 = min(x0 + C, N);
   if (x0 >= x1) {
     if (lane == 0) a.ws_rec[w] = make_int4(-1, 0, 0, 0);  // nothing cut here
+    put_new_rows();
     return;
   }
 
@@ -565,11 +604,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         kb[1] = make_uint2(k0.z, k0.w);
         kb[2] = make_uint2(k1.x, k1.y);
         kb[3] = make_uint2(k1.z, k1.w);
-      } else {
-        const unsigned koff = (unsigned)((tk & bmask) * row_stride32 + kvoff + row * LB);
-        const uint64_t kbase = bsel(tk);
-#pragma unroll
-        for (int kk = 0; kk < NLD; ++kk) kb[kk] = ldkv(kpool + kbase + koff + kk * 4 * LB);
       }
       if constexpr (F8) {
         // FP8 V goes through LDS, so its load layout is free: two 16-byte
@@ -584,12 +618,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           vb[2 * jv + 1] = make_uint2(v4.z, v4.w);
         }
       } else {
+        // SUB: the tile holding token L - 1 of a decode step, whose K/V row
+        // comes from new_k/new_v (lanes that would read it, clamped rows
+        // included, read it there; a per-lane choice of address)
+        auto ld16 = [&](auto sub_tag) __attribute__((always_inline)) {
+          constexpr bool SUB = decltype(sub_tag)::value;
+          const unsigned koff = (unsigned)((tk & bmask) * row_stride32 + kvoff + row * LB);
+          const char* kp = kpool + bsel(tk) + koff;
+          if constexpr (SUB) {
+            if (tk == c.L - 1)
+              kp = static_cast<const char*>(a.new_k) + (int64_t)c.s * row_stride + kvoff + row * LB;
+          }
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-          const int tv = min(ts + 4 * row + i, c.L - 1);
-          const unsigned voff = (unsigned)((tv & bmask) * row_stride32 + kvoff + col * LB);
-          vb[i] = ldkv(vpool + bsel(tv) + voff);
-        }
+          for (int kk = 0; kk < NLD; ++kk) kb[kk] = ldkv(kp + kk * 4 * LB);
+#pragma unroll
+          for (int i = 0; i < NLD; ++i) {
+            const int tv = min(ts + 4 * row + i, c.L - 1);
+            const unsigned voff = (unsigned)((tv & bmask) * row_stride32 + kvoff + col * LB);
+            const char* vp = vpool + bsel(tv) + voff;
+            if constexpr (SUB) {
+              if (tv == c.L - 1)
+                vp = static_cast<const char*>(a.new_v) + (int64_t)c.s * row_stride + kvoff + col * LB;
+            }
+            vb[i] = ldkv(vp);
+          }
+        };
+        if (step_on && c.j == c.nt - 1) ld16(BoolTag<true>{});
+        else ld16(BoolTag<false>{});
       }
     } else if constexpr (UNI) {
 #pragma unroll
@@ -1005,6 +1060,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     constexpr int U = decltype(u)::value;
     if (U < r) step(x + U, u, U == r - 1);
   });
+  put_new_rows();
 }
 
 // Merge: one wave per range boundary b = 1 .. n_waves - 1.  The split kernel's
@@ -1302,6 +1358,20 @@ pkv_status launch_decode(int kv_dt, bool fp8, const DecodePlan& plan, DecodeArgs
   const int ncu = device_cu_count();
   if (ncu <= 0) return fail(PKV_ERR_HIP, "decode: cannot query the current device");
   const int es = dt_bytes(kv_dt), oes = dt_bytes(a.out_dt);
+  const int64_t row_bytes = (int64_t)a.Hkv * a.D * es;  // one token's K (or V) row, 16-bit pools
+  if (a.new_k && (!mf || fp8)) {
+    // decode step off the 16-bit matrix-core path: the cache write as a launch
+    // of its own, then the plain decode over the written pools
+    if (!waves_only) {
+      const pkv_status st =
+          launch_reshape_and_cache(a.new_k, a.new_v, const_cast<void*>(a.k_cache),
+                                   const_cast<void*>(a.v_cache), a.slot_mapping, a.S, row_bytes,
+                                   a.nslots, stream);
+      if (st != PKV_OK) return st;
+    }
+    a.new_k = a.new_v = nullptr;
+    a.slot_mapping = nullptr;
+  }
   for (int s0 = 0; s0 < S_total; s0 += plan.seqs_per_launch) {
     DecodeArgs b = a;
     b.S = S_total - s0 < plan.seqs_per_launch ? S_total - s0 : plan.seqs_per_launch;
@@ -1311,6 +1381,11 @@ pkv_status launch_decode(int kv_dt, bool fp8, const DecodePlan& plan, DecodeArgs
     b.context_lens = a.context_lens + s0;
     if (a.seq_start) b.seq_start = a.seq_start + s0;
     if (a.lse) b.lse = a.lse + (int64_t)s0 * a.Hq;
+    if (a.new_k) {
+      b.new_k = static_cast<const char*>(a.new_k) + s0 * row_bytes;
+      b.new_v = static_cast<const char*>(a.new_v) + s0 * row_bytes;
+      b.slot_mapping = a.slot_mapping + s0;
+    }
     // no more waves than the batch could ever use, nor than the workspace
     // has slots for (the launch also caps at one resident wave set)
     const int64_t max_tiles = (int64_t)b.S * a.rows_per_seq * nt_max;

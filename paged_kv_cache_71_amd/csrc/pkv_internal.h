@@ -155,6 +155,14 @@ struct DecodeArgs {
   // per (sequence, head) (device [S, Hq]; -inf for an empty range)
   const int32_t* seq_start;
   float* lse;
+  // optional (null = off): the decode step's new tokens, device [S, Hkv, D] of
+  // the pools' 16-bit dtype.  Token context_lens[s] - 1 of sequence s is read
+  // from new_k/new_v[s] instead of the pools, and those rows are stored at
+  // slot_mapping[s] of the pools (int64 [S]; skipped outside [0, nslots)).
+  const void* new_k = nullptr;
+  const void* new_v = nullptr;
+  const int64_t* slot_mapping = nullptr;
+  int64_t nslots = 0;
 };
 // q_dt: dtype of q (and of the pools unless fp8); fp8: the pools hold E4M3 codes.
 // waves_only != null: launch nothing, store the most waves any split launch of
