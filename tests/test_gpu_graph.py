@@ -52,6 +52,31 @@ def test_decode_step_in_a_graph(gpu_lib):
     replay_matches_eager(step, out)
 
 
+def test_one_call_decode_step_in_a_graph(gpu_lib):
+    """pkv_decode_step (the cache write inside the decode launch), workspace
+    given; the new tokens' slots start poisoned, so every replay must also
+    leave the new rows in the pools."""
+    b = W.llama3_8b_bf16(0, S=64, NB=20000)
+    print(f"[graph] one-call decode step S={b.S}", flush=True)
+    db = DevBatch(b)
+    for pool in (db.k_cache, db.v_cache):
+        pool.view(-1, b.Hkv, b.D).index_fill_(0, db.new_slots, float("nan"))
+    out = db.out()
+    ws = torch.empty(max(gpu_lib.decode_workspace_size(b.S, b.Hq, b.Hkv, b.D, b.B, b.max_context_len), 1),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        gpu_lib.decode_step(out, db.q, db.new_k, db.new_v, db.new_slots, db.k_cache, db.v_cache,
+                            db.block_tables, db.context_lens, b.max_context_len, b.scale,
+                            workspace=ws)
+
+    replay_matches_eager(step, out)
+    assert torch.equal(db.k_cache.view(-1, b.Hkv, b.D)[db.new_slots].view(torch.int16),
+                       db.new_k.view(torch.int16))
+    assert torch.equal(db.v_cache.view(-1, b.Hkv, b.D)[db.new_slots].view(torch.int16),
+                       db.new_v.view(torch.int16))
+
+
 def test_split_prefill_in_a_graph(gpu_lib):
     """A prefill whose KV ranges are split (partials + merge kernel)."""
     b = W.varlen_prefill(3, [3000, 500], [100, 40], 32, 8, 128, 16, "bf16")
