@@ -1,13 +1,13 @@
 """Seeded random sweep against the fp64 oracle: every case draws its own
 shape (head dim, KV heads, group size, block size), dtype, length mix (empty
 contexts, contexts shorter than a block, long ones), chunk layout and softmax
-scale, for decode, prefill, mixed batches, cascade (shared-prefix) decode and
-the FP8 variants; every mixed and cascade case and half of the decode and
-prefill cases also check that a 16-bit output is exactly the fp32 output
-rounded to nearest even.  Each case
-prints its parameters before it runs, so a failure names the draw.  The
-fixed-shape tests cover the named configurations; this sweep covers the
-combinations between them."""
+scale, for decode, prefill, mixed batches, cascade (shared-prefix) decode,
+the FP8 variants and the one-call decode step; every mixed and cascade case
+and half of the decode and prefill cases also check that a 16-bit output is
+exactly the fp32 output rounded to nearest even.  Each case prints its
+parameters before it runs, so a failure names the draw.  The fixed-shape
+tests cover the named configurations; this sweep covers the combinations
+between them."""
 import numpy as np
 import pytest
 import torch
@@ -231,3 +231,23 @@ def test_random_mixed_fp8(gpu_lib, case):
                              tables, b.context_lens, b.scale)
     err = max_abs(out, ref)
     assert err <= TOL[q_dtype], f"max abs err {err}"
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_random_decode_step(gpu_lib, case):
+    """pkv_decode_step against reshape_and_cache + paged_attention_decode (out
+    and both pools bit for bit, the written slots poisoned beforehand) and
+    against the oracle."""
+    from test_gpu_decode_step import _check_oracle, _run_both
+    rng = np.random.default_rng(17000 + case)
+    Hq, Hkv, D = _heads(rng, (64, 128, 128))
+    B = int(rng.choice([1, 4, 8, 16, 16, 32]))
+    dtype = str(rng.choice(["f32", "f16", "bf16", "bf16"]))
+    S = int(rng.integers(1, 40))
+    lengths = _lengths(rng, S, 3000)
+    print(f"[random decode step {case}] Hq={Hq} Hkv={Hkv} D={D} B={B} {dtype} "
+          f"lengths={lengths.tolist()}", flush=True)
+    b = W.decode_batch(18000 + case, lengths, Hq, Hkv, D, B, dtype)
+    b.scale = _scale(rng, D)
+    out, dev, key, val, slots, pre = _run_both(gpu_lib, b, case)
+    _check_oracle(b, out, dev, key, val, slots, pre)
