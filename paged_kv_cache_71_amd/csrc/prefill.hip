@@ -401,9 +401,9 @@ __host__ __device__ constexpr int tile_waves(int D, bool F8, bool NARROW) {
   return (!F8 && !NARROW && D == 128) ? 8 : 4;
 }
 // The tile kernel adds the lo parts of the weights (second P.V product) only
-// on tiles where some row's largest weight exceeds 1% of that row's running
-// total (kLog2LoShare = log2(0.01)); see the softmax step.
-constexpr float kLog2LoShare = -6.6438562f;
+// on tiles where some row's largest weight exceeds 4% of that row's running
+// total (kLog2LoShare = log2(0.04)); see the softmax step.
+constexpr float kLog2LoShare = -4.6438562f;
 
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma16(const u32x4_t a, const u32x4_t b, f32x4_t c) {
@@ -853,16 +853,20 @@ __global__ __launch_bounds__(64 * tile_waves(D, F8, NARROW)) __attribute__((amdg
         }
         nph[c] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
         if constexpr (PSPLIT) {
-          // Rounding a weight w to 16 bits moves the row's result by about
-          // w * eps * (v - o) / total weight (the total is the sum of the same
-          // rounded weights, so a dominant weight's rounding cancels).  Where
-          // the largest weight of every row is at most 1% of the row's
-          // total (a lower bound of it: the total two tiles back), the result
-          // moves by far less than the tolerance and the lo parts are
-          // skipped; else this tile carries them (about 16 significant bits
-          // per weight).  A grown maximum (a new dominant token) always does.
+          // Rounding the weights w_i to 16 bits (by d_i, |d_i| <= eps w_i)
+          // moves the row's result by sum_i d_i (v_i - o) / total (the total
+          // is the sum of the same rounded weights, so a dominant weight's
+          // rounding cancels).  The roundings of different weights are
+          // independent, so the shift is of order eps sqrt(sum_i (w_i /
+          // total)^2) |v - o| <= eps sqrt(p) |v - o| when no weight exceeds a
+          // share p of the total.  Where the largest weight of every row is
+          // at most 4% of the row's total (a lower bound of it: the total two
+          // tiles back), that is a fifth of one weight's rounding, well inside
+          // the tolerance, and the lo parts are skipped; else this tile
+          // carries them (about 16 significant bits per weight).  A grown
+          // maximum (a new dominant token) always does.
           // The test is taken in log2 units: the row's largest weight is
-          // 2^(tsl - mu); log2(0.01 * total) comes from the total's bits
+          // 2^(tsl - mu); log2(0.04 * total) comes from the total's bits
           // (e + f - 127 for 2^(e - 127) (1 + f), at most 0.087 below log2,
           // so it errs towards carrying the lo parts).  All masked or scale
           // 0: -inf or NaN, no lo parts.

@@ -86,6 +86,20 @@ def test_peaked_attention_stays_accurate(gpu_lib):
     check(gpu_lib, b)
 
 
+@pytest.mark.parametrize("factor", [6.0, 10.0, 16.0])
+def test_peaked_queries_keep_half_the_tolerance(gpu_lib, factor):
+    """Queries scaled up 6-16x put most of a row's weight on a few tokens, the
+    case where rounding the weights to bf16 matters most; the tiles that skip
+    the lo parts of the weights (every weight at most 4% of its row's total)
+    must still leave half the tolerance unused."""
+    for seed in range(3):
+        b = W.varlen_prefill(50 + seed, [30, 300, 2000], [20, 64, 128], 32, 8, 128, 16, "bf16")
+        b.q[...] = W.to_storage(W.storage_to_f32(b.q, "bf16") * factor, "bf16")
+        err = check(gpu_lib, b)
+        print(f"[prefill] peaked x{factor} seed {seed}: max abs err {err:.2e}", flush=True)
+        assert err <= TOL["bf16"] / 2
+
+
 def test_prefill_reduced_workload_sampled(gpu_lib):
     b = W.prefill_bf16(0, S=3, prior_lo=900, prior_hi=3000, NB=2000)
     rng = np.random.default_rng(0)
