@@ -157,7 +157,7 @@ pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void
  * other sequence reads that slot (the ordinary step of a block manager that
  * copies shared blocks before writing).  Then out and both pools are
  * bit-identical to the two calls made in order.  On the matrix-core path
- * (16-bit pools, D = 128, B >= 4, 4, 8 or 16 query heads per KV head) it is one
+ * (16-bit pools, D = 128, B >= 4, a multiple of 4 query heads per KV head) it is one
  * pass: the attention takes token context_lens[s] - 1 from key/value directly
  * while the same launch stores those rows in their slots; elsewhere the cache
  * write runs as its own launch first.  Errors as for both calls.
