@@ -134,3 +134,23 @@ def test_misaligned_pointers_are_refused(lib):
     assert b"layer 1" in lib.pkv_last_error()
     assert lib.pkv_copy_blocks(good, good, 2, ctypes.c_void_p(0x1004), 3, 16, 8, 128, 2, None) == 1
     assert lib.pkv_swap_blocks(good, pools, 2, FAKE, 3, 16, 8, 128, 2, None) == 1
+
+
+def test_decode_step_rejects_bad_arguments(lib):
+    """pkv_decode_step validates the cache write's arguments and the decode's
+    before any launch (fake device pointers never reach a kernel)."""
+    need = ctypes.c_size_t(0)
+    lib.pkv_decode_workspace_size(4, 8, 4, 128, 16, 2048, ctypes.byref(need))
+
+    def step(key=FAKE, value=FAKE, slots=FAKE, NB=100, kv=2, ws=need.value, out=FAKE, S=4):
+        return lib.pkv_decode_step(out, 0, FAKE, key, value, slots, FAKE, FAKE, NB, kv, FAKE, 128,
+                                   FAKE, 2048, S, 8, 4, 128, 16, 0.1, FAKE, ws, None)
+    assert step(key=None) == 1 and lib.pkv_last_error()            # null new rows
+    assert step(slots=None) == 1
+    assert step(key=MIS) == 1 and b"aligned" in lib.pkv_last_error()
+    assert step(slots=ctypes.c_void_p(0x1004)) == 1                # int64 slots, 8-byte aligned
+    assert step(NB=0) == 1                                         # empty pools
+    assert step(kv=3) == 2                                         # FP8 pools: not this call
+    assert step(ws=16) == 3                                        # workspace too small
+    assert step(out=MIS) == 1
+    assert step(S=0) == 0                                          # nothing to do
